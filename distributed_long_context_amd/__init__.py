@@ -1,0 +1,344 @@
+"""MI355X (gfx950) attention tiles for one GPU's share of distributed attention.
+
+Thin Python binding over libmesh_attn.so (include/mesh_attn.h).  The functions
+keep the C names; they only marshal torch tensors (device memory) and the
+current HIP stream into the C structs.  Every step of the computation runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Iterable, Optional, Sequence
+
+from . import _abi
+from ._abi import (MA_OK, MA_ERR_INVALID, MA_ERR_UNSUPPORTED, MA_ERR_LAUNCH, MA_F32, MA_BF16, MA_MASK_NONE,
+                   MA_MASK_CAUSAL, MA_MASK_STRIPED_ZIGZAG, MA_TILE_EMPTY, MA_TILE_PARTIAL, MA_TILE_FULL,
+                   MA_MAX_MERGE, MeshAttnError, lib)
+
+__all__ = [
+    "mesh_attn_tile_fwd", "mesh_attn_merge", "mesh_attn_tile_bwd", "mesh_attn_tile_bwd_workspace_size",
+    "mesh_attn_map_mesh_tile", "mesh_attn_map_groups", "mesh_attn_map_zigzag", "mesh_attn_pos_contiguous",
+    "mesh_attn_pos_zigzag", "mesh_attn_pos_striped", "mesh_attn_pos_at", "mesh_attn_classify",
+    "mesh_attn_count_allowed", "mesh_attn_build_worklist", "mesh_attn_version", "Pos", "Tile", "BwdTile",
+    "MA_F32", "MA_BF16", "MA_MASK_NONE", "MA_MASK_CAUSAL", "MA_MASK_STRIPED_ZIGZAG", "MA_TILE_EMPTY",
+    "MA_TILE_PARTIAL", "MA_TILE_FULL", "MeshAttnError", "lib",
+]
+
+
+# ---------------------------------------------------------------- positions --
+
+class Pos:
+    """Token positions of a partition: segments (local_begin, global_begin, stride)."""
+
+    def __init__(self, segments: Sequence[Sequence[int]]):
+        self.segments = [tuple(int(x) for x in s) for s in segments]
+
+    @classmethod
+    def from_c(cls, p: _abi.ma_pos) -> "Pos":
+        return cls([(p.seg[i].local_begin, p.seg[i].global_begin, p.seg[i].stride) for i in range(p.nseg)])
+
+    def to_c(self) -> _abi.ma_pos:
+        p = _abi.ma_pos()
+        p.nseg = len(self.segments)
+        for i, (lb, gb, st) in enumerate(self.segments[:_abi.MA_MAX_SEGMENTS]):
+            p.seg[i].local_begin, p.seg[i].global_begin, p.seg[i].stride = lb, gb, st
+        return p
+
+    def __repr__(self):
+        return f"Pos({self.segments})"
+
+
+def _pos_c(pos: Optional[Pos]) -> _abi.ma_pos:
+    return pos.to_c() if pos is not None else Pos([(0, 0, 1)]).to_c()
+
+
+# ------------------------------------------------------------ tensor checks --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MA_BF16
+    if t.dtype == torch.float32:
+        return MA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: last axis must be contiguous")
+
+
+def _bshd_strides(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, S, H, d]")
+    _check_dev(t, name)
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _head_map_c(head_map, hq):
+    if head_map is None:
+        return None, None
+    arr = (C.c_int32 * hq)(*[int(x) for x in head_map])
+    return arr, C.cast(arr, C.POINTER(C.c_int32))
+
+
+# ---------------------------------------------------------------- forward --
+
+class Tile:
+    """One (Q partition, KV partition) tile: q, k, v inputs and o, lse outputs (device tensors)."""
+
+    def __init__(self, q, k, v, o, lse, q_pos: Optional[Pos] = None, k_pos: Optional[Pos] = None):
+        self.q, self.k, self.v, self.o, self.lse = q, k, v, o, lse
+        self.q_pos, self.k_pos = q_pos, k_pos
+
+
+def mesh_attn_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
+                       stream=None) -> None:
+    """Partial (O, LSE) of every tile, enqueued on `stream` (default: current stream)."""
+    tiles = list(tiles)
+    if not tiles:
+        return
+    t0 = tiles[0]
+    B, _, Hq, d = t0.q.shape
+    Hkv = t0.k.shape[2]
+    dt = _dtype_code(t0.q)
+    arr = (_abi.ma_tile * len(tiles))()
+    for i, t in enumerate(tiles):
+        for name, x in (("q", t.q), ("o", t.o)):
+            if x.dim() != 4 or x.shape[0] != B or x.shape[2] != Hq or x.shape[3] != d or _dtype_code(x) != dt:
+                raise ValueError(f"tile {i}: {name} shape/dtype mismatch")
+            _check_dev(x, name)
+        for name, x in (("k", t.k), ("v", t.v)):
+            if x.dim() != 4 or x.shape[0] != B or x.shape[2] != Hkv or x.shape[3] != d or _dtype_code(x) != dt:
+                raise ValueError(f"tile {i}: {name} shape/dtype mismatch")
+            _check_dev(x, name)
+        if t.o.shape[1] != t.q.shape[1] or t.v.shape[1] != t.k.shape[1]:
+            raise ValueError(f"tile {i}: sequence lengths disagree")
+        if tuple(t.lse.shape) != (B, Hq, t.q.shape[1]) or t.lse.dtype != _torch().float32:
+            raise ValueError(f"tile {i}: lse must be float32 [B, Hq, Sq]")
+        _check_dev(t.lse, "lse")
+        for name, x, ref in (("q", t.q, t0.q), ("k", t.k, t0.k), ("v", t.v, t0.v), ("o", t.o, t0.o)):
+            if x.stride()[:3] != ref.stride()[:3]:
+                raise ValueError(f"tile {i}: {name} strides differ from tile 0")
+        if t.lse.stride()[:2] != t0.lse.stride()[:2]:
+            raise ValueError(f"tile {i}: lse strides differ from tile 0")
+        c = arr[i]
+        c.q, c.k, c.v, c.o, c.lse = t.q.data_ptr(), t.k.data_ptr(), t.v.data_ptr(), t.o.data_ptr(), t.lse.data_ptr()
+        c.sq, c.sk = t.q.shape[1], t.k.shape[1]
+        c.q_pos, c.k_pos = _pos_c(t.q_pos), _pos_c(t.k_pos)
+    a = _abi.ma_tile_fwd_args()
+    a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.mask_mode = dt, B, Hq, Hkv, d, int(mask_mode)
+    a.scale, a.ntiles = float(scale), len(tiles)
+    hm_keep, a.head_map = _head_map_c(head_map, Hq)
+    a.tiles = C.cast(arr, C.POINTER(_abi.ma_tile))
+    a.q_stride[:] = _bshd_strides(t0.q, "q")
+    a.k_stride[:] = _bshd_strides(t0.k, "k")
+    a.v_stride[:] = _bshd_strides(t0.v, "v")
+    a.o_stride[:] = _bshd_strides(t0.o, "o")
+    a.lse_stride[:] = (t0.lse.stride(0), t0.lse.stride(1))
+    _abi.check(lib().mesh_attn_tile_fwd(C.byref(a), _stream_ptr(stream)), "mesh_attn_tile_fwd")
+
+
+# ------------------------------------------------------------------ merge --
+
+def mesh_attn_merge(o_in: Sequence, lse_in: Sequence, o_out, lse_out, stream=None) -> None:
+    """Merge k partial (O [B,S,H,d], LSE [B,H,S]) pairs into (o_out, lse_out)."""
+    k = len(o_in)
+    if k != len(lse_in) or k < 1:
+        raise ValueError("need k >= 1 matching O and LSE partials")
+    B, S, H, d = o_out.shape
+    dt = _dtype_code(o_out)
+    for x in list(o_in) + [o_out]:
+        if tuple(x.shape) != (B, S, H, d) or _dtype_code(x) != dt or x.stride() != o_out.stride():
+            raise ValueError("all O tensors must share shape, dtype and strides")
+        _check_dev(x, "o")
+    for x in list(lse_in) + [lse_out]:
+        if tuple(x.shape) != (B, H, S) or x.dtype != _torch().float32 or x.stride() != lse_out.stride():
+            raise ValueError("all LSE tensors must be float32 [B, H, S] with equal strides")
+        _check_dev(x, "lse")
+    optr = (C.c_void_p * k)(*[x.data_ptr() for x in o_in])
+    lptr = (C.c_void_p * k)(*[x.data_ptr() for x in lse_in])
+    a = _abi.ma_merge_args()
+    a.dtype, a.batch, a.seqlen, a.heads, a.head_dim, a.k = dt, B, S, H, d, k
+    a.o_in, a.lse_in = C.cast(optr, C.POINTER(C.c_void_p)), C.cast(lptr, C.POINTER(C.c_void_p))
+    a.o_out, a.lse_out = o_out.data_ptr(), lse_out.data_ptr()
+    a.o_stride[:] = _bshd_strides(o_out, "o_out")
+    a.lse_stride[:] = (lse_out.stride(0), lse_out.stride(1))
+    _abi.check(lib().mesh_attn_merge(C.byref(a), _stream_ptr(stream)), "mesh_attn_merge")
+
+
+# --------------------------------------------------------------- backward --
+
+class BwdTile:
+    """One tile of the backward: q, k, v, o, dout, lse inputs; dq, dk, dv float32 outputs."""
+
+    def __init__(self, q, k, v, o, dout, lse, dq, dk, dv, q_pos: Optional[Pos] = None, k_pos: Optional[Pos] = None):
+        self.q, self.k, self.v, self.o, self.dout, self.lse = q, k, v, o, dout, lse
+        self.dq, self.dk, self.dv = dq, dk, dv
+        self.q_pos, self.k_pos = q_pos, k_pos
+
+
+def _bwd_args(tiles, scale, mask_mode, head_map, accumulate):
+    torch = _torch()
+    t0 = tiles[0]
+    B, _, Hq, d = t0.q.shape
+    Hkv = t0.k.shape[2]
+    arr = (_abi.ma_bwd_tile * len(tiles))()
+    for i, t in enumerate(tiles):
+        for name, x, ref in (("q", t.q, t0.q), ("o", t.o, t0.q), ("dout", t.dout, t0.q)):
+            if x.dtype != torch.bfloat16 or x.dim() != 4 or x.shape[0] != B or x.shape[2:] != t0.q.shape[2:] \
+                    or x.shape[1] != t.q.shape[1] or x.stride()[:3] != ref.stride()[:3]:
+                raise ValueError(f"tile {i}: {name} must be bf16 [B, Sq, Hq, d] with q's strides")
+            _check_dev(x, name)
+        for name, x in (("k", t.k), ("v", t.v)):
+            if x.dtype != torch.bfloat16 or x.shape[0] != B or x.shape[2:] != t0.k.shape[2:] \
+                    or x.shape[1] != t.k.shape[1] or x.stride()[:3] != t0.k.stride()[:3]:
+                raise ValueError(f"tile {i}: {name} must be bf16 [B, Sk, Hkv, d] with k's strides")
+            _check_dev(x, name)
+        if t.dq.dtype != torch.float32 or tuple(t.dq.shape) != tuple(t.q.shape) or t.dq.stride()[:3] != t0.dq.stride()[:3]:
+            raise ValueError(f"tile {i}: dq must be float32 shaped like q")
+        for name, x in (("dk", t.dk), ("dv", t.dv)):
+            if x.dtype != torch.float32 or tuple(x.shape) != tuple(t.k.shape) or x.stride()[:3] != t0.dk.stride()[:3]:
+                raise ValueError(f"tile {i}: {name} must be float32 shaped like k")
+            _check_dev(x, name)
+        _check_dev(t.dq, "dq")
+        if tuple(t.lse.shape) != (B, Hq, t.q.shape[1]) or t.lse.dtype != torch.float32 \
+                or t.lse.stride()[:2] != t0.lse.stride()[:2]:
+            raise ValueError(f"tile {i}: lse must be float32 [B, Hq, Sq]")
+        _check_dev(t.lse, "lse")
+        c = arr[i]
+        c.q, c.k, c.v, c.o, c.dout = t.q.data_ptr(), t.k.data_ptr(), t.v.data_ptr(), t.o.data_ptr(), t.dout.data_ptr()
+        c.lse, c.dq, c.dk, c.dv = t.lse.data_ptr(), t.dq.data_ptr(), t.dk.data_ptr(), t.dv.data_ptr()
+        c.sq, c.sk = t.q.shape[1], t.k.shape[1]
+        c.q_pos, c.k_pos = _pos_c(t.q_pos), _pos_c(t.k_pos)
+    a = _abi.ma_tile_bwd_args()
+    a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.mask_mode = MA_BF16, B, Hq, Hkv, d, int(mask_mode)
+    a.scale, a.ntiles, a.accumulate = float(scale), len(tiles), int(bool(accumulate))
+    keep, a.head_map = _head_map_c(head_map, Hq)
+    a.tiles = C.cast(arr, C.POINTER(_abi.ma_bwd_tile))
+    a.q_stride[:] = _bshd_strides(t0.q, "q")
+    a.k_stride[:] = _bshd_strides(t0.k, "k")
+    a.dq_stride[:] = _bshd_strides(t0.dq, "dq")
+    a.dk_stride[:] = _bshd_strides(t0.dk, "dk")
+    a.lse_stride[:] = (t0.lse.stride(0), t0.lse.stride(1))
+    return a, (arr, keep)
+
+
+def mesh_attn_tile_bwd_workspace_size(tiles: Sequence[BwdTile], scale: float = 1.0, mask_mode: int = MA_MASK_NONE,
+                                      head_map=None) -> int:
+    a, keep = _bwd_args(list(tiles), scale, mask_mode, head_map, False)
+    return int(lib().mesh_attn_tile_bwd_workspace_size(C.byref(a)))
+
+
+def mesh_attn_tile_bwd(tiles: Sequence[BwdTile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
+                       accumulate: bool = False, workspace=None, stream=None) -> None:
+    """dQ, dK, dV of every tile (dK/dV summed over tiles sharing a KV buffer), enqueued on `stream`.
+
+    `workspace` is a device uint8 tensor of at least mesh_attn_tile_bwd_workspace_size bytes; when None
+    one is allocated here through torch (the library itself never allocates)."""
+    torch = _torch()
+    tiles = list(tiles)
+    if not tiles:
+        return
+    a, keep = _bwd_args(tiles, scale, mask_mode, head_map, accumulate)
+    need = int(lib().mesh_attn_tile_bwd_workspace_size(C.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=tiles[0].q.device)
+    if workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+        raise ValueError(f"workspace must be a device buffer of >= {need} bytes")
+    _abi.check(lib().mesh_attn_tile_bwd(C.byref(a), C.c_void_p(workspace.data_ptr()),
+                                        workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+               "mesh_attn_tile_bwd")
+
+
+# ----------------------------------------------------------------- mapper --
+
+def mesh_attn_map_mesh_tile(n: int, a: int, b: int, g: int, kvr: bool = True):
+    q = (C.c_int32 * max(a, 1))()
+    kv = (C.c_int32 * max(b, 1))()
+    _abi.check(lib().mesh_attn_map_mesh_tile(n, a, b, g, int(kvr), q, kv), "mesh_attn_map_mesh_tile")
+    return list(q)[:a], list(kv)[:b]
+
+
+def mesh_attn_map_groups(n: int, a: int, b: int, g: int):
+    q = (C.c_int32 * max(a, 1))()
+    kv = (C.c_int32 * max(b, 1))()
+    _abi.check(lib().mesh_attn_map_groups(n, a, b, g, q, kv), "mesh_attn_map_groups")
+    return list(q)[:a], list(kv)[:b]
+
+
+def mesh_attn_map_zigzag(N: int, r: int):
+    out = (C.c_int32 * 2)()
+    _abi.check(lib().mesh_attn_map_zigzag(N, r, out), "mesh_attn_map_zigzag")
+    return tuple(out)
+
+
+def mesh_attn_pos_contiguous(global_begin: int) -> Pos:
+    p = _abi.ma_pos()
+    _abi.check(lib().mesh_attn_pos_contiguous(global_begin, C.byref(p)), "mesh_attn_pos_contiguous")
+    return Pos.from_c(p)
+
+
+def mesh_attn_pos_zigzag(N: int, r: int, chunk_len: int) -> Pos:
+    p = _abi.ma_pos()
+    _abi.check(lib().mesh_attn_pos_zigzag(N, r, chunk_len, C.byref(p)), "mesh_attn_pos_zigzag")
+    return Pos.from_c(p)
+
+
+def mesh_attn_pos_striped(N: int, r: int) -> Pos:
+    p = _abi.ma_pos()
+    _abi.check(lib().mesh_attn_pos_striped(N, r, C.byref(p)), "mesh_attn_pos_striped")
+    return Pos.from_c(p)
+
+
+def mesh_attn_pos_at(pos: Pos, t: int) -> int:
+    p = pos.to_c()
+    return int(lib().mesh_attn_pos_at(C.byref(p), t))
+
+
+def mesh_attn_classify(q_pos: Pos, sq: int, k_pos: Pos, sk: int, mask_mode: int) -> int:
+    qp, kp = _pos_c(q_pos), _pos_c(k_pos)
+    r = int(lib().mesh_attn_classify(C.byref(qp), sq, C.byref(kp), sk, int(mask_mode)))
+    if r < 0:
+        raise MeshAttnError(-r, "mesh_attn_classify")
+    return r
+
+
+def mesh_attn_count_allowed(q_pos: Pos, sq: int, k_pos: Pos, sk: int, mask_mode: int) -> int:
+    qp, kp = _pos_c(q_pos), _pos_c(k_pos)
+    r = int(lib().mesh_attn_count_allowed(C.byref(qp), sq, C.byref(kp), sk, int(mask_mode)))
+    if r < 0:
+        raise MeshAttnError(MA_ERR_INVALID, "mesh_attn_count_allowed")
+    return r
+
+
+def mesh_attn_build_worklist(q_pos: Sequence[Pos], sq: Sequence[int], k_pos: Sequence[Pos], sk: Sequence[int],
+                             mask_mode: int):
+    nq, nk = len(q_pos), len(k_pos)
+    qa = (_abi.ma_pos * max(nq, 1))(*[p.to_c() for p in q_pos])
+    ka = (_abi.ma_pos * max(nk, 1))(*[p.to_c() for p in k_pos])
+    sqa = (C.c_int64 * max(nq, 1))(*sq)
+    ska = (C.c_int64 * max(nk, 1))(*sk)
+    cap = max(nq * nk, 1)
+    oq, ok_, oc = (C.c_int32 * cap)(), (C.c_int32 * cap)(), (C.c_int32 * cap)()
+    n = int(lib().mesh_attn_build_worklist(nq, qa, sqa, nk, ka, ska, int(mask_mode), cap, oq, ok_, oc))
+    if n < 0:
+        raise MeshAttnError(MA_ERR_INVALID, "mesh_attn_build_worklist")
+    return [(oq[i], ok_[i], oc[i]) for i in range(n)]
+
+
+def mesh_attn_version() -> int:
+    return int(lib().mesh_attn_version())

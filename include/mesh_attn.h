@@ -1,0 +1,287 @@
+/*
+ * mesh_attn.h - C ABI of the MI355X (gfx950) attention-tile library.
+ *
+ * One GPU's share of the Q-KV assignment matrix of distributed attention:
+ *   - mesh_attn_tile_fwd : exact attention of (Q partition, KV partition) tiles,
+ *                          each emitting a partial output O and a per-row LSE;
+ *   - mesh_attn_merge    : the LSE-based merge that folds k partial (O, LSE)
+ *                          pairs of one Q partition into its output;
+ *   - mesh_attn_tile_bwd : the matching backward (dQ, dK, dV from O, LSE, dO);
+ *   - host-only mapper   : Mesh tiles with KV partition rotation, Q/KV groups,
+ *                          zigzag and striped token positions, tile classes.
+ *
+ * Sources, cited by title and section:
+ *   [Mesh]   "Mesh-Attention: A New Communication-Efficient Distributed Attention
+ *             with Improved Data Locality" (arXiv 2512.20968)
+ *   [CHARM+] "CHARM+: Cross-Hardware Attention with Re-Merge Multistream
+ *             Mechanism" (arXiv 2611.05906v1)
+ *   [Ring]   "Ring Attention and Context Parallelism: How Long-Context LLMs Are
+ *             Trained Across GPUs"
+ *
+ * Conventions for every call:
+ *   - Return value: MA_OK (0) or an MA_ERR_* code; no call aborts or throws.
+ *     mesh_attn_last_error() returns a message for the calling thread's last error.
+ *   - Device pointers are borrowed for the work enqueued on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream); the caller keeps
+ *     them alive until the stream reaches that point.  Calls are asynchronous
+ *     and never synchronise the device.  Host arrays (tile lists, head maps,
+ *     pointer lists) are read before the call returns.
+ *   - The library allocates no device memory and keeps no state between calls.
+ *   - Layouts: Q, O, dO are [B, S, Hq, d]; K, V are [B, S, Hkv, d]; LSE is
+ *     [B, Hq, S] float32 (natural log).  Strides are in ELEMENTS; the d axis
+ *     (and the S axis of LSE) must have stride 1.  bf16 tensors need 16-byte
+ *     aligned base pointers and strides that are multiples of 8 elements;
+ *     fp32 tensors 16-byte aligned bases and strides multiple of 4.
+ *   - Head map: query head h reads KV head head_map[h] (host array of Hq
+ *     entries).  NULL means groups of Hq/Hkv consecutive query heads share one
+ *     KV head, kv(h) = h / (Hq/Hkv) ([Mesh] section 4.8, GQA).
+ *   - Masks act on GLOBAL token positions ([Ring], "Gotchas": masks must use
+ *     global positions): key u is allowed for query t iff pos_k(u) <= pos_q(t)
+ *     ([Mesh] section 3.7; [Ring] "Causal masks and load balancing").  A query
+ *     row with no allowed key gets O = 0 and LSE = -inf, never NaN.
+ */
+#ifndef MESH_ATTN_H
+#define MESH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MA_VERSION 1
+
+/* status codes */
+#define MA_OK 0
+#define MA_ERR_INVALID 1      /* bad argument: null pointer, size <= 0, out-of-range map, ... */
+#define MA_ERR_UNSUPPORTED 2  /* valid but not implemented: head_dim not 64/128, fp32 backward, ... */
+#define MA_ERR_LAUNCH 3       /* the HIP runtime reported an error while enqueueing */
+
+/* element types */
+#define MA_F32 0
+#define MA_BF16 1
+
+/* mask modes */
+#define MA_MASK_NONE 0            /* every key allowed; positions ignored */
+#define MA_MASK_CAUSAL 1          /* causal; q_pos and k_pos must each be ONE segment of stride 1 */
+#define MA_MASK_STRIPED_ZIGZAG 2  /* causal; up to MA_MAX_SEGMENTS segments of any stride >= 1
+                                     (zigzag shares = 2 contiguous segments, [Ring] "Causal masks
+                                     and load balancing"; striped = stride N, [Mesh] section 3.7) */
+
+/* tile classes ([Mesh] section 3.7: masked, triangular, dense pairs) */
+#define MA_TILE_EMPTY 0    /* no (query, key) pair allowed */
+#define MA_TILE_PARTIAL 1  /* some allowed */
+#define MA_TILE_FULL 2     /* all allowed */
+
+#define MA_MAX_SEGMENTS 4
+#define MA_MAX_MERGE 64
+#define MA_MAX_HEADS 128
+#define MA_MAX_TILES 4096
+
+/*
+ * Token positions of a partition.  Segment s covers local indices
+ * [local_begin_s, local_begin_{s+1}) (the last runs to the partition end); local
+ * index t in it has global position global_begin_s + (t - local_begin_s)*stride_s.
+ * Segments are given in increasing local_begin order, the first at 0; strides
+ * are >= 1; every position must lie in [0, 2^31 - 1).  Contiguous partition =
+ * one segment of stride 1; zigzag share = two segments; striped rank r of N =
+ * one segment {0, r, N}.
+ */
+typedef struct {
+  int64_t local_begin;
+  int64_t global_begin;
+  int64_t stride;
+} ma_segment;
+
+typedef struct {
+  int32_t nseg; /* 1..MA_MAX_SEGMENTS; ignored under MA_MASK_NONE */
+  int32_t reserved;
+  ma_segment seg[MA_MAX_SEGMENTS];
+} ma_pos;
+
+/* ---------------------------------------------------------------------------
+ * Tile forward.  [Mesh] section 2.2: one (Q_i, KV_j) pair yields
+ * (O_ij, lse_ij) = Attention(Q_i, K_j, V_j); [Mesh] section 2.1 softmax
+ * attention; [CHARM+] appendix A, Algorithm 2 (CompAttention).
+ *
+ * For each tile, batch b and query head h, query row t:
+ *   s[t,u] = scale * q[t] . k[u]   over keys u of KV head head_map[h]
+ *   LSE[t] = ln sum_{u allowed} exp(s[t,u])
+ *   O[t]   = sum_{u allowed} exp(s[t,u] - LSE[t]) v[u]
+ * Accumulation is fp32; bf16 O is rounded to nearest even at the store.
+ * Every tile writes its own (O, LSE) over its whole [sq] range.  A tile that is
+ * EMPTY under the mask is not computed: its O is filled with 0 and its LSE with
+ * -inf (callers normally leave EMPTY tiles out; see mesh_attn_classify).
+ * --------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;  /* device, [B, sq, Hq, d], dtype */
+  const void* k;  /* device, [B, sk, Hkv, d], dtype */
+  const void* v;  /* device, [B, sk, Hkv, d], dtype */
+  void* o;        /* device, [B, sq, Hq, d], dtype (written) */
+  float* lse;     /* device, [B, Hq, sq] float32 (written) */
+  int64_t sq;     /* >= 1 */
+  int64_t sk;     /* >= 1 */
+  ma_pos q_pos;
+  ma_pos k_pos;
+} ma_tile;
+
+typedef struct {
+  int32_t dtype;      /* MA_BF16 or MA_F32 (inputs and O) */
+  int32_t batch;      /* B >= 1 */
+  int32_t hq;         /* 1..MA_MAX_HEADS */
+  int32_t hkv;        /* 1..hq */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t mask_mode;  /* MA_MASK_* */
+  float scale;        /* softmax scale, e.g. 1/sqrt(d) ([Mesh] section 2.1) */
+  int32_t ntiles;     /* 0..MA_MAX_TILES (0 is a no-op) */
+  const int32_t* head_map;  /* host, hq entries in [0, hkv), or NULL */
+  const ma_tile* tiles;     /* host array of ntiles */
+  int64_t q_stride[3];      /* b, s, h (elements) - shared by all tiles */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int64_t lse_stride[2];    /* b, h */
+} ma_tile_fwd_args;
+
+int mesh_attn_tile_fwd(const ma_tile_fwd_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * LSE merge.  [Mesh] section 2.2 (online softmax rescales partial outputs by
+ * their LSE), section 3.3 (online softmax as the reduce-scatter reducer);
+ * [CHARM+] appendix A, Algorithm 2 (CommAndUpdate); [Ring] "Ring Attention:
+ * Pass KV Blocks Around the Ring".  For each (b, h, t):
+ *   L* = max_r lse_r;  lse = L* + ln sum_r exp(lse_r - L*);
+ *   O  = sum_r exp(lse_r - lse) * O_r;   all lse_r = -inf -> (0, -inf).
+ * Math in fp32; bf16 O rounded to nearest even.  o_out may equal o_in[0] and
+ * lse_out may equal lse_in[0] (in place); other overlaps are undefined.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+  int32_t dtype;      /* MA_BF16 or MA_F32 (all O tensors) */
+  int32_t batch;      /* >= 1 */
+  int32_t seqlen;     /* S >= 1 */
+  int32_t heads;      /* H >= 1 */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t k;          /* 1..MA_MAX_MERGE partials */
+  const void* const* o_in;     /* host array of k device pointers, [B, S, H, d] */
+  const float* const* lse_in;  /* host array of k device pointers, [B, H, S] */
+  void* o_out;                 /* device, [B, S, H, d] */
+  float* lse_out;              /* device, [B, H, S] */
+  int64_t o_stride[3];         /* b, s, h - shared by inputs and output */
+  int64_t lse_stride[2];       /* b, h */
+} ma_merge_args;
+
+int mesh_attn_merge(const ma_merge_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Tile backward.  [Mesh] section 3.5: the backward kernel runs per pair with
+ * (Q_i, KV_j, O_i, dO_i) and its partial dQ_i, dKV_j are accumulated locally
+ * with addition.  The pages print no formula; this is the derivative of the
+ * forward with P = exp(s - LSE) on allowed entries:
+ *   D[t] = dO[t].O[t];  dS = P (dO[t].v[u] - D[t]);
+ *   dQ[t] = scale sum_u dS k[u];  dK[u] = scale sum dS q[t];  dV[u] = sum P dO[t],
+ * dK/dV summed over the query heads that read the KV head and over every tile
+ * in the call that names the same dk/dv buffers.  O and LSE may be the row's
+ * FINAL values over a larger KV set (the distributed case); then the outputs
+ * are this KV partition's share.
+ *
+ * accumulate = 0: dq, dk, dv are overwritten; = 1: the results are added to
+ * what the buffers hold.  All tiles naming the same dk (or dv) buffer must name
+ * the same k and v buffers and sk.  dq buffers of different tiles must not
+ * overlap unless they are identical (then contributions add).  bf16 only.
+ * The workspace (device, >= mesh_attn_tile_bwd_workspace_size bytes, 256-byte
+ * aligned) holds D and per-call scratch; its contents on entry do not matter.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;     /* device bf16 [B, sq, Hq, d] */
+  const void* k;     /* device bf16 [B, sk, Hkv, d] */
+  const void* v;     /* device bf16 [B, sk, Hkv, d] */
+  const void* o;     /* device bf16 [B, sq, Hq, d] */
+  const void* dout;  /* device bf16 [B, sq, Hq, d] */
+  const float* lse;  /* device float32 [B, Hq, sq] */
+  float* dq;         /* device float32 [B, sq, Hq, d] */
+  float* dk;         /* device float32 [B, sk, Hkv, d] */
+  float* dv;         /* device float32 [B, sk, Hkv, d] */
+  int64_t sq;
+  int64_t sk;
+  ma_pos q_pos;
+  ma_pos k_pos;
+} ma_bwd_tile;
+
+typedef struct {
+  int32_t dtype;      /* MA_BF16 */
+  int32_t batch;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t mask_mode;
+  float scale;
+  int32_t ntiles;
+  int32_t accumulate;
+  int32_t reserved;
+  const int32_t* head_map;     /* host or NULL */
+  const ma_bwd_tile* tiles;    /* host array */
+  int64_t q_stride[3];         /* q, o, dout share these (b, s, h) */
+  int64_t k_stride[3];         /* k and v share these */
+  int64_t dq_stride[3];        /* float32 dq */
+  int64_t dk_stride[3];        /* float32 dk and dv share these */
+  int64_t lse_stride[2];       /* b, h */
+} ma_tile_bwd_args;
+
+size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* args);
+int mesh_attn_tile_bwd(const ma_tile_bwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-only mapper.  Pure functions: no device work, no allocation; output
+ * arrays are caller-sized.  Return MA_OK or MA_ERR_INVALID.
+ * --------------------------------------------------------------------------- */
+
+/* [Mesh] sections 3.2-3.3: GPU g of n = a*b computes Q partitions
+ * r*a .. r*a+a-1 (r = g / a) against KV partitions c*b .. c*b+b-1 (basic, kvr=0)
+ * or {c + t*a : 0 <= t < b} (KV partition rotation, kvr=1), c = g mod a.
+ * q_parts gets a entries, kv_parts b entries (tile order). */
+int mesh_attn_map_mesh_tile(int32_t n, int32_t a, int32_t b, int32_t g, int32_t kvr,
+                            int32_t* q_parts, int32_t* kv_parts);
+
+/* [Mesh] section 3.3: Q group {r*a + x : x < a} and KV group {c + a*x : x < b} of GPU g. */
+int mesh_attn_map_groups(int32_t n, int32_t a, int32_t b, int32_t g,
+                         int32_t* q_group, int32_t* kv_group);
+
+/* [Ring] "Causal masks and load balancing": with 2N chunks, rank r holds chunks r and 2N-1-r. */
+int mesh_attn_map_zigzag(int32_t N, int32_t r, int32_t chunks[2]);
+
+/* Position descriptors: contiguous partition starting at global_begin; zigzag share
+ * of rank r (two chunks of chunk_len tokens); striped rank r of N (positions r + N*t). */
+int mesh_attn_pos_contiguous(int64_t global_begin, ma_pos* out);
+int mesh_attn_pos_zigzag(int32_t N, int32_t r, int64_t chunk_len, ma_pos* out);
+int mesh_attn_pos_striped(int32_t N, int32_t r, ma_pos* out);
+
+/* Global position of local index t (t in [0, length)); -1 on invalid input. */
+int64_t mesh_attn_pos_at(const ma_pos* pos, int64_t t);
+
+/* Class of a (Q partition, KV partition) pair under mask_mode: MA_TILE_EMPTY,
+ * MA_TILE_PARTIAL or MA_TILE_FULL (MA_MASK_NONE always FULL); negative
+ * (-MA_ERR_INVALID) on invalid input. */
+int mesh_attn_classify(const ma_pos* q_pos, int64_t sq, const ma_pos* k_pos, int64_t sk, int32_t mask_mode);
+
+/* Exact number of allowed (query, key) pairs of the pair (per head); -1 on invalid input. */
+int64_t mesh_attn_count_allowed(const ma_pos* q_pos, int64_t sq, const ma_pos* k_pos, int64_t sk,
+                                int32_t mask_mode);
+
+/* Non-EMPTY pairs among nq Q partitions x nk KV partitions (row-major scan).
+ * Writes up to max_out entries of (q index, kv index, class) into out_q, out_k,
+ * out_class and returns the number of non-EMPTY pairs (may exceed max_out),
+ * or -1 on invalid input. */
+int32_t mesh_attn_build_worklist(int32_t nq, const ma_pos* q_pos, const int64_t* sq,
+                                 int32_t nk, const ma_pos* k_pos, const int64_t* sk,
+                                 int32_t mask_mode, int32_t max_out,
+                                 int32_t* out_q, int32_t* out_k, int32_t* out_class);
+
+/* diagnostics */
+const char* mesh_attn_last_error(void);
+int mesh_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MESH_ATTN_H */

@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every declared symbol, and validates arguments on the host (CPU only)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from distributed_long_context_amd import _abi
+
+HEADER_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(HEADER_DIR):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(mesh_attn_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _abi.SIGNATURES, f"binding lacks {n}"
+    assert L.mesh_attn_version() == 1
+
+
+def _fwd_args(**kw):
+    a = _abi.ma_tile_fwd_args()
+    a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.mask_mode = _abi.MA_BF16, 1, 4, 2, 128, 0
+    a.scale, a.ntiles = 0.1, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), _abi.MA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _abi.MA_ERR_INVALID),
+    (dict(hq=3, hkv=2), _abi.MA_ERR_INVALID),
+    (dict(hq=200, hkv=2), _abi.MA_ERR_INVALID),
+    (dict(mask_mode=9), _abi.MA_ERR_INVALID),
+    (dict(scale=0.0), _abi.MA_ERR_INVALID),
+    (dict(scale=float("nan")), _abi.MA_ERR_INVALID),
+    (dict(ntiles=1), _abi.MA_ERR_INVALID),  # null tile list
+    (dict(ntiles=-1), _abi.MA_ERR_INVALID),
+])
+def test_tile_fwd_rejects_bad_arguments(kw, code):
+    a = _fwd_args(**kw)
+    assert _abi.lib().mesh_attn_tile_fwd(C.byref(a), None) == code
+    assert len(_abi.lib().mesh_attn_last_error()) > 0
+
+
+def test_tile_fwd_rejects_bad_tiles_without_launching():
+    L = _abi.lib()
+    t = (_abi.ma_tile * 1)()
+    a = _fwd_args(ntiles=1)
+    a.tiles = C.cast(t, C.POINTER(_abi.ma_tile))
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID  # null pointers
+    t[0].q = t[0].k = t[0].v = t[0].o = 4096
+    t[0].lse = 4096
+    t[0].sq, t[0].sk = 0, 5
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID  # sq = 0
+    t[0].sq = 5
+    t[0].q = 4100
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID  # misaligned
+    t[0].q = 4096
+    a.mask_mode = _abi.MA_MASK_CAUSAL
+    t[0].q_pos.nseg = 2  # causal needs a single stride-1 segment
+    t[0].q_pos.seg[1].local_begin = 2
+    t[0].k_pos.nseg = 1
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID
+    t[0].q_pos.nseg = 5
+    a.mask_mode = _abi.MA_MASK_STRIPED_ZIGZAG
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID  # too many segments
+    a.head_map = C.cast((C.c_int32 * 4)(0, 1, 2, 0), C.POINTER(C.c_int32))
+    t[0].q_pos.nseg = 1
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID  # head_map entry 2 >= hkv
+
+
+def test_merge_rejects_bad_arguments():
+    L = _abi.lib()
+    a = _abi.ma_merge_args()
+    a.dtype, a.batch, a.seqlen, a.heads, a.head_dim, a.k = _abi.MA_BF16, 1, 8, 2, 128, 0
+    assert L.mesh_attn_merge(C.byref(a), None) == _abi.MA_ERR_INVALID  # k = 0
+    a.k = _abi.MA_MAX_MERGE + 1
+    assert L.mesh_attn_merge(C.byref(a), None) == _abi.MA_ERR_INVALID  # k > 64
+    a.k, a.head_dim = 2, 80
+    assert L.mesh_attn_merge(C.byref(a), None) == _abi.MA_ERR_UNSUPPORTED
+    a.head_dim = 128
+    assert L.mesh_attn_merge(C.byref(a), None) == _abi.MA_ERR_INVALID  # null pointers
+
+
+def test_bwd_rejects_bad_arguments():
+    L = _abi.lib()
+    a = _abi.ma_tile_bwd_args()
+    a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.scale = _abi.MA_F32, 1, 2, 1, 128, 0.1
+    assert L.mesh_attn_tile_bwd(C.byref(a), None, 0, None) in (_abi.MA_ERR_UNSUPPORTED, _abi.MA_ERR_INVALID)
+    assert L.mesh_attn_tile_bwd(None, None, 0, None) == _abi.MA_ERR_INVALID
+
+
+def test_null_args():
+    L = _abi.lib()
+    assert L.mesh_attn_tile_fwd(None, None) == _abi.MA_ERR_INVALID
+    assert L.mesh_attn_merge(None, None) == _abi.MA_ERR_INVALID

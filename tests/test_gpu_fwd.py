@@ -1,0 +1,229 @@
+"""GPU parity of the tile forward and the LSE merge against the fp64 oracle (through the C ABI)."""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import distributed_long_context_amd as ma  # noqa: E402
+from distributed_long_context_amd import Pos, Tile  # noqa: E402
+from oracle import attn_tile, merge  # noqa: E402
+from gpu_helpers import (BF16_LSE_TOL, BF16_O_TOL, DEV, F32_TOL, check_close, gen, host_f64, log,  # noqa: E402
+                         positions)
+
+import synthetic  # noqa: E402
+
+
+def run_fwd(tiles, scale, mask, head_map=None):
+    ma.mesh_attn_tile_fwd(tiles, scale, mask, head_map)
+    torch.cuda.synchronize()
+
+
+def make_case(wid, sq, sk, hq, hkv, d, dtype="bf16", B=1, zero_q=False):
+    q, qv = gen(wid, synthetic.T_Q, 0, (B, sq, hq, d), dtype)
+    k, kv = gen(wid, synthetic.T_K, 0, (B, sk, hkv, d), dtype)
+    v, vv = gen(wid, synthetic.T_V, 0, (B, sk, hkv, d), dtype)
+    if zero_q:
+        q.zero_()
+        qv = np.zeros_like(qv)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o = torch.full((B, sq, hq, d), float("nan"), dtype=tdt, device=DEV)
+    lse = torch.full((B, hq, sq), float("nan"), dtype=torch.float32, device=DEV)
+    return (q, k, v, o, lse), (qv, kv, vv)
+
+
+def _two_seg(n, g0, g1, st1):
+    """Two-segment (zigzag-like) positions; one segment when the partition is too short to split."""
+    half = (n + 1) // 2
+    return Pos([(0, g0, 1), (half, g1, st1)]) if half < n else Pos([(0, g0, 1)])
+
+
+MASKS = {
+    "none": (ma.MA_MASK_NONE, None, None),
+    "causal_diag": (ma.MA_MASK_CAUSAL, lambda sq, sk: Pos([(0, 1000, 1)]), lambda sq, sk: Pos([(0, 1000, 1)])),
+    "causal_offset": (ma.MA_MASK_CAUSAL, lambda sq, sk: Pos([(0, 5000 + sk // 2, 1)]), lambda sq, sk: Pos([(0, 5000, 1)])),
+    "causal_future": (ma.MA_MASK_CAUSAL, lambda sq, sk: Pos([(0, 7, 1)]), lambda sq, sk: Pos([(0, 7 + sq // 3, 1)])),
+    "striped": (ma.MA_MASK_STRIPED_ZIGZAG, lambda sq, sk: ma.mesh_attn_pos_striped(4, 1),
+                lambda sq, sk: ma.mesh_attn_pos_striped(4, 3)),
+    "zigzag": (ma.MA_MASK_STRIPED_ZIGZAG, lambda sq, sk: _two_seg(sq, 0, 3 * sq, 1),
+               lambda sq, sk: _two_seg(sk, 0, 2 * sq, 2)),
+}
+
+SHAPES = [(1, 1), (17, 64), (64, 64), (100, 257), (257, 130), (300, 333), (128, 1000)]
+GQA = [(4, 4), (8, 4), (8, 2), (16, 2)]
+
+
+def _cases():
+    out = []
+    i = 0
+    for s in SHAPES:
+        for mname in MASKS:
+            hq, hkv = GQA[i % len(GQA)]
+            d = 128 if i % 3 else 64
+            out.append((s[0], s[1], hq, hkv, d, mname))
+            i += 1
+    return out
+
+
+@pytest.mark.parametrize("sq,sk,hq,hkv,d,mname", _cases())
+def test_fwd_bf16_small_shapes(sq, sk, hq, hkv, d, mname):
+    mode, qpf, kpf = MASKS[mname]
+    wid = 100 + sq * 7 + sk * 13 + hq + d
+    log(f"[fwd bf16] sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} mask={mname} seed={wid}")
+    (q, k, v, o, lse), (qv, kv, vv) = make_case(wid, sq, sk, hq, hkv, d)
+    qp = qpf(sq, sk) if qpf else None
+    kp = kpf(sq, sk) if kpf else None
+    scale = 1.0 / math.sqrt(d)
+    run_fwd([Tile(q, k, v, o, lse, qp, kp)], scale, mode)
+    causal = mode != ma.MA_MASK_NONE
+    Oref, Lref = attn_tile(qv, kv, vv, np.float32(scale), None, causal,
+                           positions(qp, sq) if causal else None, positions(kp, sk) if causal else None)
+    check_close("O", host_f64(o), Oref, BF16_O_TOL)
+    check_close("LSE", host_f64(lse), Lref, BF16_LSE_TOL)
+    # fully masked rows are exactly (0, -inf)
+    Og = host_f64(o)
+    for b, h, t in zip(*np.nonzero(np.isneginf(Lref))):
+        assert np.all(Og[b, t, h] == 0.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_bf16_head_map_and_batch(d):
+    sq, sk, hq, hkv, B = 130, 200, 6, 3, 2
+    head_map = [2, 0, 1, 1, 0, 2]
+    log(f"[fwd bf16 head_map] d={d} B={B}")
+    (q, k, v, o, lse), (qv, kv, vv) = make_case(300 + d, sq, sk, hq, hkv, d, B=B)
+    qp, kp = Pos([(0, 150, 1)]), Pos([(0, 0, 1)])
+    run_fwd([Tile(q, k, v, o, lse, qp, kp)], 0.09, ma.MA_MASK_CAUSAL, head_map)
+    Oref, Lref = attn_tile(qv, kv, vv, np.float32(0.09), head_map, True, positions(qp, sq), positions(kp, sk))
+    check_close("O", host_f64(o), Oref, BF16_O_TOL)
+    check_close("LSE", host_f64(lse), Lref, BF16_LSE_TOL)
+
+
+@pytest.mark.parametrize("mname", ["causal_diag", "causal_offset", "striped", "zigzag"])
+def test_mask_probe_counts_are_exact(mname):
+    # Q = 0 makes every score 0, so exp(LSE[t]) is the exact number of allowed keys.
+    mode, qpf, kpf = MASKS[mname]
+    sq, sk = 333, 517
+    log(f"[mask probe] {mname}")
+    (q, k, v, o, lse), (qv, kv, vv) = make_case(400, sq, sk, 8, 2, 128, zero_q=True)
+    qp, kp = qpf(sq, sk), kpf(sq, sk)
+    run_fwd([Tile(q, k, v, o, lse, qp, kp)], 0.125, mode)
+    L = host_f64(lse)
+    qa, ka = positions(qp, sq), positions(kp, sk)
+    n_ref = (ka[None, :] <= qa[:, None]).sum(axis=1)
+    for h in range(8):
+        n_gpu = np.where(np.isneginf(L[0, h]), 0, np.rint(np.exp(L[0, h]))).astype(np.int64)
+        assert np.array_equal(n_gpu, n_ref), mname
+
+
+def test_empty_tile_is_filled():
+    log("[fwd empty tile]")
+    (q, k, v, o, lse), _ = make_case(500, 64, 64, 4, 1, 128)
+    run_fwd([Tile(q, k, v, o, lse, Pos([(0, 0, 1)]), Pos([(0, 64, 1)]))], 0.1, ma.MA_MASK_CAUSAL)
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_many_tiles_one_call():
+    # more tiles than one launch packs; mixed classes (EMPTY, PARTIAL, FULL) in one call
+    log("[fwd many tiles]")
+    n, P, hq, hkv, d = 11, 96, 4, 2, 128
+    parts = [gen(600, synthetic.T_Q, i, (1, P, hq, d)) for i in range(n)]
+    kparts = [gen(600, synthetic.T_K, i, (1, P, hkv, d)) for i in range(n)]
+    vparts = [gen(600, synthetic.T_V, i, (1, P, hkv, d)) for i in range(n)]
+    tiles, refs = [], []
+    for i in range(n):
+        j = (i * 5) % n
+        o = torch.empty((1, P, hq, d), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((1, hq, P), dtype=torch.float32, device=DEV)
+        qp, kp = Pos([(0, i * P, 1)]), Pos([(0, j * P, 1)])
+        tiles.append(Tile(parts[i][0], kparts[j][0], vparts[j][0], o, lse, qp, kp))
+        refs.append(attn_tile(parts[i][1], kparts[j][1], vparts[j][1], np.float32(0.1), None, True,
+                              positions(qp, P), positions(kp, P)))
+    run_fwd(tiles, 0.1, ma.MA_MASK_CAUSAL)
+    for t, (Oref, Lref) in zip(tiles, refs):
+        check_close("O", host_f64(t.o), Oref, BF16_O_TOL, normalised_also=False)
+        check_close("LSE", host_f64(t.lse), Lref, BF16_LSE_TOL)
+
+
+def test_fp32_mha_s256_four_partitions():
+    # fp32, 1 head, d=64, S=256 in 4 partitions of 64: all 16 tiles, then a 4-way merge per Q partition,
+    # compared with unsplit attention (tolerance 1e-5 on O and LSE).
+    log("[fp32 s256 n4]")
+    S, n, d = 256, 4, 64
+    P = S // n
+    q, qv = gen(1, synthetic.T_Q, 0, (1, S, 1, d), "f32")
+    k, kv = gen(1, synthetic.T_K, 0, (1, S, 1, d), "f32")
+    v, vv = gen(1, synthetic.T_V, 0, (1, S, 1, d), "f32")
+    scale = np.float32(1.0 / math.sqrt(d))
+    tiles = []
+    for i in range(n):
+        for j in range(n):
+            o = torch.empty((1, P, 1, d), dtype=torch.float32, device=DEV)
+            lse = torch.empty((1, 1, P), dtype=torch.float32, device=DEV)
+            tiles.append(Tile(q[:, i * P:(i + 1) * P], k[:, j * P:(j + 1) * P], v[:, j * P:(j + 1) * P], o, lse))
+    run_fwd(tiles, float(scale), ma.MA_MASK_NONE)
+    for i in range(n):
+        for j in range(n):
+            Oref, Lref = attn_tile(qv[:, i * P:(i + 1) * P], kv[:, j * P:(j + 1) * P], vv[:, j * P:(j + 1) * P], scale)
+            t = tiles[i * n + j]
+            check_close(f"O[{i},{j}]", host_f64(t.o), Oref, F32_TOL, normalised_also=False)
+            check_close(f"LSE[{i},{j}]", host_f64(t.lse), Lref, F32_TOL)
+    Ofull, Lfull = attn_tile(qv, kv, vv, scale)
+    for i in range(n):
+        o_out = torch.empty((1, P, 1, d), dtype=torch.float32, device=DEV)
+        l_out = torch.empty((1, 1, P), dtype=torch.float32, device=DEV)
+        row = tiles[i * n:(i + 1) * n]
+        ma.mesh_attn_merge([t.o for t in row], [t.lse for t in row], o_out, l_out)
+        torch.cuda.synchronize()
+        check_close(f"merged O[{i}]", host_f64(o_out), Ofull[:, i * P:(i + 1) * P], F32_TOL, normalised_also=False)
+        check_close(f"merged LSE[{i}]", host_f64(l_out), Lfull[:, :, i * P:(i + 1) * P], F32_TOL)
+
+
+@pytest.mark.parametrize("k,dtype,d", [(1, "bf16", 128), (2, "bf16", 64), (6, "bf16", 128), (27, "bf16", 128),
+                                       (64, "bf16", 128), (5, "f32", 64), (9, "f32", 128)])
+def test_merge_matches_oracle(k, dtype, d):
+    B, S, H = 2, 77, 3
+    log(f"[merge] k={k} dtype={dtype} d={d}")
+    wid = 700 + k
+    Os, Ls, Oh, Lh = [], [], [], []
+    for r in range(k):
+        o, ov = gen(wid, synthetic.T_O_IN, r, (B, S, H, d), dtype)
+        lv = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, r, (B, H, S)) * 3 + 10).astype(np.float32)
+        if r == 1:  # rows that one partial did not reach
+            lv[:, 0, :10] = -np.inf
+        if r < 3 and k > 3:
+            lv[:, 1, 5] = -np.inf
+        Os.append(o); Oh.append(ov)
+        Ls.append(torch.from_numpy(lv).to(DEV)); Lh.append(lv.astype(np.float64))
+    if k > 3:  # one row with every partial empty
+        for r in range(k):
+            Ls[r][0, 2, 7] = float("-inf"); Lh[r][0, 2, 7] = -np.inf
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o_out = torch.empty((B, S, H, d), dtype=tdt, device=DEV)
+    l_out = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    ma.mesh_attn_merge(Os, Ls, o_out, l_out)
+    torch.cuda.synchronize()
+    Oref, Lref = merge(list(zip(Oh, Lh)))
+    tol_o, tol_l = (BF16_O_TOL, BF16_LSE_TOL) if dtype == "bf16" else (F32_TOL, F32_TOL)
+    check_close("O", host_f64(o_out), Oref, tol_o, normalised_also=False)
+    check_close("LSE", host_f64(l_out), Lref, tol_l)
+    if k > 3:
+        assert torch.all(o_out[0, 7, 2].float() == 0)
+
+
+def test_merge_in_place():
+    log("[merge in place]")
+    B, S, H, d, k = 1, 50, 2, 128, 4
+    Os, Ls, Oh, Lh = [], [], [], []
+    for r in range(k):
+        o, ov = gen(800, synthetic.T_O_IN, r, (B, S, H, d))
+        lv = synthetic.normal_f32(800, synthetic.T_LSE_IN, r, (B, H, S)) + 5
+        Os.append(o); Oh.append(ov); Ls.append(torch.from_numpy(lv).to(DEV)); Lh.append(lv.astype(np.float64))
+    Oref, Lref = merge(list(zip(Oh, Lh)))
+    ma.mesh_attn_merge(Os, Ls, Os[0], Ls[0])
+    torch.cuda.synchronize()
+    check_close("O", host_f64(Os[0]), Oref, BF16_O_TOL, normalised_also=False)
+    check_close("LSE", host_f64(Ls[0]), Lref, BF16_LSE_TOL)
