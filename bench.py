@@ -1,0 +1,213 @@
+"""Bench of one GPU's share: tile forward + LSE merge + tile backward on MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input,
+at the single-tile GQA shape (Q partition 8192 x KV partition 8192 tokens,
+32 query / 8 KV heads, head_dim 128, bf16, non-causal):
+
+  1. host mapping and tile classification (C++ mapper through the C ABI);
+  2. mesh_attn_tile_fwd  -> partial O (bf16) and LSE (fp32);
+  3. mesh_attn_merge     -> folds the partial with one incoming seeded partial
+                            (the rest of the row's KV, as another GPU would send);
+  4. mesh_attn_tile_bwd  -> dQ, dK, dV (fp32) from the merged O and LSE and a
+                            seeded dO (this KV partition's share of the gradient).
+
+Prints ONE JSON line.  `value` is the whole step's algorithmic tile FLOPs per
+second (forward 4*d*Hq and backward 10*d*Hq per allowed pair), inputs already
+resident in HBM.  Per-kernel times come from events recorded on the stream the
+kernels are launched on (torch's current stream, which the binding passes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tile fwd/bwd TFLOP/s + % bf16 MFMA peak; merge GB/s + % HBM peak (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+SQ = SK = 8192
+HQ, HKV, D = 32, 8, 128
+WORKLOAD_ID = 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle sample")
+    ap.add_argument("--parts", default="fwd,merge,bwd", help="kernels in the step (all by default)")
+    return ap.parse_args()
+
+
+def cpu_baseline(rows, scale):
+    """The fp64 oracle on a bounded sample of the same workload: `rows` query rows x 32 heads,
+    forward over all 8192 keys, the merge with the incoming partial, and the backward."""
+    import numpy as np
+    import synthetic
+    from oracle import attn_tile, merge, attn_tile_bwd
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    _, qv = synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_Q, 0, (1, SQ, HQ, D))
+    _, kv = synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_K, 0, (1, SK, HKV, D))
+    _, vv = synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_V, 0, (1, SK, HKV, D))
+    _, dov = synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_DO, 0, (1, SQ, HQ, D))
+    _, oin = synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_O_IN, 0, (1, SQ, HQ, D))
+    lin = incoming_lse()
+    sel = np.arange(rows)
+    q = qv[:, sel]
+    t0 = time.perf_counter()
+    O, L = attn_tile(q, kv, vv, scale)
+    Om, Lm = merge([(O, L), (oin[:, sel], lin[:, :, sel])])
+    attn_tile_bwd(q, kv, vv, Om, dov[:, sel], Lm, scale)
+    dt = time.perf_counter() - t0
+    flops = (4 + 10) * D * HQ * rows * SK
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {SQ} query rows x {HQ} heads against all {SK} keys: forward, 2-way merge, "
+                      f"backward in float64 NumPy ({dt:.1f} s; cpu {platform.processor() or platform.machine()}, "
+                      f"{len(os.sched_getaffinity(0))} host cores visible)"}
+
+
+def incoming_lse():
+    """LSE of the incoming partial: ln(8192) + 0.5 + N(0,1), float32 (seeded)."""
+    import numpy as np
+    import synthetic
+    mu = math.log(SK) + 0.5
+    return (synthetic.normal_f32(WORKLOAD_ID, synthetic.T_LSE_IN, 0, (1, HQ, SQ)) + np.float32(mu)).astype(np.float32)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share on one GPU; --gpus above 1 is not supported "
+              "(this build runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synthetic
+    import distributed_long_context_amd as ma
+    from distributed_long_context_amd import Pos, Tile, BwdTile
+
+    parts = set(args.parts.split(","))
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    q = bf16(synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_Q, 0, (1, SQ, HQ, D))[0])
+    k = bf16(synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_K, 0, (1, SK, HKV, D))[0])
+    v = bf16(synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_V, 0, (1, SK, HKV, D))[0])
+    dO = bf16(synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_DO, 0, (1, SQ, HQ, D))[0])
+    o_in = bf16(synthetic.normal_bf16(WORKLOAD_ID, synthetic.T_O_IN, 0, (1, SQ, HQ, D))[0])
+    lse_in = torch.from_numpy(incoming_lse()).to(dev)
+    o = torch.empty((1, SQ, HQ, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, HQ, SQ), dtype=torch.float32, device=dev)
+    o_m = torch.empty_like(o)
+    lse_m = torch.empty_like(lse)
+    dq = torch.empty((1, SQ, HQ, D), dtype=torch.float32, device=dev)
+    dk = torch.empty((1, SK, HKV, D), dtype=torch.float32, device=dev)
+    dv = torch.empty((1, SK, HKV, D), dtype=torch.float32, device=dev)
+    q_pos, k_pos = ma.mesh_attn_pos_contiguous(0), ma.mesh_attn_pos_contiguous(0)
+    bwd_tiles = [BwdTile(q, k, v, o_m, dO, lse_m, dq, dk, dv, q_pos, k_pos)]
+    ws = None
+    if "bwd" in parts:
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(bwd_tiles, scale)), dtype=torch.uint8, device=dev)
+
+    pairs = ma.mesh_attn_count_allowed(q_pos, SQ, k_pos, SK, ma.MA_MASK_NONE)
+    fwd_flop = 4.0 * D * HQ * pairs
+    bwd_flop = 10.0 * D * HQ * pairs
+    merge_bytes = 2 * (SQ * HQ * D * 2 + HQ * SQ * 4) + (SQ * HQ * D * 2 + HQ * SQ * 4)
+
+    stream = torch.cuda.current_stream()
+    evs = []
+
+    def step(record):
+        # (1) host mapping: the tile list for this GPU's share (one non-causal pair)
+        wl = ma.mesh_attn_build_worklist([q_pos], [SQ], [k_pos], [SK], ma.MA_MASK_NONE)
+        assert wl == [(0, 0, ma.MA_TILE_FULL)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        if "fwd" in parts:
+            ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, q_pos, k_pos)], scale, ma.MA_MASK_NONE)
+        if record:
+            e[1].record(stream)
+        if "merge" in parts:
+            ma.mesh_attn_merge([o, o_in], [lse, lse_in], o_m, lse_m)
+        if record:
+            e[2].record(stream)
+        if "bwd" in parts:
+            ma.mesh_attn_tile_bwd(bwd_tiles, scale, ma.MA_MASK_NONE, workspace=ws)
+        if record:
+            e[3].record(stream)
+            evs.append(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+    merge_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / len(evs)
+    step_flop = (fwd_flop if "fwd" in parts else 0) + (bwd_flop if "bwd" in parts else 0)
+    value = step_flop / (ms_step * 1e-3) / 1e12
+
+    res_parts = {}
+    if "fwd" in parts:
+        t = fwd_flop / (fwd_ms * 1e-3) / 1e12
+        res_parts["tile_fwd"] = {"ms": round(fwd_ms, 4), "TFLOP/s": round(t, 1), "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4),
+                                 "flop": fwd_flop}
+    if "merge" in parts:
+        g = merge_bytes / (merge_ms * 1e-3) / 1e9
+        res_parts["merge"] = {"ms": round(merge_ms, 4), "GB/s": round(g, 1), "frac_hbm_peak": round(g / PEAK_HBM_GBPS, 4),
+                              "bytes": merge_bytes, "k": 2}
+    if "bwd" in parts:
+        t = bwd_flop / (bwd_ms * 1e-3) / 1e12
+        res_parts["tile_bwd"] = {"ms": round(bwd_ms, 4), "TFLOP/s": round(t, 1), "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4),
+                                 "flop": bwd_flop, "includes": "D=rowsum(dO*O) preprocessing"}
+    # dominant kernel by time
+    dom = max(((n, p["ms"]) for n, p in res_parts.items()), key=lambda x: x[1])[0]
+    if dom == "merge":
+        rl = {"bound": "hbm", "achieved": res_parts["merge"]["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+              "frac": res_parts["merge"]["frac_hbm_peak"], "traffic": None, "kernel": "merge"}
+    else:
+        rl = {"bound": "mfma", "achieved": res_parts[dom]["TFLOP/s"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+              "frac": res_parts[dom]["frac_bf16_peak"], "traffic": None, "kernel": dom}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gqa-tile-8k: one non-causal (Q 8192 x KV 8192) tile, 32/8 heads, d=128, bf16; "
+                               "fwd + 2-way LSE merge + bwd", "batch": 1, "q_tokens": SQ, "kv_tokens": SK,
+                   "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "mask": "none", "steps_parts": sorted(parts)},
+        "roofline": rl, "parts": res_parts,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows, np.float32(scale))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
