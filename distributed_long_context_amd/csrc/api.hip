@@ -244,9 +244,136 @@ size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* a) {
 }
 
 int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace; (void)workspace_bytes; (void)stream;
   if (!a) return set_error(MA_ERR_INVALID, "null args");
-  return set_error(MA_ERR_UNSUPPORTED, "tile_bwd: not built yet");
+  if (a->dtype != MA_BF16) return set_error(a->dtype == MA_F32 ? MA_ERR_UNSUPPORTED : MA_ERR_INVALID,
+                                            "tile_bwd supports bf16 inputs only");
+  int rc = check_common(a->dtype, a->batch, a->hq, a->hkv, a->head_dim, a->mask_mode, a->scale);
+  if (rc) return rc;
+  if (!a->head_map && a->hq % a->hkv) return set_error(MA_ERR_INVALID, "hq must be a multiple of hkv when head_map is NULL");
+  if (a->ntiles < 0 || a->ntiles > MA_MAX_TILES) return set_error(MA_ERR_INVALID, "ntiles out of range");
+  if (a->ntiles == 0) return MA_OK;
+  if (!a->tiles) return set_error(MA_ERR_INVALID, "null tile list");
+  if (!strides_ok(a->q_stride, 3, MA_BF16) || !strides_ok(a->k_stride, 3, MA_BF16) ||
+      !strides_ok(a->dq_stride, 3, MA_F32) || !strides_ok(a->dk_stride, 3, MA_F32) || a->lse_stride[0] < 0 ||
+      a->lse_stride[1] < 0)
+    return set_error(MA_ERR_INVALID, "strides must be >= 0 and multiples of 16 bytes");
+  const size_t need = mesh_attn_tile_bwd_workspace_size(a);
+  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & 255u))
+    return set_error(MA_ERR_INVALID, "workspace missing, too small or not 256-byte aligned");
+  for (int i = 0; i < a->ntiles; ++i) {
+    const ma_bwd_tile& t = a->tiles[i];
+    if (!t.q || !t.k || !t.v || !t.o || !t.dout || !t.lse || !t.dq || !t.dk || !t.dv)
+      return set_error(MA_ERR_INVALID, "null tensor pointer in a tile");
+    if (!aligned16(t.q) || !aligned16(t.k) || !aligned16(t.v) || !aligned16(t.o) || !aligned16(t.dout) ||
+        !aligned16(t.dq) || !aligned16(t.dk) || !aligned16(t.dv) || ((uintptr_t)t.lse & 3u))
+      return set_error(MA_ERR_INVALID, "tensor pointers must be 16-byte aligned (lse 4-byte)");
+    if (t.sq < 1 || t.sk < 1 || t.sq >= INT32_MAX || t.sk >= INT32_MAX)
+      return set_error(MA_ERR_INVALID, "tile sizes must be in [1, 2^31-1)");
+    rc = check_positions(a->mask_mode, t.q_pos, t.sq, t.k_pos, t.sk);
+    if (rc) return rc;
+    for (int j = 0; j < i; ++j) {  // tiles sharing dk or dv must share the whole KV description
+      const ma_bwd_tile& u = a->tiles[j];
+      if ((u.dk == t.dk || u.dv == t.dv || u.dk == t.dv || u.dv == t.dk) &&
+          (u.dk != t.dk || u.dv != t.dv || u.k != t.k || u.v != t.v || u.sk != t.sk ||
+           (a->mask_mode != MA_MASK_NONE && std::memcmp(&u.k_pos, &t.k_pos, sizeof(ma_pos)) != 0)))
+        return set_error(MA_ERR_INVALID, "tiles naming the same dk/dv must name the same k, v, sk and k_pos");
+    }
+  }
+
+  BwdParams base;
+  std::memset(&base, 0, sizeof(base));
+  const char* why = nullptr;
+  base.gmax = build_head_groups(a->hq, a->hkv, a->head_map, base.heads_of, base.kv_first, &why);
+  if (base.gmax < 0) return set_error(MA_ERR_INVALID, why);
+  base.batch = a->batch;
+  base.hq = a->hq;
+  base.hkv = a->hkv;
+  base.mask = a->mask_mode != MA_MASK_NONE;
+  base.scale = a->scale;
+  base.scale_log2 = a->scale * 1.4426950408889634f;
+  base.q_sb = a->q_stride[0]; base.q_ss = a->q_stride[1]; base.q_sh = a->q_stride[2];
+  base.k_sb = a->k_stride[0]; base.k_ss = a->k_stride[1]; base.k_sh = a->k_stride[2];
+  base.dq_sb = a->dq_stride[0]; base.dq_ss = a->dq_stride[1]; base.dq_sh = a->dq_stride[2];
+  base.dk_sb = a->dk_stride[0]; base.dk_ss = a->dk_stride[1]; base.dk_sh = a->dk_stride[2];
+  base.l_sb = a->lse_stride[0]; base.l_sh = a->lse_stride[1];
+
+  // per-tile kernel view (D goes to the tile's slice of the workspace)
+  std::vector<BwdTile> bt(a->ntiles);
+  size_t off = 0;
+  for (int i = 0; i < a->ntiles; ++i) {
+    const ma_bwd_tile& t = a->tiles[i];
+    BwdTile& x = bt[i];
+    std::memset(&x, 0, sizeof(x));
+    x.q = t.q; x.o = t.o; x.dout = t.dout; x.lse = t.lse; x.dq = t.dq;
+    x.dscratch = (float*)((char*)workspace + off);
+    off += ((size_t)a->batch * a->hq * t.sq * sizeof(float) + 255) / 256 * 256;
+    x.sq = (int32_t)t.sq;
+    x.zero_dq = a->accumulate ? 0 : 1;
+    if (a->mask_mode != MA_MASK_NONE) to_kpos(t.q_pos, x.qp);
+    else x.qp.nseg = 1;
+  }
+  // 1) D for every tile and cleared dQ, before any main launch (tiles may share a dq buffer)
+  for (int i0 = 0; i0 < a->ntiles; i0 += kBwdTilesPerLaunch) {
+    BwdParams p = base;
+    p.ntiles = std::min(kBwdTilesPerLaunch, a->ntiles - i0);
+    for (int j = 0; j < p.ntiles; ++j) p.tiles[j] = bt[i0 + j];
+    rc = check_hip(launch_bwd_preprocess(p, a->head_dim, stream), "tile_bwd preprocess launch");
+    if (rc) return rc;
+  }
+  // 2) group tiles by KV partition (same dk buffer); split each group into entries of <= 8 tiles
+  struct Entry { int group; int first_tile_pos; int n; int accumulate; };
+  std::vector<int> group_of(a->ntiles, -1);
+  std::vector<std::vector<int>> groups;
+  for (int i = 0; i < a->ntiles; ++i) {
+    for (int j = 0; j < i; ++j)
+      if (a->tiles[j].dk == a->tiles[i].dk) { group_of[i] = group_of[j]; break; }
+    if (group_of[i] < 0) { group_of[i] = (int)groups.size(); groups.emplace_back(); }
+    groups[group_of[i]].push_back(i);
+  }
+  std::vector<Entry> entries;
+  for (int g = 0; g < (int)groups.size(); ++g)
+    for (int s0 = 0; s0 < (int)groups[g].size(); s0 += kBwdTilesPerLaunch)
+      entries.push_back({g, s0, std::min(kBwdTilesPerLaunch, (int)groups[g].size() - s0),
+                         (s0 == 0) ? (a->accumulate ? 1 : 0) : 1});
+  // 3) pack entries into launches: <= 8 tiles, <= 8 entries, one entry per group per launch
+  size_t e0 = 0;
+  while (e0 < entries.size()) {
+    BwdParams p = base;
+    int nt = 0, nk = 0, wg = 0;
+    std::vector<int> used_groups;
+    size_t e = e0;
+    for (; e < entries.size(); ++e) {
+      const Entry& en = entries[e];
+      if (nk == kBwdTilesPerLaunch || nt + en.n > kBwdTilesPerLaunch) break;
+      if (std::find(used_groups.begin(), used_groups.end(), en.group) != used_groups.end()) break;
+      used_groups.push_back(en.group);
+      const ma_bwd_tile& t0 = a->tiles[groups[en.group][en.first_tile_pos]];
+      BwdKV& kv = p.kvs[nk];
+      kv.k = t0.k; kv.v = t0.v; kv.dk = t0.dk; kv.dv = t0.dv;
+      kv.sk = (int32_t)t0.sk;
+      kv.ntiles = en.n;
+      kv.accumulate = en.accumulate;
+      if (a->mask_mode != MA_MASK_NONE) to_kpos(t0.k_pos, kv.kp);
+      else kv.kp.nseg = 1;
+      for (int j = 0; j < en.n; ++j) {
+        p.tiles[nt] = bt[groups[en.group][en.first_tile_pos + j]];
+        kv.tile_idx[j] = nt++;
+      }
+      const int64_t nkb = (t0.sk + 127) / 128;
+      int64_t wgs = (int64_t)a->batch * a->hkv * nkb;
+      wgs = (wgs + 7) / 8 * 8;  // keep each KV partition's first workgroup on XCD 0
+      if (wg + wgs >= INT32_MAX) return set_error(MA_ERR_INVALID, "backward too large for one launch");
+      kv.wg_begin = wg;
+      wg += (int)wgs;
+      ++nk;
+    }
+    p.nkv = nk;
+    p.ntiles = nt;
+    rc = check_hip(launch_bwd_main(p, a->head_dim, wg, stream), "tile_bwd launch");
+    if (rc) return rc;
+    e0 = e;
+  }
+  return MA_OK;
 }
 
 }  // extern "C"

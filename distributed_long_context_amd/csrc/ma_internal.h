@@ -85,6 +85,7 @@ struct BwdTile {
   float* dq;
   float* dscratch;  // D = rowsum(dO*O), [B, Hq, sq] float32 in the workspace
   int32_t sq;
+  int32_t zero_dq;  // clear dq in the preprocessing pass (overwrite mode)
   KPos qp;
 };
 
@@ -95,6 +96,8 @@ struct BwdKV {  // one KV partition with the tiles that read it
   float* dv;
   int32_t sk;
   int32_t ntiles;
+  int32_t wg_begin;    // first workgroup of this KV partition in the launch
+  int32_t accumulate;  // add dK/dV to the buffers instead of overwriting
   int32_t tile_idx[kBwdTilesPerLaunch];
   KPos kp;
 };
@@ -116,7 +119,6 @@ struct BwdParams {
   BwdKV kvs[kBwdTilesPerLaunch];
 };
 int launch_bwd_preprocess(const BwdParams& p, int head_dim, void* stream);
-int launch_bwd_dkdv(const BwdParams& p, int head_dim, void* stream);
-int launch_bwd_dq(const BwdParams& p, int head_dim, void* stream);
+int launch_bwd_main(const BwdParams& p, int head_dim, int total_wgs, void* stream);
 
 }  // namespace ma

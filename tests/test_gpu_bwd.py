@@ -1,0 +1,167 @@
+"""GPU parity of the tile backward against the fp64 oracle (through the C ABI).
+
+O and LSE given to the backward are the oracle's forward, rounded to their
+stored types (bf16 O, fp32 LSE); both sides read the same stored values.
+Tolerance (the pages give none for gradients): max abs error <= 2e-2 * max(max|ref|, 1e-3)
+per output tensor, the bf16 O bar applied relative to the gradient's scale (the floor
+covers references that are exactly zero by a closed form, e.g. dQ with a single key).
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import distributed_long_context_amd as ma  # noqa: E402
+from distributed_long_context_amd import BwdTile, Pos  # noqa: E402
+from oracle import attn_tile, attn_tile_bwd, merge  # noqa: E402
+from gpu_helpers import DEV, dev_bf16, gen, host_f64, log, positions  # noqa: E402
+
+import synthetic  # noqa: E402
+
+GRAD_REL_TOL = 2e-2
+
+
+def stored_o_lse(O, L):
+    """Round the oracle's O to bf16 and LSE to fp32 (the stored inputs of the backward)."""
+    ob = synthetic.f32_to_bf16_bits(O.astype(np.float32))
+    return dev_bf16(ob), synthetic.bf16_bits_to_f32(ob).astype(np.float64), \
+        torch.from_numpy(L.astype(np.float32)).to(DEV), L.astype(np.float32).astype(np.float64)
+
+
+def check_grad(name, got, ref):
+    got = host_f64(got)
+    assert not np.isnan(got).any(), f"{name}: NaN"
+    scale = max(float(np.max(np.abs(ref))), 1e-3)
+    err = float(np.max(np.abs(got - ref)))
+    rms = float(np.sqrt(np.mean((got - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
+    log(f"  {name}: max_abs_err={err:.3e} max|ref|={scale:.3e} rel={err/scale:.2e} rel_rms={rms:.2e}")
+    assert err <= GRAD_REL_TOL * scale, f"{name}: {err} > {GRAD_REL_TOL} * {scale}"
+
+
+def run_case(wid, sq, sk, hq, hkv, d, mode=ma.MA_MASK_NONE, qp=None, kp=None, head_map=None, B=1, ntiles=1):
+    causal = mode != ma.MA_MASK_NONE
+    k, kv = gen(wid, synthetic.T_K, 0, (B, sk, hkv, d))
+    v, vv = gen(wid, synthetic.T_V, 0, (B, sk, hkv, d))
+    scale = np.float32(1.0 / math.sqrt(d))
+    kpos = positions(kp, sk) if causal else None
+    dk = torch.full((B, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full_like(dk, float("nan"))
+    tiles, refs = [], []
+    for i in range(ntiles):
+        q, qv = gen(wid, synthetic.T_Q, i, (B, sq, hq, d))
+        do, dov = gen(wid, synthetic.T_DO, i, (B, sq, hq, d))
+        qpi = qp[i] if isinstance(qp, list) else qp
+        qpos = positions(qpi, sq) if causal else None
+        O, L = attn_tile(qv, kv, vv, scale, head_map, causal, qpos, kpos)
+        o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+        dq = torch.full((B, sq, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+        tiles.append(BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv, qpi, kp))
+        refs.append(dict(q=qv, o=o_used, do=dov, lse=l_used, q_pos=qpos))
+    ma.mesh_attn_tile_bwd(tiles, float(scale), mode, head_map)
+    torch.cuda.synchronize()
+    dk_ref = dv_ref = None
+    for t, r in zip(tiles, refs):
+        dq_r, dk_r, dv_r = attn_tile_bwd(r["q"], kv, vv, r["o"], r["do"], r["lse"], scale, head_map, causal,
+                                         r["q_pos"], kpos)
+        check_grad("dQ", t.dq, dq_r)
+        dk_ref = dk_r if dk_ref is None else dk_ref + dk_r
+        dv_ref = dv_r if dv_ref is None else dv_ref + dv_r
+    check_grad("dK", dk, dk_ref)
+    check_grad("dV", dv, dv_ref)
+    return tiles
+
+
+SHAPES = [(1, 1), (17, 64), (64, 128), (100, 257), (257, 130), (300, 333), (128, 1000)]
+GQA = [(4, 4), (8, 4), (8, 2), (16, 2), (4, 1)]
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(SHAPES)))
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_noncausal_shapes(i, shape, d):
+    sq, sk = shape
+    hq, hkv = GQA[i % len(GQA)]
+    log(f"[bwd] sq={sq} sk={sk} hq={hq} hkv={hkv} d={d}")
+    run_case(1000 + i * 10 + d, sq, sk, hq, hkv, d)
+
+
+MASKS = [
+    ("causal_diag", ma.MA_MASK_CAUSAL, lambda sq, sk: Pos([(0, 500, 1)]), lambda sq, sk: Pos([(0, 500, 1)])),
+    ("causal_offset", ma.MA_MASK_CAUSAL, lambda sq, sk: Pos([(0, 900 + sk // 3, 1)]), lambda sq, sk: Pos([(0, 900, 1)])),
+    ("causal_future", ma.MA_MASK_CAUSAL, lambda sq, sk: Pos([(0, 0, 1)]), lambda sq, sk: Pos([(0, sq // 2, 1)])),
+    ("striped", ma.MA_MASK_STRIPED_ZIGZAG, lambda sq, sk: Pos([(0, 2, 4)]), lambda sq, sk: Pos([(0, 1, 4)])),
+    ("zigzag", ma.MA_MASK_STRIPED_ZIGZAG, lambda sq, sk: Pos([(0, 0, 1), (sq // 2, 3 * sq, 1)]),
+     lambda sq, sk: Pos([(0, 0, 1), (sk // 2, 2 * sq, 1)])),
+]
+
+
+@pytest.mark.parametrize("name,mode,qpf,kpf", MASKS, ids=[m[0] for m in MASKS])
+@pytest.mark.parametrize("shape", [(200, 300), (129, 257)])
+def test_bwd_masks(name, mode, qpf, kpf, shape):
+    sq, sk = shape
+    log(f"[bwd mask] {name} sq={sq} sk={sk}")
+    run_case(1100 + sq + sk, sq, sk, 8, 2, 128, mode, qpf(sq, sk), kpf(sq, sk))
+
+
+def test_bwd_head_map_batch():
+    log("[bwd head_map batch]")
+    run_case(1200, 150, 190, 6, 3, 128, ma.MA_MASK_CAUSAL, Pos([(0, 100, 1)]), Pos([(0, 0, 1)]),
+             head_map=[1, 2, 0, 0, 2, 1], B=2)
+
+
+def test_bwd_many_q_tiles_share_kv():
+    # dK/dV summed over several Q partitions (more than one launch packs)
+    log("[bwd 11 q tiles]")
+    qps = [Pos([(0, 100 * i, 1)]) for i in range(11)]
+    run_case(1300, 96, 200, 8, 2, 128, ma.MA_MASK_CAUSAL, qps, Pos([(0, 0, 1)]), ntiles=11)
+
+
+def test_bwd_accumulate_adds():
+    log("[bwd accumulate]")
+    sq, sk, hq, hkv, d = 70, 90, 4, 2, 128
+    wid = 1400
+    q, qv = gen(wid, synthetic.T_Q, 0, (1, sq, hq, d))
+    k, kv = gen(wid, synthetic.T_K, 0, (1, sk, hkv, d))
+    v, vv = gen(wid, synthetic.T_V, 0, (1, sk, hkv, d))
+    do, dov = gen(wid, synthetic.T_DO, 0, (1, sq, hq, d))
+    scale = np.float32(0.1)
+    O, L = attn_tile(qv, kv, vv, scale)
+    o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+    dq = torch.ones((1, sq, hq, d), dtype=torch.float32, device=DEV)
+    dk = torch.ones((1, sk, hkv, d), dtype=torch.float32, device=DEV) * 2
+    dv = torch.ones((1, sk, hkv, d), dtype=torch.float32, device=DEV) * 3
+    ma.mesh_attn_tile_bwd([BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv)], float(scale), accumulate=True)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = attn_tile_bwd(qv, kv, vv, o_used, dov, l_used, scale)
+    check_grad("dQ+1", dq, dq_r + 1)
+    check_grad("dK+2", dk, dk_r + 2)
+    check_grad("dV+3", dv, dv_r + 3)
+
+
+def test_bwd_distributed_share():
+    # The row's final O and LSE come from a merge over two KV partitions; the backward of one
+    # partition with them gives that partition's share ([Mesh] section 3.5).
+    log("[bwd distributed share]")
+    sq, sk, hq, hkv, d = 160, 256, 8, 2, 128
+    wid = 1500
+    q, qv = gen(wid, synthetic.T_Q, 0, (1, sq, hq, d))
+    kA, kAv = gen(wid, synthetic.T_K, 0, (1, sk, hkv, d))
+    vA, vAv = gen(wid, synthetic.T_V, 0, (1, sk, hkv, d))
+    _, kBv = gen(wid, synthetic.T_K, 1, (1, sk, hkv, d))
+    _, vBv = gen(wid, synthetic.T_V, 1, (1, sk, hkv, d))
+    do, dov = gen(wid, synthetic.T_DO, 0, (1, sq, hq, d))
+    scale = np.float32(1 / math.sqrt(d))
+    O, L = merge([attn_tile(qv, kAv, vAv, scale), attn_tile(qv, kBv, vBv, scale)])
+    o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+    dq = torch.empty((1, sq, hq, d), dtype=torch.float32, device=DEV)
+    dk = torch.empty((1, sk, hkv, d), dtype=torch.float32, device=DEV)
+    dv = torch.empty_like(dk)
+    ma.mesh_attn_tile_bwd([BwdTile(q, kA, vA, o_dev, do, l_dev, dq, dk, dv)], float(scale))
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = attn_tile_bwd(qv, kAv, vAv, o_used, dov, l_used, scale)
+    check_grad("dQ share", dq, dq_r)
+    check_grad("dK", dk, dk_r)
+    check_grad("dV", dv, dv_r)
