@@ -1,0 +1,217 @@
+"""Full-size parity of the five workloads, in the launch configuration the bench uses.
+
+At these sizes the oracle checks sampled outputs: each output row depends only
+on its own query row (forward, merge, dQ) and each dK/dV row only on its own
+key, so sampled rows and keys are checked exactly against the fp64 oracle, and
+properties that hold at any size are checked on every row.
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import distributed_long_context_amd as ma  # noqa: E402
+from distributed_long_context_amd import BwdTile, Pos, Tile  # noqa: E402
+from oracle import attn_tile, attn_tile_bwd, merge, layout  # noqa: E402
+from gpu_helpers import (BF16_LSE_TOL, BF16_O_TOL, DEV, check_close, dev_bf16, gen, host_f64, log,  # noqa: E402
+                         positions)
+
+import synthetic  # noqa: E402
+
+HQ, HKV, D = 32, 8, 128
+SCALE = np.float32(1.0 / math.sqrt(D))
+
+
+def sample_rows(n, wid, extra=16):
+    rng = np.random.default_rng([wid, 77])
+    fixed = [0, 1, 31, 32, 63, 64, 127, n // 2, n - 65, n - 64, n - 2, n - 1]
+    rows = sorted(set([r for r in fixed if 0 <= r < n] + list(rng.choice(n, size=min(extra, n), replace=False))))
+    return np.array(rows, dtype=np.int64)
+
+
+def empty_out(sq):
+    return (torch.empty((1, sq, HQ, D), dtype=torch.bfloat16, device=DEV),
+            torch.empty((1, HQ, sq), dtype=torch.float32, device=DEV))
+
+
+def test_gqa_tile_8k_forward():
+    # single non-causal tile, Q 8192 x KV 8192, 32/8 heads, d=128, bf16
+    wid, S = 2, 8192
+    log("[workload gqa-tile-8k fwd]")
+    q, qv = gen(wid, synthetic.T_Q, 0, (1, S, HQ, D))
+    k, kv = gen(wid, synthetic.T_K, 0, (1, S, HKV, D))
+    v, vv = gen(wid, synthetic.T_V, 0, (1, S, HKV, D))
+    o, lse = empty_out(S)
+    p0 = ma.mesh_attn_pos_contiguous(0)
+    ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, p0, p0)], float(SCALE), ma.MA_MASK_NONE)
+    torch.cuda.synchronize()
+    rows = sample_rows(S, wid)
+    Oref, Lref = attn_tile(qv, kv, vv, SCALE, rows=rows)
+    Og, Lg = host_f64(o), host_f64(lse)
+    check_close("O[rows]", Og[:, rows], Oref, BF16_O_TOL)
+    check_close("LSE[rows]", Lg[:, :, rows], Lref, BF16_LSE_TOL)
+    # every row: finite, and each output is a convex combination of the V column values
+    assert np.isfinite(Og).all() and np.isfinite(Lg).all()
+    vmax = np.abs(vv).max(axis=1)                      # [1, Hkv, d]
+    bound = np.repeat(vmax, HQ // HKV, axis=1)         # [1, Hq, d]
+    assert (np.abs(Og) <= bound[:, None] * (1 + 2 ** -7) + 1e-6).all()
+
+
+def test_zigzag_causal_128k_rank5_forward_and_merge():
+    # S = 131072 in 32 chunks of 4096; rank 5 of 16 owns chunks {5, 26}; causal on global positions
+    wid, N, r, C = 3, 16, 5, 4096
+    log("[workload zigzag-causal-128k]")
+    qchunks = ma.mesh_attn_map_zigzag(N, r)
+    assert qchunks == layout.zigzag_chunks(N, r) == (5, 26)
+    Q = {c: gen(wid, synthetic.T_Q, c, (1, C, HQ, D)) for c in qchunks}
+    K = [gen(wid, synthetic.T_K, j, (1, C, HKV, D)) for j in range(2 * N)]
+    V = [gen(wid, synthetic.T_V, j, (1, C, HKV, D)) for j in range(2 * N)]
+    qpos = [ma.mesh_attn_pos_contiguous(c * C) for c in qchunks]
+    kpos = [ma.mesh_attn_pos_contiguous(j * C) for j in range(2 * N)]
+    wl = ma.mesh_attn_build_worklist(qpos, [C, C], kpos, [C] * (2 * N), ma.MA_MASK_CAUSAL)
+    assert len(wl) == 33 and sum(c == ma.MA_TILE_PARTIAL for _, _, c in wl) == 2
+    tiles = []
+    for i, j, _ in wl:
+        o, lse = empty_out(C)
+        tiles.append(Tile(Q[qchunks[i]][0], K[j][0], V[j][0], o, lse, qpos[i], kpos[j]))
+    ma.mesh_attn_tile_fwd(tiles, float(SCALE), ma.MA_MASK_CAUSAL)
+    merged = []
+    for i in range(2):
+        mine = [t for t, (ii, _, _) in zip(tiles, wl) if ii == i]
+        assert len(mine) == (6 if i == 0 else 27)
+        o, lse = empty_out(C)
+        ma.mesh_attn_merge([t.o for t in mine], [t.lse for t in mine], o, lse)
+        merged.append((o, lse))
+    torch.cuda.synchronize()
+    kall = np.concatenate([x[1] for x in K], axis=1)
+    vall = np.concatenate([x[1] for x in V], axis=1)
+    kp_all = np.arange(2 * N * C)
+    for i, c in enumerate(qchunks):
+        rows = sample_rows(C, wid + i)
+        qp = positions(qpos[i], C)
+        Oref, Lref = attn_tile(Q[c][1], kall, vall, SCALE, None, True, qp, kp_all, rows=rows)
+        check_close(f"merged O chunk {c}", host_f64(merged[i][0])[:, rows], Oref, BF16_O_TOL)
+        check_close(f"merged LSE chunk {c}", host_f64(merged[i][1])[:, :, rows], Lref, BF16_LSE_TOL)
+        # the diagonal (partially masked) tile's own partial
+        t = [t for t, (ii, jj, _) in zip(tiles, wl) if ii == i and jj == c][0]
+        Ot, Lt = attn_tile(Q[c][1], K[c][1], V[c][1], SCALE, None, True, qp, positions(kpos[c], C), rows=rows)
+        check_close(f"diagonal O chunk {c}", host_f64(t.o)[:, rows], Ot, BF16_O_TOL)
+        check_close(f"diagonal LSE chunk {c}", host_f64(t.lse)[:, :, rows], Lt, BF16_LSE_TOL)
+
+
+def test_zigzag_diagonal_mask_probe_full_size():
+    # Q = 0 on the 4096 x 4096 diagonal tile of chunk 26: exp(LSE[t]) is exactly t + 1 for every row.
+    C = 4096
+    log("[workload mask probe 4096 diagonal]")
+    q = torch.zeros((1, C, HQ, D), dtype=torch.bfloat16, device=DEV)
+    k, _ = gen(3, synthetic.T_K, 26, (1, C, HKV, D))
+    v, _ = gen(3, synthetic.T_V, 26, (1, C, HKV, D))
+    o, lse = empty_out(C)
+    p = ma.mesh_attn_pos_contiguous(26 * C)
+    ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, p, p)], float(SCALE), ma.MA_MASK_CAUSAL)
+    torch.cuda.synchronize()
+    counts = np.rint(np.exp(host_f64(lse)[0])).astype(np.int64)
+    assert np.array_equal(counts, np.broadcast_to(np.arange(1, C + 1), counts.shape))
+
+
+def test_mesh_8x8_1m_forward_and_merge():
+    # One GPU (g = 9) of n = 64 at S = 1,048,576: partitions of 16384 tokens, 8 x 8 tile with KV rotation,
+    # non-causal; 8-way merges per Q partition plus 7 incoming seeded partials for the owned partition.
+    wid, n, a, b, g, P = 4, 64, 8, 8, 9, 16384
+    log("[workload mesh-8x8-1m]")
+    qparts, kparts = ma.mesh_attn_map_mesh_tile(n, a, b, g, True)
+    assert (qparts, kparts) == layout.mesh_tile(n, a, b, g, True)
+    Q = {i: gen(wid, synthetic.T_Q, i, (1, P, HQ, D)) for i in qparts}
+    K = {j: gen(wid, synthetic.T_K, j, (1, P, HKV, D)) for j in kparts}
+    V = {j: gen(wid, synthetic.T_V, j, (1, P, HKV, D)) for j in kparts}
+    tiles = {}
+    for i in qparts:
+        for j in kparts:
+            o, lse = empty_out(P)
+            tiles[(i, j)] = Tile(Q[i][0], K[j][0], V[j][0], o, lse)
+    ma.mesh_attn_tile_fwd(list(tiles.values()), float(SCALE), ma.MA_MASK_NONE)
+    mu = np.float32(math.log(b * P) + 0.5)
+    inc = []
+    for r in range(a - 1):
+        oi, oiv = gen(wid, synthetic.T_O_IN, r, (1, P, HQ, D))
+        li = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, r, (1, HQ, P)) + mu).astype(np.float32)
+        inc.append((oi, oiv, torch.from_numpy(li).to(DEV), li.astype(np.float64)))
+    merged = {}
+    for i in qparts:
+        os_ = [tiles[(i, j)].o for j in kparts]
+        ls_ = [tiles[(i, j)].lse for j in kparts]
+        if i == g:
+            os_ += [x[0] for x in inc]
+            ls_ += [x[2] for x in inc]
+        o, lse = empty_out(P)
+        ma.mesh_attn_merge(os_, ls_, o, lse)
+        merged[i] = (o, lse)
+    torch.cuda.synchronize()
+    kall = np.concatenate([K[j][1] for j in kparts], axis=1)
+    vall = np.concatenate([V[j][1] for j in kparts], axis=1)
+    for i in qparts:
+        rows = sample_rows(P, wid + i, extra=6 if i != g else 16)
+        Oloc, Lloc = attn_tile(Q[i][1], kall, vall, SCALE, rows=rows)
+        if i == g:
+            Oref, Lref = merge([(Oloc, Lloc)] + [(x[1][:, rows], x[3][:, :, rows]) for x in inc])
+        else:
+            Oref, Lref = Oloc, Lloc
+        check_close(f"merged O Q{i}", host_f64(merged[i][0])[:, rows], Oref, BF16_O_TOL)
+        check_close(f"merged LSE Q{i}", host_f64(merged[i][1])[:, :, rows], Lref, BF16_LSE_TOL)
+    # one partial tile on its own
+    i, j = qparts[3], kparts[5]
+    rows = sample_rows(P, 99)
+    Ot, Lt = attn_tile(Q[i][1], K[j][1], V[j][1], SCALE, rows=rows)
+    check_close("tile O", host_f64(tiles[(i, j)].o)[:, rows], Ot, BF16_O_TOL)
+    check_close("tile LSE", host_f64(tiles[(i, j)].lse)[:, :, rows], Lt, BF16_LSE_TOL)
+
+
+def test_gqa_bwd_4x8k():
+    # Backward at the 8k GQA shape: 4 Q partitions of 8192 against one KV partition of 8192, non-causal;
+    # dK/dV summed over the 4 partitions.  O and LSE are seeded stored inputs with the magnitudes of a
+    # real forward (O ~ 0.02 N(0,1), LSE ~ ln 8192 + 0.5 + 0.3 N(0,1)); both sides read the same values.
+    wid, S, nq = 5, 8192, 4
+    log("[workload gqa-bwd-4x8k]")
+    k, kv = gen(wid, synthetic.T_K, 0, (1, S, HKV, D))
+    v, vv = gen(wid, synthetic.T_V, 0, (1, S, HKV, D))
+    dk = torch.empty((1, S, HKV, D), dtype=torch.float32, device=DEV)
+    dv = torch.empty_like(dk)
+    tiles, host = [], []
+    mu = np.float32(math.log(S) + 0.5)
+    for i in range(nq):
+        q, qv = gen(wid, synthetic.T_Q, i, (1, S, HQ, D))
+        do, dov = gen(wid, synthetic.T_DO, i, (1, S, HQ, D))
+        ob = synthetic.f32_to_bf16_bits(synthetic.normal_f32(wid, synthetic.T_O_IN, i, (1, S, HQ, D)) * np.float32(0.02))
+        ov = synthetic.bf16_bits_to_f32(ob).astype(np.float64)
+        lv = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (1, HQ, S)) * np.float32(0.3) + mu).astype(np.float32)
+        dq = torch.empty((1, S, HQ, D), dtype=torch.float32, device=DEV)
+        tiles.append(BwdTile(q, k, v, dev_bf16(ob), do, torch.from_numpy(lv).to(DEV), dq, dk, dv))
+        host.append(dict(q=qv, o=ov, do=dov, lse=lv.astype(np.float64)))
+    ma.mesh_attn_tile_bwd(tiles, float(SCALE), ma.MA_MASK_NONE)
+    torch.cuda.synchronize()
+
+    def check(name, got, ref):
+        scale = max(float(np.max(np.abs(ref))), 1e-3)
+        err = float(np.max(np.abs(got - ref)))
+        log(f"  {name}: max_abs_err={err:.3e} max|ref|={scale:.3e} rel={err/scale:.2e}")
+        assert np.isfinite(got).all() and err <= 2e-2 * scale
+
+    # dQ on sampled rows of each partition (needs all keys)
+    for i, h in enumerate(host):
+        rows = sample_rows(S, wid + 10 * i, extra=8)
+        dq_r, _, _ = attn_tile_bwd(h["q"][:, rows], kv, vv, h["o"][:, rows], h["do"][:, rows], h["lse"][:, :, rows], SCALE)
+        check(f"dQ part {i}", host_f64(tiles[i].dq)[:, rows], dq_r)
+    # dK/dV on sampled keys (needs every query row of every partition)
+    keys = sample_rows(S, wid + 100, extra=12)
+    dk_r = dv_r = 0
+    for h in host:
+        _, a_, b_ = attn_tile_bwd(h["q"], kv[:, keys], vv[:, keys], h["o"], h["do"], h["lse"], SCALE)
+        dk_r = dk_r + a_
+        dv_r = dv_r + b_
+    check("dK[keys]", host_f64(dk)[:, keys], dk_r)
+    check("dV[keys]", host_f64(dv)[:, keys], dv_r)
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
