@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="query rows in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle sample")
     ap.add_argument("--parts", default="fwd,merge,bwd", help="kernels in the step (all by default)")
     return ap.parse_args()
 
