@@ -122,6 +122,8 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       !strides_ok(a->v_stride, 3, a->dtype) || !strides_ok(a->o_stride, 3, a->dtype) || a->lse_stride[0] < 0 ||
       a->lse_stride[1] < 0)
     return set_error(MA_ERR_INVALID, "strides must be >= 0 and multiples of 16 bytes");
+  if (a->dtype == MA_BF16 && (a->k_stride[1] >= (1 << 24) || a->v_stride[1] >= (1 << 24)))
+    return set_error(MA_ERR_UNSUPPORTED, "K/V sequence strides must be below 2^24 elements");
 
   FwdParams p;
   std::memset(&p, 0, sizeof(p));
@@ -184,8 +186,9 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     }
     int64_t wgs;
     if (bf16) {
-      const int64_t nqb = (t.sq + 63) / 64;
-      ft.chunks = (int32_t)((nqb * p.gmax + 3) / 4);
+      // 8 waves of 32 query rows per workgroup; units are (32-row block, head of the group)
+      const int64_t nqb = (t.sq + 31) / 32;
+      ft.chunks = (int32_t)((nqb * p.gmax + 7) / 8);
       wgs = (int64_t)a->batch * a->hkv * ft.chunks;
       wgs = (wgs + 7) / 8 * 8;  // keep each tile's first workgroup on XCD 0
     } else {

@@ -6,24 +6,36 @@
 // running denominator, unnormalised output).  The layout on the chip is this
 // file's own design:
 //
-//  * A workgroup is 4 waves; each wave owns 64 query rows of one query head
-//    (two 32-row MFMA sub-blocks) and all waves of a workgroup read the same KV
-//    head, so one LDS copy of a 64-key K/V block serves 256 query rows.
+//  * A workgroup is 8 waves, two per SIMD; each wave owns 32 query rows of one
+//    query head and all waves read the same KV head, so one LDS copy of a
+//    64-key K/V block serves 256 query rows.  A wave's state (O^T, its Q
+//    fragments, two score tiles) fits in the 256 architectural VGPRs, and the
+//    two waves of a SIMD overlap one's softmax with the other's MFMAs.
+//    Workgroup index modulo the KV head count picks the KV head, so with 8 KV
+//    heads each XCD's L2 serves one.
+//  * K and V blocks go from global memory straight into LDS
+//    (global_load_lds_dwordx4, no register staging) through a ring of four
+//    stages, loaded two blocks ahead; 16-byte chunks of each row are
+//    XOR-swizzled by row so that both the b128 reads of K and the transposed b64
+//    reads of V are free of bank conflicts on the 64-bank LDS.  K stages and V
+//    stages sit in two separate 64 KB regions and the loop is unrolled over the
+//    stages, so every fragment read is a lane offset plus an immediate.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    the accumulator puts one query per lane (16 of its keys; the other 16 in
-//    lane l^32), so the row max needs one cross-lane exchange and the row sum
-//    none until the end.  K rows are fed to the MFMA in a permuted order (bits
-//    2 and 3 of the row index swapped) so that each lane's 16 accumulator
-//    values are, unchanged, the B operand (P^T) of the P.V MFMA.
-//  * O is accumulated transposed too (O^T = V^T P^T), so every lane again holds
-//    only its own query's outputs and rescaling is lane-local.  V stays
-//    row-major in LDS and is read transposed with ds_read_b64_tr_b16.
+//    each lane owns one query (16 of the keys of a 32-key tile, the other 16 in
+//    lane l^32), so the row max needs one permlane32 swap.  K rows enter the
+//    MFMA in a permuted order (bits 2 and 3 of the row index swapped) so that
+//    each lane's 16 accumulator values are, unchanged, the B operand (P^T) of
+//    O^T = V^T P^T; V^T fragments come from ds_read_b64_tr_b16.
+//  * Software pipeline over 32-key steps: while the exponentials of step h run
+//    on the VALU, the MFMAs of the scores of step h+1 are in flight; then
+//    O^T += V_h^T P_h^T runs while step h+1 is masked and its row max taken.
 //  * Softmax runs in base 2 with scale*log2(e) folded into one FMA; the running
 //    max is only raised when a row's block max exceeds it by more than 8
 //    (factor 256), which keeps the result exact while skipping most rescales.
-//  * Masks are resolved per 64-key block: blocks with no allowed pair are not
-//    loaded, blocks with every pair allowed run unmasked, the rest compare
-//    global positions element by element ([Mesh] section 3.7 pair classes).
+//  * Masks are resolved per 64-key block ([Mesh] section 3.7 pair classes):
+//    blocks with no allowed pair for the workgroup are never loaded, blocks with
+//    every pair allowed run unmasked, the rest (and the ragged last block)
+//    compare global positions element by element.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -34,39 +46,88 @@ namespace ma {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQW = 64;  // query rows per wave
+constexpr int kQW = 32;  // query rows per wave
 constexpr int kBN = 64;  // keys per block
+constexpr int kStages = 4;
 
 template <int D>
 struct FwdCfg {
-  static constexpr int KROW = D + 8;                    // K row pitch in LDS (elements)
-  static constexpr int VROW = D == 128 ? D + 32 : D + 32;  // V row pitch: 320 B (D=128), 192 B (D=64)
-  static constexpr int KS = D / 16;                     // MFMA k-steps over d
-  static constexpr int NC = D / 32;                     // 32-row chunks of O^T
-  static constexpr int CH = D / 8;                      // 16-byte chunks per row
-  static constexpr int LOADS = kBN * CH / kThreads;     // 16-byte loads per thread per tensor
-  static constexpr int K_ELEMS = kBN * KROW;
-  static constexpr int V_ELEMS = kBN * VROW;
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int KS = D / 16;                  // MFMA k-steps over d
+  static constexpr int NC = D / 32;                  // 32-row chunks of O^T
+  static constexpr int BLK = kBN * D;                // elements of one K or V block
+  static constexpr int LPW = kBN * CH / 64 / kWaves;  // direct-to-LDS loads per wave per tensor
 };
+
+// XOR mask applied to the 16-byte chunk index of LDS row `row` (period 16 rows).
+// D=128 (one row = 64 banks): rows 0..15 map a chunk to 16 distinct chunks, and
+// rows 4k..4k+3 to distinct 64-byte groups.  D=64 (two rows per bank line): the
+// same two properties over (row parity, chunk).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 __device__ __forceinline__ int perm_key(int m) {  // swap bits 2 and 3
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-template <int D>
+__device__ __forceinline__ float xhalf_max(float x) {  // max(x[l], x[l ^ 32])
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {  // x[l] + x[l ^ 32]
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Byte address of an LDS location, made opaque to the optimiser so that later
+// constant offsets (stage, slice) fold into the 16-bit immediate of the DS
+// instruction instead of creating one address register per constant.
+__device__ __forceinline__ uint32_t lds_lane_addr(const void* p) {
+  uint32_t a = (uint32_t)(uintptr_t)(const lds_char*)p;
+  asm volatile("" : "+v"(a));
+  return a;
+}
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at LDS byte address lds_dst + 16 i.  Written as inline asm
+// so that the compiler does not add vmcnt(0) waits in front of every LDS read;
+// the kernel orders these loads itself with s_waitcnt vmcnt and a barrier.
+__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff_bytes, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff_bytes), "s"(gbase), "s"(lds_dst) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_char*)p; }
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
+}
+__device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) i16x4*)(uintptr_t)addr));
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this
+// wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left free)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+template <int D, bool MASKED>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(const FwdParams p) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][C::V_ELEMS];
-  __shared__ int kpos_s[2][kBN];
+  // K stages in the first half, V stages in the second: kv_s[0][st] is K, kv_s[1][st] is V
+  __shared__ __attribute__((aligned(1024))) __bf16 kv_s[2][kStages][C::BLK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
@@ -83,244 +144,287 @@ fwd_bf16_kernel(const FwdParams p) {
   if (b >= p.batch) return;  // padding workgroup (uniform)
   const int g0 = p.kv_first[kvh];
   const int gsz = p.kv_first[kvh + 1] - g0;
+  if (gsz <= 0) return;
   const int nqb = (T.sq + kQW - 1) / kQW;
 
   // units of this workgroup: (query block, head) pairs, query-block major
-  int wg_qlo = INT32_MAX, wg_qhi = INT32_MIN;  // row range of the workgroup (for block skipping)
-  bool any_valid = false;
+  int wg_qlo = INT32_MAX, wg_qhi = INT32_MIN;
   int my_qb = -1, my_head = 0;
   for (int wv = 0; wv < kWaves; ++wv) {
     const int u = chunk * kWaves + wv;
-    if (gsz <= 0) break;
     const int qb = u / gsz;
     if (qb >= nqb) continue;
-    any_valid = true;
-    const int r0 = qb * kQW, r1 = min(T.sq, r0 + kQW);
-    wg_qlo = min(wg_qlo, r0);
-    wg_qhi = max(wg_qhi, r1);
+    wg_qlo = min(wg_qlo, qb * kQW);
+    wg_qhi = max(wg_qhi, min(T.sq, qb * kQW + kQW));
     if (wv == wave) {
       my_qb = qb;
       my_head = p.heads_of[g0 + (u % gsz)];
     }
   }
-  if (!any_valid) return;  // uniform across the workgroup
+  if (wg_qlo == INT32_MAX) return;  // no unit in this workgroup (uniform)
   const bool active = my_qb >= 0;
-  const int q0 = active ? my_qb * kQW : 0;
+  const int q0 = active ? my_qb * kQW : wg_qlo;
 
-  // position ranges for block classification
-  int wg_pmin = 0, wg_pmax = 0;
-  if (p.mask) pos_minmax_dev(T.qp, T.sq, wg_qlo, wg_qhi, wg_pmin, wg_pmax);
-  int w_pmin = 0, w_pmax = 0;
-  if (p.mask && active) pos_minmax_dev(T.qp, T.sq, q0, min(T.sq, q0 + kQW), w_pmin, w_pmax);
+  int wg_pmin = 0, wg_pmax = 0, w_pmin = 0, w_pmax = 0;
+  if constexpr (MASKED) {
+    pos_minmax_dev(T.qp, T.sq, wg_qlo, wg_qhi, wg_pmin, wg_pmax);
+    pos_minmax_dev(T.qp, T.sq, q0, min(T.sq, q0 + kQW), w_pmin, w_pmax);
+  }
 
   const __bf16* __restrict__ Kg = (const __bf16*)T.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
   const __bf16* __restrict__ Vg = (const __bf16*)T.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+  const int k_ss = (int)p.k_ss, v_ss = (int)p.v_ss;  // below 2^24 (checked by the caller)
 
-  // ---- query fragments (B operand of S^T = K Q^T) and query positions ----
-  bf16x8 qf[2][C::KS];
-  int qpos[2];
+  // ---- query fragments (B operand of S^T = K Q^T) and query position ----
+  bf16x8 qf[C::KS];
+  int qpos = 0;
   {
     const __bf16* Qg = (const __bf16*)T.q + (int64_t)b * p.q_sb + (int64_t)my_head * p.q_sh;
+    const int row = q0 + l32;
+    const bool ok = active && row < T.sq;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int row = q0 + qs * 32 + l32;
-      const bool ok = active && row < T.sq;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        bf16x8 z = {};
-        qf[qs][ks] = ok ? *(const bf16x8*)(Qg + (int64_t)row * p.q_ss + ks * 16 + hl * 8) : z;
-      }
-      qpos[qs] = (p.mask && ok) ? pos_at_dev(T.qp, row) : 0;
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8 z = {};
+      qf[ks] = ok ? *(const bf16x8*)(Qg + (int64_t)row * p.q_ss + ks * 16 + hl * 8) : z;
     }
+    if constexpr (MASKED) qpos = ok ? pos_at_dev(T.qp, row) : INT32_MIN;
   }
 
-  // ---- KV block iteration over blocks that are not EMPTY for the workgroup ----
+  // ---- block classes: 0 empty, 1 partial (element mask), 2 full ----
   const int nkb = (T.sk + kBN - 1) / kBN;
-  auto block_class = [&](int kb, int pmin, int pmax) -> int {  // 0 empty, 1 partial, 2 full
-    const int u0 = kb * kBN, u1 = min(T.sk, u0 + kBN);
-    const bool tail = (u1 - u0) < kBN;
-    if (!p.mask) return tail ? 1 : 2;
-    int kmin, kmax;
-    pos_minmax_dev(T.kp, T.sk, u0, u1, kmin, kmax);
-    if (kmin > pmax) return 0;
-    if (kmax <= pmin && !tail) return 2;
-    return 1;
+  auto block_class = [&](int kb, int pmin, int pmax) -> int {
+    const bool tail = kb * kBN + kBN > T.sk;
+    if constexpr (!MASKED) {
+      return tail ? 1 : 2;
+    } else {
+      int kmin, kmax;
+      pos_minmax_dev(T.kp, T.sk, kb * kBN, min(T.sk, kb * kBN + kBN), kmin, kmax);
+      if (kmin > pmax) return 0;
+      if (kmax <= pmin && !tail) return 2;
+      return 1;
+    }
   };
   auto next_block = [&](int from) -> int {
-    for (int kb = from; kb < nkb; ++kb)
-      if (block_class(kb, wg_pmin, wg_pmax) != 0) return kb;
-    return nkb;
+    if constexpr (!MASKED) {
+      return from < nkb ? from : nkb;
+    } else {
+      for (int kb = from; kb < nkb; ++kb)
+        if (block_class(kb, wg_pmin, wg_pmax) != 0) return kb;
+      return nkb;
+    }
   };
 
-  uint4 kreg[C::LOADS], vreg[C::LOADS];
-  auto gload = [&](int kb) {
+  // ---- direct-to-LDS loads: wave instruction i fills LDS chunks [(wave*LPW+i)*64, +64) ----
+  auto load_row = [&](int i) { return ((wave * C::LPW + i) * 64 + lane) / C::CH; };
+  auto load_col = [&](int i) { return ((((wave * C::LPW + i) * 64 + lane) % C::CH) ^ swz<D>(load_row(i))) * 8; };
+  uint32_t kgo[C::LPW], vgo[C::LPW];  // byte offsets of this lane's chunks inside a full block
 #pragma unroll
-    for (int it = 0; it < C::LOADS; ++it) {
-      const int c = tid + it * kThreads;
-      const int row = c / C::CH, col = (c % C::CH) * 8;
-      const int key = kb * kBN + row;
-      if (key < T.sk) {
-        kreg[it] = *(const uint4*)(Kg + (int64_t)key * p.k_ss + col);
-        vreg[it] = *(const uint4*)(Vg + (int64_t)key * p.v_ss + col);
-      } else {
-        kreg[it] = make_uint4(0, 0, 0, 0);
-        vreg[it] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < C::LPW; ++i) {
+    kgo[i] = (uint32_t)(load_row(i) * k_ss + load_col(i)) * 2u;
+    vgo[i] = (uint32_t)(load_row(i) * v_ss + load_col(i)) * 2u;
+  }
+  auto issue = [&](int st, int kb) {
+    const __bf16* kbase = Kg + (int64_t)kb * kBN * p.k_ss;
+    const __bf16* vbase = Vg + (int64_t)kb * kBN * p.v_ss;
+    const int valid = T.sk - kb * kBN;  // rows of this block inside the partition
+    if (valid >= kBN) {
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        lds_dma16(kbase, kgo[i], lds_addr(&kv_s[0][st][(wave * C::LPW + i) * 512]));
+        lds_dma16(vbase, vgo[i], lds_addr(&kv_s[1][st][(wave * C::LPW + i) * 512]));
+      }
+    } else {  // ragged last block: rows past the end repeat the last row (finite; masked later)
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        const int r = min(load_row(i), valid - 1);
+        lds_dma16(kbase, (uint32_t)(r * k_ss + load_col(i)) * 2u, lds_addr(&kv_s[0][st][(wave * C::LPW + i) * 512]));
+        lds_dma16(vbase, (uint32_t)(r * v_ss + load_col(i)) * 2u, lds_addr(&kv_s[1][st][(wave * C::LPW + i) * 512]));
       }
     }
   };
-  auto swrite = [&](int buf, int kb) {
-#pragma unroll
-    for (int it = 0; it < C::LOADS; ++it) {
-      const int c = tid + it * kThreads;
-      const int row = c / C::CH, col = (c % C::CH) * 8;
-      *(uint4*)(&Ks[buf][row * C::KROW + col]) = kreg[it];
-      *(uint4*)(&Vs[buf][row * C::VROW + col]) = vreg[it];
-    }
-    if (tid < kBN) {
-      const int key = kb * kBN + tid;
-      int kp;
-      if (key >= T.sk) kp = INT32_MAX;
-      else kp = p.mask ? pos_at_dev(T.kp, key) : INT32_MIN;
-      kpos_s[buf][tid] = kp;
-    }
+  // wait until at most n later sequence positions have loads in flight (n in 0..2)
+  auto wait_positions = [&](int n) {
+    if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * C::LPW));
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::LPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
+
+  // ---- per-lane LDS byte addresses of the K and V^T fragments (stage 0, first slice) ----
+  uint32_t kaddr[C::KS];  // K row perm(l32) (+32 rows for the second 32-key half), chunk 2ks+hl
+  {
+    const int row = perm_key(l32);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kaddr[ks] = lds_lane_addr(&kv_s[0][0][row * D + (((2 * ks + hl) ^ swz<D>(row)) << 3)]);
+  }
+  const int G = lane >> 4, lam = lane & 15;
+  uint32_t vaddr[C::NC][2];  // V rows (G>>1)*8 + lam/4 (+4), columns c*32 + (G&1)*16 + (lam&3)*4 (+16 rows per slice)
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = (G >> 1) * 8 + (lam >> 2) + h * 4;
+      const int col = c * 32 + (G & 1) * 16 + (lam & 3) * 4;
+      vaddr[c][h] = lds_lane_addr(&kv_s[1][0][row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7)]);
+    }
+  constexpr uint32_t kStageBytes = C::BLK * 2;
 
   // ---- accumulators ----
-  f32x16 oacc[2][C::NC];
+  f32x16 oacc[C::NC];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) oacc[qs][c] = f32x16{};
-  float m2[2] = {-INFINITY, -INFINITY};  // running max in log2 units (reference for exp2)
-  float lsum[2] = {0.f, 0.f};            // this lane's share of the row sum
+  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
+  float m2 = -INFINITY;  // running max in log2 units
+  float lsum = 0.f;      // this lane's share of the row sum
   const float c2 = p.scale_log2;
 
-  int kb = next_block(0);
-  int buf = 0;
-  if (kb < nkb) {
-    gload(kb);
-    swrite(0, kb);
-  }
-  __syncthreads();
-  int kb_next = (kb < nkb) ? next_block(kb + 1) : nkb;
-  if (kb_next < nkb) gload(kb_next);
+  // S^T of one 32-key half (kb2) of the block in stage st
+  auto s_half = [&](int st, int kb2, f32x16& s) {
+    const uint32_t off = st * kStageBytes + kb2 * 32 * D * 2;
+    s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 kf = lds_read_b128(kaddr[ks] + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+  };
 
-  while (kb < nkb) {
-    const int cls = active ? block_class(kb, w_pmin, w_pmax) : 0;
-    if (cls != 0) {
-      const __bf16* Kl = Ks[buf];
-      const __bf16* Vl = Vs[buf];
-      // S^T = K Q^T for two 32-key sub-blocks and two 32-query sub-blocks
-      f32x16 s[2][2];
+  // element mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8
+  auto mask_half = [&](int kb, int kb2, f32x16& s) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        s[0][kb2] = f32x16{};
-        s[1][kb2] = f32x16{};
-        const int krow = kb2 * 32 + perm_key(l32);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 kf = *(const bf16x8*)(Kl + krow * C::KROW + ks * 16 + hl * 8);
-          s[0][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][ks], s[0][kb2], 0, 0, 0);
-          s[1][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][ks], s[1][kb2], 0, 0, 0);
-        }
-      }
-      // element masking on partial blocks
-      if (cls == 1) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-            const int kp = kpos_s[buf][key];
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs)
-              if (!(kp <= qpos[qs])) s[qs][kb2][e] = -INFINITY;
-          }
-      }
-      // online softmax per query sub-block; P^T packed to bf16 as the B operand
-      bf16x8 pf[2][4];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qs][kb2][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mb2 = mx * c2;
-        if (__any(mb2 > m2[qs] + 8.0f)) {
-          const float mn = fmaxf(m2[qs], mb2);
-          const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m2[qs] - mn);
-          lsum[qs] *= alpha;
-#pragma unroll
-          for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[qs][c][i] *= alpha;
-          m2[qs] = mn;
-        }
-        const float mref = (m2[qs] == -INFINITY) ? 0.0f : m2[qs];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            float pv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qs][kb2][half * 8 + i], c2, -mref));
-              lsum[qs] += pv[i];
-            }
-            pf[qs][kb2 * 2 + half] = pack_bf16x8(pv);
-          }
-        }
-      }
-      // O^T += V^T P^T : V^T fragments read transposed from row-major LDS
-      const int G = lane >> 4, lam = lane & 15;
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = j * 16 + (G >> 1) * 8 + (lam >> 2);
-          const int col = c * 32 + (G & 1) * 16 + (lam & 3) * 4;
-          const bf16x4 lo = ds_read_tr16(Vl + row * C::VROW + col);
-          const bf16x4 hi = ds_read_tr16(Vl + (row + 4) * C::VROW + col);
-          const bf16x8 vf = concat_bf16x4(lo, hi);
-          oacc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][j], oacc[0][c], 0, 0, 0);
-          oacc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[1][j], oacc[1][c], 0, 0, 0);
-        }
+    for (int e = 0; e < 16; ++e) {
+      const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
+      if constexpr (MASKED) {
+        const int kp = key < T.sk ? pos_at_dev(T.kp, key) : INT32_MAX;
+        if (!(kp <= qpos)) s[e] = -INFINITY;
+      } else {
+        if (key >= T.sk) s[e] = -INFINITY;
       }
     }
-    // stage the next block, then the one after it
-    const int kb_after = (kb_next < nkb) ? next_block(kb_next + 1) : nkb;
-    if (kb_next < nkb) swrite(buf ^ 1, kb_next);
+  };
+
+  // mask (when the block is not fully allowed for this wave) and row max of a half, in log2 units
+  float mb2 = -INFINITY;
+  auto half_max = [&](int kb, int kb2, f32x16& s) {
+    const int cls = active ? block_class(kb, w_pmin, w_pmax) : 1;
+    if (cls != 2) mask_half(kb, kb2, s);  // partial, or empty for this wave only
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+    mb2 = xhalf_max(mx) * c2;
+  };
+  // raise the running max when a row's new max exceeds it by more than 8 (rare after the first step)
+  auto maybe_rescale = [&]() {
+    if (__any(mb2 > m2 + 8.0f)) {
+      const float mn = fmaxf(m2, mb2);
+      const float alpha = (mn == -INFINITY || m2 == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m2 - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+      m2 = mn;
+    }
+  };
+
+  // One pipeline step over a 32-key half (stage st, half kb2) whose scores are
+  // in sc and whose max is already folded into m2: the exponentials while the
+  // MFMAs of the next half's scores (block nkb_, stage nst, half nkb2) run, then
+  // the half's PV MFMAs while the next half is masked and its row max taken.
+  // A half past the last block reads a stale stage; half_max masks it to -inf
+  // (no key of a block index >= nkb is allowed), so it never changes the state.
+  auto half_step = [&](int st, int kb2, f32x16& sc, int nkb_, int nst, int nkb2, f32x16& sn) {
+    const float mref = (m2 == -INFINITY) ? 0.0f : m2;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half * 8 + i], c2, -mref));
+        lsum += pv[i];
+      }
+      pf[half] = pack_bf16x8(pv);
+    }
+    s_half(nst, nkb2, sn);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t off = st * kStageBytes + (kb2 * 2 + half) * 16 * D * 2;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const bf16x4 lo = lds_read_tr16(vaddr[c][0] + off);
+        const bf16x4 hi = lds_read_tr16(vaddr[c][1] + off);
+        const bf16x8 vf = concat_bf16x4(lo, hi);
+        oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[half], oacc[c], 0, 0, 0);
+      }
+    }
+    half_max(nkb_, nkb2, sn);
+  };
+
+  // ---- pipeline over the blocks with any allowed pair for the workgroup ----
+  // Sequence position j lives in stage j % 4.  Before the step that first reads
+  // position j+1 (the second half of position j), its loads have landed (j+2 may
+  // still be in flight) and position j+3 is issued into the stage that the
+  // previous block's steps finished reading.
+  int bj0 = next_block(0);
+  int bj1 = bj0 < nkb ? next_block(bj0 + 1) : nkb;
+  int bj2 = bj1 < nkb ? next_block(bj1 + 1) : nkb;
+  if (bj0 < nkb) issue(0, bj0);
+  if (bj1 < nkb) issue(1, bj1);
+  if (bj2 < nkb) issue(2, bj2);
+  f32x16 sA, sB;
+  // one full wait here also retires the query loads, so the compiler needs no
+  // vmcnt waits inside the loop
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (bj0 < nkb) {
     __syncthreads();
-    if (kb_after < nkb) gload(kb_after);
-    kb = kb_next;
-    kb_next = kb_after;
-    buf ^= 1;
+    s_half(0, 0, sA);
+    half_max(bj0, 0, sA);
+    maybe_rescale();
   }
+#define MA_FWD_BLOCK(ST)                                                        \
+  {                                                                             \
+    /* first half: next scores are the second half of the same block */        \
+    half_step((ST), 0, sA, bj0, (ST), 1, sB);                                    \
+    maybe_rescale();                                                            \
+    /* second half: next scores come from the next block (stage ST+1) */       \
+    const int bj3 = bj2 < nkb ? next_block(bj2 + 1) : nkb;                      \
+    wait_positions(bj2 < nkb ? 1 : 0);                                          \
+    __syncthreads();                                                            \
+    if (bj3 < nkb) issue(((ST) + 3) & 3, bj3);                                  \
+    half_step((ST), 1, sB, bj1, ((ST) + 1) & 3, 0, sA);                          \
+    maybe_rescale();                                                            \
+    bj0 = bj1;                                                                  \
+    bj1 = bj2;                                                                  \
+    bj2 = bj3;                                                                  \
+    if (bj0 >= nkb) break;                                                      \
+  }
+  while (bj0 < nkb) {
+    MA_FWD_BLOCK(0)
+    MA_FWD_BLOCK(1)
+    MA_FWD_BLOCK(2)
+    MA_FWD_BLOCK(3)
+  }
+#undef MA_FWD_BLOCK
 
   if (!active) return;
   // ---- epilogue: normalise, store O (bf16) and LSE (fp32, natural log) ----
   __bf16* Og = (__bf16*)T.o + (int64_t)b * p.o_sb + (int64_t)my_head * p.o_sh;
   float* Lg = T.lse + (int64_t)b * p.l_sb + (int64_t)my_head * p.l_sh;
+  const float ltot = xhalf_sum(lsum);
+  const int row = q0 + l32;
+  const bool has = ltot > 0.0f;
+  const float inv = has ? 1.0f / ltot : 0.0f;
+  if (row < T.sq) {
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    const float ltot = lsum[qs] + __shfl_xor(lsum[qs], 32);
-    const int row = q0 + qs * 32 + l32;
-    const bool has = ltot > 0.0f;
-    const float inv = has ? 1.0f / ltot : 0.0f;
-    if (row < T.sq) {
+    for (int c = 0; c < C::NC; ++c)
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c)
+      for (int g = 0; g < 4; ++g) {
+        float v4[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v4[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v4[i] = oacc[qs][c][g * 4 + i] * inv;
-          *(bf16x4*)(Og + (int64_t)row * p.o_ss + c * 32 + g * 8 + hl * 4) = pack_bf16x4(v4);
-        }
-      if (hl == 0) Lg[row] = has ? (m2[qs] + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f : -INFINITY;
-    }
+        for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * inv;
+        *(bf16x4*)(Og + (int64_t)row * p.o_ss + c * 32 + g * 8 + hl * 4) = pack_bf16x4(v4);
+      }
+    if (hl == 0) Lg[row] = has ? (m2 + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
@@ -329,10 +433,14 @@ fwd_bf16_kernel(const FwdParams p) {
 int launch_fwd_bf16(const FwdParams& p, int head_dim, int total_wgs, void* stream) {
   if (total_wgs <= 0) return 0;
   dim3 grid(total_wgs), block(kThreads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, (hipStream_t)stream, p);
-  else
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, (hipStream_t)stream, p);
+  hipStream_t s = (hipStream_t)stream;
+  if (head_dim == 128) {
+    if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, s, p);
+  } else {
+    if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
+  }
   return (int)hipGetLastError();
 }
 
