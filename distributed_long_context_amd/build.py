@@ -25,7 +25,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Kernels never produce or consume NaN on purpose (masked scores are -inf); this lets
 # fmaxf lower to plain v_max/v_max3 without NaN canonicalisation.
-FAST_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"]}
+FAST_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"], "bwd.hip": ["-fno-honor-nans"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_f32.hip", "merge.hip", "bwd.hip", "mapper.cpp"]

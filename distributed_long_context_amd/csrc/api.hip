@@ -236,13 +236,53 @@ int mesh_attn_merge(const ma_merge_args* a, void* stream) {
   return check_hip(launch_merge(p, a->dtype, a->head_dim, stream), "merge launch");
 }
 
-size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* a) {
-  if (!a || a->ntiles < 0 || (a->ntiles > 0 && !a->tiles) || a->batch < 1 || a->hq < 1) return 0;
-  size_t bytes = 0;
+}  // extern "C"
+
+namespace ma {
+namespace {
+
+// Q groups (tiles sharing a dq buffer) and KV groups (tiles sharing a dk buffer)
+// of a backward call, with the tiles of each group in call order.
+struct BwdGroups {
+  std::vector<int> q_of, kv_of;                 // group of each tile
+  std::vector<std::vector<int>> qg, kvg;        // tiles of each group
+};
+
+BwdGroups bwd_groups(const ma_tile_bwd_args* a) {
+  BwdGroups g;
+  g.q_of.assign(a->ntiles, -1);
+  g.kv_of.assign(a->ntiles, -1);
   for (int i = 0; i < a->ntiles; ++i) {
-    const int64_t sq = a->tiles[i].sq < 0 ? 0 : a->tiles[i].sq;
-    bytes += ((size_t)a->batch * a->hq * sq * sizeof(float) + 255) / 256 * 256;
+    for (int j = 0; j < i; ++j)
+      if (a->tiles[j].dq == a->tiles[i].dq) { g.q_of[i] = g.q_of[j]; break; }
+    if (g.q_of[i] < 0) { g.q_of[i] = (int)g.qg.size(); g.qg.emplace_back(); }
+    g.qg[g.q_of[i]].push_back(i);
+    for (int j = 0; j < i; ++j)
+      if (a->tiles[j].dk == a->tiles[i].dk) { g.kv_of[i] = g.kv_of[j]; break; }
+    if (g.kv_of[i] < 0) { g.kv_of[i] = (int)g.kvg.size(); g.kvg.emplace_back(); }
+    g.kvg[g.kv_of[i]].push_back(i);
   }
+  return g;
+}
+
+// bytes of the blocked LSE2/D arrays of one Q partition
+size_t lsed_bytes(int batch, int hq, int64_t sq) {
+  const int64_t nqb = (sq + 63) / 64;
+  return ((size_t)batch * hq * nqb * 128 * sizeof(float) + 255) / 256 * 256;
+}
+
+}  // namespace
+}  // namespace ma
+
+extern "C" {
+
+size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* a) {
+  if (!a || a->ntiles <= 0 || !a->tiles || a->batch < 1 || a->hq < 1) return 0;
+  for (int i = 0; i < a->ntiles; ++i)
+    if (a->tiles[i].sq < 1) return 0;
+  const BwdGroups g = bwd_groups(a);
+  size_t bytes = 0;
+  for (const auto& grp : g.qg) bytes += lsed_bytes(a->batch, a->hq, a->tiles[grp[0]].sq);
   return bytes;
 }
 
@@ -260,9 +300,8 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
       !strides_ok(a->dq_stride, 3, MA_F32) || !strides_ok(a->dk_stride, 3, MA_F32) || a->lse_stride[0] < 0 ||
       a->lse_stride[1] < 0)
     return set_error(MA_ERR_INVALID, "strides must be >= 0 and multiples of 16 bytes");
-  const size_t need = mesh_attn_tile_bwd_workspace_size(a);
-  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & 255u))
-    return set_error(MA_ERR_INVALID, "workspace missing, too small or not 256-byte aligned");
+  if (a->q_stride[1] >= (1 << 24) || a->k_stride[1] >= (1 << 24))
+    return set_error(MA_ERR_UNSUPPORTED, "Q/K/V sequence strides must be below 2^24 elements");
   for (int i = 0; i < a->ntiles; ++i) {
     const ma_bwd_tile& t = a->tiles[i];
     if (!t.q || !t.k || !t.v || !t.o || !t.dout || !t.lse || !t.dq || !t.dk || !t.dv)
@@ -274,15 +313,25 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
       return set_error(MA_ERR_INVALID, "tile sizes must be in [1, 2^31-1)");
     rc = check_positions(a->mask_mode, t.q_pos, t.sq, t.k_pos, t.sk);
     if (rc) return rc;
-    for (int j = 0; j < i; ++j) {  // tiles sharing dk or dv must share the whole KV description
+    for (int j = 0; j < i; ++j) {
       const ma_bwd_tile& u = a->tiles[j];
+      // tiles sharing dk or dv must share the whole KV description
       if ((u.dk == t.dk || u.dv == t.dv || u.dk == t.dv || u.dv == t.dk) &&
           (u.dk != t.dk || u.dv != t.dv || u.k != t.k || u.v != t.v || u.sk != t.sk ||
            (a->mask_mode != MA_MASK_NONE && std::memcmp(&u.k_pos, &t.k_pos, sizeof(ma_pos)) != 0)))
         return set_error(MA_ERR_INVALID, "tiles naming the same dk/dv must name the same k, v, sk and k_pos");
+      // tiles sharing dq must share the whole Q description
+      if (u.dq == t.dq &&
+          (u.q != t.q || u.o != t.o || u.dout != t.dout || u.lse != t.lse || u.sq != t.sq ||
+           (a->mask_mode != MA_MASK_NONE && std::memcmp(&u.q_pos, &t.q_pos, sizeof(ma_pos)) != 0)))
+        return set_error(MA_ERR_INVALID, "tiles naming the same dq must name the same q, o, dout, lse, sq and q_pos");
     }
   }
+  const size_t need = mesh_attn_tile_bwd_workspace_size(a);
+  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & 255u))
+    return set_error(MA_ERR_INVALID, "workspace missing, too small or not 256-byte aligned");
 
+  const BwdGroups grp = bwd_groups(a);
   BwdParams base;
   std::memset(&base, 0, sizeof(base));
   const char* why = nullptr;
@@ -298,83 +347,121 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
   base.k_sb = a->k_stride[0]; base.k_ss = a->k_stride[1]; base.k_sh = a->k_stride[2];
   base.dq_sb = a->dq_stride[0]; base.dq_ss = a->dq_stride[1]; base.dq_sh = a->dq_stride[2];
   base.dk_sb = a->dk_stride[0]; base.dk_ss = a->dk_stride[1]; base.dk_sh = a->dk_stride[2];
-  base.l_sb = a->lse_stride[0]; base.l_sh = a->lse_stride[1];
 
-  // per-tile kernel view (D goes to the tile's slice of the workspace)
-  std::vector<BwdTile> bt(a->ntiles);
+  // 1) per Q group: blocked LSE2 / D in its workspace slice
+  std::vector<BwdQPart> qparts(grp.qg.size());
   size_t off = 0;
-  for (int i = 0; i < a->ntiles; ++i) {
-    const ma_bwd_tile& t = a->tiles[i];
-    BwdTile& x = bt[i];
-    std::memset(&x, 0, sizeof(x));
-    x.q = t.q; x.o = t.o; x.dout = t.dout; x.lse = t.lse; x.dq = t.dq;
-    x.dscratch = (float*)((char*)workspace + off);
-    off += ((size_t)a->batch * a->hq * t.sq * sizeof(float) + 255) / 256 * 256;
-    x.sq = (int32_t)t.sq;
-    x.zero_dq = a->accumulate ? 0 : 1;
-    if (a->mask_mode != MA_MASK_NONE) to_kpos(t.q_pos, x.qp);
-    else x.qp.nseg = 1;
-  }
-  // 1) D for every tile and cleared dQ, before any main launch (tiles may share a dq buffer)
-  for (int i0 = 0; i0 < a->ntiles; i0 += kBwdTilesPerLaunch) {
-    BwdParams p = base;
-    p.ntiles = std::min(kBwdTilesPerLaunch, a->ntiles - i0);
-    for (int j = 0; j < p.ntiles; ++j) p.tiles[j] = bt[i0 + j];
-    rc = check_hip(launch_bwd_preprocess(p, a->head_dim, stream), "tile_bwd preprocess launch");
+  for (size_t gi = 0; gi < grp.qg.size(); ++gi) {
+    const ma_bwd_tile& t = a->tiles[grp.qg[gi][0]];
+    BwdQPart& q = qparts[gi];
+    std::memset(&q, 0, sizeof(q));
+    q.q = t.q; q.dout = t.dout; q.dq = t.dq;
+    q.lsed = (const float*)((char*)workspace + off);
+    q.sq = (int32_t)t.sq;
+    if (a->mask_mode != MA_MASK_NONE) to_kpos(t.q_pos, q.qp);
+    else q.qp.nseg = 1;
+    BwdPreParams pp;
+    pp.batch = a->batch; pp.hq = a->hq; pp.sq = (int32_t)t.sq;
+    pp.o = t.o; pp.dout = t.dout; pp.lse = t.lse; pp.lsed = (float*)((char*)workspace + off);
+    pp.q_sb = a->q_stride[0]; pp.q_ss = a->q_stride[1]; pp.q_sh = a->q_stride[2];
+    pp.l_sb = a->lse_stride[0]; pp.l_sh = a->lse_stride[1];
+    off += lsed_bytes(a->batch, a->hq, t.sq);
+    rc = check_hip(launch_bwd_preprocess(pp, a->head_dim, stream), "tile_bwd preprocess launch");
     if (rc) return rc;
   }
-  // 2) group tiles by KV partition (same dk buffer); split each group into entries of <= 8 tiles
-  struct Entry { int group; int first_tile_pos; int n; int accumulate; };
-  std::vector<int> group_of(a->ntiles, -1);
-  std::vector<std::vector<int>> groups;
-  for (int i = 0; i < a->ntiles; ++i) {
-    for (int j = 0; j < i; ++j)
-      if (a->tiles[j].dk == a->tiles[i].dk) { group_of[i] = group_of[j]; break; }
-    if (group_of[i] < 0) { group_of[i] = (int)groups.size(); groups.emplace_back(); }
-    groups[group_of[i]].push_back(i);
+  std::vector<BwdKVPart> kvparts(grp.kvg.size());
+  for (size_t gi = 0; gi < grp.kvg.size(); ++gi) {
+    const ma_bwd_tile& t = a->tiles[grp.kvg[gi][0]];
+    BwdKVPart& k = kvparts[gi];
+    std::memset(&k, 0, sizeof(k));
+    k.k = t.k; k.v = t.v; k.dk = t.dk; k.dv = t.dv;
+    k.sk = (int32_t)t.sk;
+    if (a->mask_mode != MA_MASK_NONE) to_kpos(t.k_pos, k.kp);
+    else k.kp.nseg = 1;
   }
-  std::vector<Entry> entries;
-  for (int g = 0; g < (int)groups.size(); ++g)
-    for (int s0 = 0; s0 < (int)groups[g].size(); s0 += kBwdTilesPerLaunch)
-      entries.push_back({g, s0, std::min(kBwdTilesPerLaunch, (int)groups[g].size() - s0),
-                         (s0 == 0) ? (a->accumulate ? 1 : 0) : 1});
-  // 3) pack entries into launches: <= 8 tiles, <= 8 entries, one entry per group per launch
-  size_t e0 = 0;
-  while (e0 < entries.size()) {
-    BwdParams p = base;
-    int nt = 0, nk = 0, wg = 0;
-    std::vector<int> used_groups;
-    size_t e = e0;
-    for (; e < entries.size(); ++e) {
-      const Entry& en = entries[e];
-      if (nk == kBwdTilesPerLaunch || nt + en.n > kBwdTilesPerLaunch) break;
-      if (std::find(used_groups.begin(), used_groups.end(), en.group) != used_groups.end()) break;
-      used_groups.push_back(en.group);
-      const ma_bwd_tile& t0 = a->tiles[groups[en.group][en.first_tile_pos]];
-      BwdKV& kv = p.kvs[nk];
-      kv.k = t0.k; kv.v = t0.v; kv.dk = t0.dk; kv.dv = t0.dv;
-      kv.sk = (int32_t)t0.sk;
-      kv.ntiles = en.n;
-      kv.accumulate = en.accumulate;
-      if (a->mask_mode != MA_MASK_NONE) to_kpos(t0.k_pos, kv.kp);
-      else kv.kp.nseg = 1;
-      for (int j = 0; j < en.n; ++j) {
-        p.tiles[nt] = bt[groups[en.group][en.first_tile_pos + j]];
-        kv.tile_idx[j] = nt++;
+
+  // 2) dQ launches (entries = Q groups with their KV partitions), then dK/dV launches
+  //    (entries = KV groups with their Q partitions).  A group with more than 8
+  //    partners is split into pieces; a later piece adds to the earlier ones and
+  //    runs in a later launch.  Each launch holds at most 8 entries, 8 partitions
+  //    of either side, and one piece per group.
+  for (int side = 0; side < 2; ++side) {
+    const bool dq_side = side == 0;
+    const auto& own = dq_side ? grp.qg : grp.kvg;
+    struct Piece { int group; std::vector<int> partners; int accumulate; };
+    std::vector<Piece> pieces;
+    for (int gi = 0; gi < (int)own.size(); ++gi) {
+      std::vector<int> partners;
+      for (int ti : own[gi]) {
+        const int pg = dq_side ? grp.kv_of[ti] : grp.q_of[ti];
+        if (std::find(partners.begin(), partners.end(), pg) == partners.end()) partners.push_back(pg);
       }
-      const int64_t nkb = (t0.sk + 127) / 128;
-      int64_t wgs = (int64_t)a->batch * a->hkv * nkb;
-      wgs = (wgs + 7) / 8 * 8;  // keep each KV partition's first workgroup on XCD 0
-      if (wg + wgs >= INT32_MAX) return set_error(MA_ERR_INVALID, "backward too large for one launch");
-      kv.wg_begin = wg;
-      wg += (int)wgs;
-      ++nk;
+      for (size_t s0 = 0; s0 < partners.size(); s0 += kBwdPerLaunch) {
+        Piece pc;
+        pc.group = gi;
+        pc.partners.assign(partners.begin() + s0, partners.begin() + std::min(partners.size(), s0 + kBwdPerLaunch));
+        pc.accumulate = (s0 == 0) ? (a->accumulate ? 1 : 0) : 1;
+        pieces.push_back(pc);
+      }
     }
-    p.nkv = nk;
-    p.ntiles = nt;
-    rc = check_hip(launch_bwd_main(p, a->head_dim, wg, stream), "tile_bwd launch");
-    if (rc) return rc;
-    e0 = e;
+    std::vector<bool> done(pieces.size(), false);
+    size_t remaining = pieces.size();
+    while (remaining > 0) {
+      BwdParams p = base;
+      std::vector<int> own_tab, part_tab, groups_in;
+      int ne = 0, wg = 0;
+      for (size_t pi = 0; pi < pieces.size() && ne < kBwdPerLaunch; ++pi) {
+        if (done[pi]) continue;
+        const Piece& pc = pieces[pi];
+        if (std::find(groups_in.begin(), groups_in.end(), pc.group) != groups_in.end()) continue;
+        // earlier pieces of this group must have run in an earlier launch
+        bool earlier_pending = false;
+        for (size_t pj = 0; pj < pi; ++pj)
+          if (!done[pj] && pieces[pj].group == pc.group) earlier_pending = true;
+        if (earlier_pending) continue;
+        std::vector<int> new_part = part_tab;
+        for (int x : pc.partners)
+          if (std::find(new_part.begin(), new_part.end(), x) == new_part.end()) new_part.push_back(x);
+        const bool own_new = std::find(own_tab.begin(), own_tab.end(), pc.group) == own_tab.end();
+        if ((int)new_part.size() > kBwdPerLaunch || (int)own_tab.size() + (own_new ? 1 : 0) > kBwdPerLaunch) continue;
+        part_tab = new_part;
+        if (own_new) own_tab.push_back(pc.group);
+        groups_in.push_back(pc.group);
+        BwdEntry& en = p.entries[ne];
+        en.self = (int32_t)(std::find(own_tab.begin(), own_tab.end(), pc.group) - own_tab.begin());
+        en.n = (int32_t)pc.partners.size();
+        for (int j = 0; j < en.n; ++j)
+          en.partner[j] = (int32_t)(std::find(part_tab.begin(), part_tab.end(), pc.partners[j]) - part_tab.begin());
+        en.accumulate = pc.accumulate;
+        int64_t wgs;
+        if (dq_side) {
+          const int64_t nqb = (qparts[pc.group].sq + 31) / 32;
+          en.chunks = (int32_t)((nqb * base.gmax + 7) / 8);
+        } else {
+          en.chunks = (int32_t)((kvparts[pc.group].sk + 127) / 128);
+        }
+        wgs = (int64_t)a->batch * a->hkv * en.chunks;
+        wgs = (wgs + 7) / 8 * 8;  // keep each entry's first workgroup on XCD 0
+        if (wg + wgs >= INT32_MAX) return set_error(MA_ERR_INVALID, "backward too large for one launch");
+        en.wg_begin = wg;
+        wg += (int)wgs;
+        ++ne;
+        done[pi] = true;
+        --remaining;
+      }
+      p.nentries = ne;
+      for (size_t i = 0; i < own_tab.size(); ++i) {
+        if (dq_side) p.qparts[i] = qparts[own_tab[i]];
+        else p.kvparts[i] = kvparts[own_tab[i]];
+      }
+      for (size_t i = 0; i < part_tab.size(); ++i) {
+        if (dq_side) p.kvparts[i] = kvparts[part_tab[i]];
+        else p.qparts[i] = qparts[part_tab[i]];
+      }
+      rc = check_hip(dq_side ? launch_bwd_dq(p, a->head_dim, wg, stream) : launch_bwd_dkv(p, a->head_dim, wg, stream),
+                     "tile_bwd launch");
+      if (rc) return rc;
+    }
   }
   return MA_OK;
 }

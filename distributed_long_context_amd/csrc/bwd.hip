@@ -1,31 +1,33 @@
 // Tile backward (dQ, dK, dV), bf16 inputs, fp32 accumulation, for CDNA4 (gfx950).
 //
-// [Mesh] section 3.5: the backward kernel is called per (Q_i, KV_j) pair with
+// [Mesh] section 3.5: the backward kernel runs per (Q_i, KV_j) pair with
 // (Q_i, KV_j, O_i, dO_i) and the partial dQ_i and dKV_j are accumulated
-// locally, addition being the reducer.  The pages print no formula; the kernel
-// evaluates the derivative of the forward definition with P = exp(s - LSE):
+// locally, addition being the reducer.  The pages print no formula; the kernels
+// evaluate the derivative of the forward definition with P = exp(s - LSE):
 //   D[t] = dO[t].O[t];  dP = dO V^T;  dS = P (dP - D);
 //   dV = P^T dO;  dK = scale dS^T Q;  dQ = scale dS K.
 //
-// Layout on the chip (this file's own design):
-//  * Preprocessing: one pass over O and dO writes D per row to the workspace
-//    and clears dQ when the call overwrites.
-//  * Main kernel, KV-stationary: a workgroup owns 128 keys of one KV head
-//    (32 per wave) and loops over every tile that reads this KV partition, every
-//    query head of the group and every 64-row query block.  K and V fragments
-//    and the dK, dV accumulators stay in registers for the whole loop, so dK/dV
-//    are written once, without atomics.
-//  * S = Q K^T and dP = dO V^T run on v_mfma_f32_32x32x16_bf16 with one key per
-//    lane; query rows are fed in a permuted order (bits 2 and 3 of the row index
-//    swapped) so that each lane's accumulator values are, unchanged, the A
-//    operand (P^T, dS^T) of the dV and dK products.  dO and Q reach those
-//    products through transposed LDS reads (ds_read_b64_tr_b16).
-//  * dS is written to LDS as [key][query] and read back transposed as the A
-//    operand of dQ = dS K; each wave covers one 32-column slice of d for the
-//    whole workgroup's 128 keys and adds it to dQ with fp32 atomics.
-//  * Query blocks with no allowed pair against the workgroup's keys are skipped;
-//    fully allowed blocks run unmasked ([Mesh] section 3.7 pair classes).
+// Layout on the chip (this file's own design): three kernels, no atomics.
+//  * bwd_pre: per Q partition, LSE*log2(e) (+inf on rows without an allowed key,
+//    so that P = 0 there) and D, written per 64-row block as 512 contiguous bytes.
+//  * bwd_dq (Q-stationary, the forward's structure): 8 waves x 32 query rows,
+//    two waves per SIMD, Q and dO fragments in registers; the 64-key K/V blocks
+//    of every KV partition of the Q group stream through a 4-stage LDS ring
+//    (direct-to-LDS loads, XOR-swizzled rows).  Per 32-key step: S^T = K Q^T and
+//    dP^T = V dO^T with one query per lane, P and dS on the VALU, then
+//    dQ^T += K^T dS^T with K^T read transposed (ds_read_b64_tr_b16); the next
+//    step's S^T and dP^T MFMAs are issued under this step's exponentials.
+//  * bwd_dkv (KV-stationary): 4 waves x 32 keys, one wave per SIMD, K and V
+//    fragments and the dK, dV accumulators in registers for the whole walk over
+//    every Q partition of the KV group, every query head reading the KV head and
+//    every 64-row query block (Q, dO and the LSE/D block staged in LDS the same
+//    way).  Per 32-query step: S = Q K^T and dP = dO V^T with one key per lane
+//    and the query rows fed in permuted order, so that P and dS are directly the
+//    A operands of dV += P^T dO and dK += dS^T Q (dO^T, Q^T read transposed).
+//  * Blocks with no allowed pair are skipped, blocks with every pair allowed run
+//    unmasked ([Mesh] section 3.7 pair classes), the rest mask element-wise.
 #include <hip/hip_runtime.h>
+#include <cstddef>
 #include <cstdint>
 
 #include "ma_internal.h"
@@ -35,247 +37,526 @@ namespace ma {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 64;    // query rows per item
-constexpr int kBN = 128;   // keys per workgroup (32 per wave)
+constexpr int kBN = 64;  // rows of one LDS tile: keys in bwd_dq, queries in bwd_dkv
+constexpr int kStages = 4;
 
 template <int D>
-struct BwdCfg {
-  static constexpr int QROW = D + 8;           // Q / dO row pitch in LDS (elements)
-  static constexpr int SROW = kBM + 8;         // dS^T row pitch (keys x queries)
-  static constexpr int KROW = D + 8;           // K / V staging pitch
-  static constexpr int KS = D / 16;            // k-steps over d
-  static constexpr int NC = D / 32;            // 32-wide d chunks
-  static constexpr int CH = D / 8;             // 16-byte chunks per row
-  static constexpr int QLOADS = kBM * CH / kThreads;  // per tensor per thread
-  static constexpr int Q_ELEMS = kBM * QROW;
-  static constexpr int S_ELEMS = kBN * SROW;
-  static constexpr int KV_ELEMS = kBN * KROW;
-  // dQ work per wave: (query sub-block, d chunk) units
-  static constexpr int DQ_UNITS = 2 * NC / kWaves;  // 2 (D=128) or 1 (D=64)
+struct Cfg {
+  static constexpr int CH = D / 8;      // 16-byte chunks per row
+  static constexpr int KS = D / 16;     // MFMA k-steps over d
+  static constexpr int NC = D / 32;     // 32-wide d chunks
+  static constexpr int BLK = kBN * D;   // elements of one tile
+  static constexpr uint32_t STAGE_BYTES = BLK * 2;
 };
 
-__device__ __forceinline__ int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// Parameter-block access by uniform index (see kernarg_at).
+__device__ __forceinline__ BwdEntry entry_at(int i) {
+  return kernarg_at<BwdEntry>(offsetof(BwdParams, entries) + (size_t)i * sizeof(BwdEntry));
+}
+__device__ __forceinline__ BwdQPart qpart_at(int i) {
+  return kernarg_at<BwdQPart>(offsetof(BwdParams, qparts) + (size_t)i * sizeof(BwdQPart));
+}
+__device__ __forceinline__ BwdKVPart kvpart_at(int i) {
+  return kernarg_at<BwdKVPart>(offsetof(BwdParams, kvparts) + (size_t)i * sizeof(BwdKVPart));
+}
+// partner pi of entry ei (read in place: a dynamically indexed copy of the entry
+// would be moved to per-thread memory)
+__device__ __forceinline__ int partner_at(int ei, int pi) {
+  return kernarg_at<int32_t>(offsetof(BwdParams, entries) + (size_t)ei * sizeof(BwdEntry) + offsetof(BwdEntry, partner) +
+                             (size_t)pi * 4);
+}
+__device__ __forceinline__ int head_of(int i) { return kernarg_byte(offsetof(BwdParams, heads_of) + i); }
+__device__ __forceinline__ int kv_first_at(int i) { return kernarg_byte(offsetof(BwdParams, kv_first) + i); }
 
 // ---------------------------------------------------------------- preprocess --
-// D[b,h,t] = sum_c dO*O for every row of every tile; clear dQ when overwriting.
+// One thread per 8 elements of a row; rows are (b, 64-row block, t%64, h) so that
+// a block of threads reads contiguous O/dO bytes.  Rows past sq in the last block
+// get LSE2 = +inf and D = 0.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdParams p, int tile, int zero_dq) {
-  constexpr int TPR = D / 8;  // threads per row
-  const BwdTile& T = p.tiles[tile];
-  const int64_t rows = (int64_t)p.batch * T.sq * p.hq;
+__global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdPreParams p) {
+  constexpr int TPR = D / 8;
+  const int nqb = (p.sq + kBN - 1) / kBN;
+  const int64_t rows = (int64_t)p.batch * nqb * kBN * p.hq;
   const int64_t r = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (r >= rows) return;  // whole rows leave together (TPR divides the wave)
   const int c = (threadIdx.x % TPR) * 8;
+  const int h = (int)(r % p.hq);
+  const int64_t tt = (r / p.hq) % ((int64_t)nqb * kBN);
+  const int64_t b = r / ((int64_t)p.hq * nqb * kBN);
+  const int t = (int)tt;
   float acc = 0.f;
-  int h = 0;
-  int64_t t = 0, b = 0;
-  if (r < rows) {
-    h = (int)(r % p.hq);
-    t = (r / p.hq) % T.sq;
-    b = r / ((int64_t)p.hq * T.sq);
-    const int64_t off = b * p.q_sb + t * p.q_ss + h * p.q_sh + c;
-    const uint4 o = *(const uint4*)((const __bf16*)T.o + off);
-    const uint4 g = *(const uint4*)((const __bf16*)T.dout + off);
+  const bool ok = t < p.sq;
+  if (ok) {
+    const int64_t off = b * p.q_sb + (int64_t)t * p.q_ss + (int64_t)h * p.q_sh + c;
+    const uint4 o = *(const uint4*)((const __bf16*)p.o + off);
+    const uint4 g = *(const uint4*)((const __bf16*)p.dout + off);
     const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc += __uint_as_float(ow[i] << 16) * __uint_as_float(gw[i] << 16);
-      acc += __uint_as_float(ow[i] & 0xffff0000u) * __uint_as_float(gw[i] & 0xffff0000u);
-    }
-    if (zero_dq) {
-      float* dq = T.dq + b * p.dq_sb + t * p.dq_ss + h * p.dq_sh + c;
-      *(float4*)dq = make_float4(0.f, 0.f, 0.f, 0.f);
-      *(float4*)(dq + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+      acc += bf16_to_f32((uint16_t)(ow[i] & 0xffffu)) * bf16_to_f32((uint16_t)(gw[i] & 0xffffu));
+      acc += bf16_to_f32((uint16_t)(ow[i] >> 16)) * bf16_to_f32((uint16_t)(gw[i] >> 16));
     }
   }
 #pragma unroll
   for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
-  if (r < rows && (threadIdx.x % TPR) == 0) T.dscratch[(b * p.hq + h) * (int64_t)T.sq + t] = acc;
+  if ((threadIdx.x % TPR) == 0) {
+    float l2 = INFINITY;
+    if (ok) {
+      const float L = p.lse[b * p.l_sb + (int64_t)h * p.l_sh + t];
+      l2 = (L == -INFINITY) ? INFINITY : L * 1.4426950408889634f;
+    }
+    float* blk = p.lsed + ((b * p.hq + h) * nqb + t / kBN) * (2 * kBN);
+    blk[t % kBN] = l2;
+    blk[kBN + t % kBN] = ok ? acc : 0.f;
+  }
 }
 
-// ---------------------------------------------------------------- main kernel --
-template <int D>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-bwd_main_kernel(const BwdParams p) {
-  using C = BwdCfg<D>;
-  // Q/dO double buffers; the first part doubles as K/V staging at start-up.
-  constexpr int QDO_BYTES = 4 * C::Q_ELEMS * 2;
-  constexpr int KV_BYTES = 2 * C::KV_ELEMS * 2;
-  constexpr int RAW = QDO_BYTES > KV_BYTES ? QDO_BYTES : KV_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
-  __shared__ __attribute__((aligned(16))) __bf16 dS_s[2][C::S_ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse2_s[2][kBM];
-  __shared__ __attribute__((aligned(16))) float dd_s[2][kBM];
-  __shared__ __attribute__((aligned(16))) int qpos_s[2][kBM];
-  __bf16* const qdo = (__bf16*)raw;  // Q buffers at [0, 2*Q_ELEMS), dO buffers after them
+// ------------------------------------------------------ walks over partners --
+// Blocks of an entry's partners, flattened: position g -> (partner index, block).
+struct PartnerWalk {
+  int n;
+  int nb[kBwdPerLaunch];  // blocks per partner (uniform); indexed at compile time only
+  __device__ __forceinline__ void decode(int g, int& pi, int& blk) const {
+    int base = 0, last = 0;
+    bool found = false;
+    pi = 0;
+    blk = 0;
+#pragma unroll
+    for (int i = 0; i < kBwdPerLaunch; ++i) {
+      if (i < n && !found) {
+        if (g < base + nb[i]) {
+          pi = i;
+          blk = g - base;
+          found = true;
+        } else {
+          base += nb[i];
+          last = nb[i];
+        }
+      }
+    }
+    if (!found) {  // past the end: the last partner, a block index past its end
+      pi = n - 1;
+      blk = g - base + last;
+    }
+    pi = __builtin_amdgcn_readfirstlane(pi);  // uniform by construction; say so
+    blk = __builtin_amdgcn_readfirstlane(blk);
+  }
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// ---------------------------------------------------------------- dQ kernel --
+template <int D, bool MASKED>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_kernel(const BwdParams p) {
+  using C = Cfg<D>;
+  constexpr int kWaves = 8, kQW = 32;
+  constexpr int LPW = kBN * C::CH / 64 / kWaves;  // direct-to-LDS loads per wave per tensor
+  // K stages, then V stages
+  __shared__ __attribute__((aligned(1024))) __bf16 kv_s[2][kStages][C::BLK];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int hl = lane >> 5;
-  const int G = lane >> 4, lam = lane & 15;
 
-  // ---- workgroup -> (KV group, batch, KV head, key block) ----
+  // ---- entry (Q group) / batch / KV head / unit ----
   const int w = blockIdx.x;
-  int gi = 0;
-  while (gi + 1 < p.nkv && w >= p.kvs[gi + 1].wg_begin) ++gi;
-  const BwdKV& KV = p.kvs[gi];
-  const int nkb = (KV.sk + kBN - 1) / kBN;
-  const int local = w - KV.wg_begin;
+  int ei = 0;
+  while (ei + 1 < p.nentries && w >= entry_at(ei + 1).wg_begin) ++ei;
+  ei = __builtin_amdgcn_readfirstlane(ei);
+  const BwdEntry E = entry_at(ei);
+  const BwdQPart QP = qpart_at(E.self);
+  const int local = w - E.wg_begin;
   const int kvh = local % p.hkv;
   const int rest = local / p.hkv;
-  const int kblk = rest % nkb;
-  const int b = rest / nkb;
-  if (b >= p.batch) return;  // padding workgroup (uniform)
-  const int g0 = p.kv_first[kvh];
-  const int gsz = p.kv_first[kvh + 1] - g0;
-
-  const int key0 = kblk * kBN;
-  const int keys_here = min(kBN, KV.sk - key0);
-  int kmin = 0, kmax = 0;
-  if (p.mask) pos_minmax_dev(KV.kp, KV.sk, key0, key0 + keys_here, kmin, kmax);
-  const int my_key = key0 + wave * 32 + l32;
-  const int my_kpos = my_key >= KV.sk ? INT32_MAX : (p.mask ? pos_at_dev(KV.kp, my_key) : INT32_MIN);
-
-  // ---- stage K and V of the 128 keys, load the stationary fragments ----
-  {
-    __bf16* Kst = (__bf16*)raw;
-    __bf16* Vst = (__bf16*)raw + C::KV_ELEMS;
-    const __bf16* Kg = (const __bf16*)KV.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-    const __bf16* Vg = (const __bf16*)KV.v + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-    for (int c = tid; c < kBN * C::CH; c += kThreads) {
-      const int row = c / C::CH, col = (c % C::CH) * 8;
-      const int key = key0 + row;
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
-      if (key < KV.sk) {
-        kx = *(const uint4*)(Kg + (int64_t)key * p.k_ss + col);
-        vx = *(const uint4*)(Vg + (int64_t)key * p.k_ss + col);
-      }
-      *(uint4*)(Kst + row * C::KROW + col) = kx;
-      *(uint4*)(Vst + row * C::KROW + col) = vx;
+  const int chunk = rest % E.chunks;
+  const int b = rest / E.chunks;
+  if (b >= p.batch) return;
+  const int g0 = kv_first_at(kvh);
+  const int gsz = kv_first_at(kvh + 1) - g0;
+  if (gsz <= 0) return;
+  const int nqb = (QP.sq + kQW - 1) / kQW;
+  int wg_qlo = INT32_MAX, wg_qhi = INT32_MIN;
+  int my_qb = -1, my_head = 0;
+  for (int wv = 0; wv < kWaves; ++wv) {
+    const int u = chunk * kWaves + wv;
+    const int qb = u / gsz;
+    if (qb >= nqb) continue;
+    wg_qlo = min(wg_qlo, qb * kQW);
+    wg_qhi = max(wg_qhi, min(QP.sq, qb * kQW + kQW));
+    if (wv == wave) {
+      my_qb = qb;
+      my_head = head_of(g0 + (u % gsz));
     }
   }
-  __syncthreads();
-  bf16x8 kf[C::KS], vf[C::KS];  // B operands of S = Q K^T and dP = dO V^T (this wave's 32 keys)
-  bf16x8 ktf[8];                // B operands of dQ = dS K (all 128 keys, this wave's d chunk)
-  // dQ work of this wave: d chunk dq_c for query sub-blocks dq_qs0 + u*(waves/NC)
-  const int dq_c = wave % C::NC;
-  const int dq_qs0 = wave / C::NC;
+  if (wg_qlo == INT32_MAX) return;
+  const bool active = my_qb >= 0;
+  const int q0 = active ? my_qb * kQW : wg_qlo;
+  int wg_pmin = 0, wg_pmax = 0, w_pmin = 0, w_pmax = 0;
+  if constexpr (MASKED) {
+    pos_minmax_dev(QP.qp, QP.sq, wg_qlo, wg_qhi, wg_pmin, wg_pmax);
+    pos_minmax_dev(QP.qp, QP.sq, q0, min(QP.sq, q0 + kQW), w_pmin, w_pmax);
+  }
+
+  // ---- Q and dO fragments (B operands), LSE2 and D of this lane's query ----
+  bf16x8 qf[C::KS], gf[C::KS];
+  float lse2 = INFINITY, dd = 0.f;
+  int qpos = INT32_MIN;
+  const int row = q0 + l32;
+  const bool row_ok = active && row < QP.sq;
   {
-    const __bf16* Kst = (const __bf16*)raw;
-    const __bf16* Vst = (const __bf16*)raw + C::KV_ELEMS;
-    const int krow = wave * 32 + l32;
+    const int64_t off = (int64_t)b * p.q_sb + (int64_t)my_head * p.q_sh + (int64_t)row * p.q_ss;
+    const __bf16* Qg = (const __bf16*)QP.q + off;
+    const __bf16* Gg = (const __bf16*)QP.dout + off;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      kf[ks] = *(const bf16x8*)(Kst + krow * C::KROW + ks * 16 + hl * 8);
-      vf[ks] = *(const bf16x8*)(Vst + krow * C::KROW + ks * 16 + hl * 8);
+      bf16x8 z = {};
+      qf[ks] = row_ok ? *(const bf16x8*)(Qg + ks * 16 + hl * 8) : z;
+      gf[ks] = row_ok ? *(const bf16x8*)(Gg + ks * 16 + hl * 8) : z;
     }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int row = kk * 16 + (G >> 1) * 8 + (lam >> 2);
-      const int col = dq_c * 32 + (G & 1) * 16 + (lam & 3) * 4;
-      ktf[kk] = concat_bf16x4(ds_read_tr16(Kst + row * C::KROW + col), ds_read_tr16(Kst + (row + 4) * C::KROW + col));
+    if (row_ok) {
+      const int nqb64 = (QP.sq + kBN - 1) / kBN;
+      const float* blk = QP.lsed + (((int64_t)b * p.hq + my_head) * nqb64 + row / kBN) * (2 * kBN);
+      lse2 = blk[row % kBN];
+      dd = blk[kBN + row % kBN];
+      if constexpr (MASKED) qpos = pos_at_dev(QP.qp, row);
     }
   }
-  __syncthreads();  // staging area becomes the Q/dO buffers
 
-  // ---- work items: (tile in this KV group, query head of the group, query block) ----
-  // flat item index: ti-major, then head, then query block
-  auto decode = [&](int it, int& ti, int& hi, int& qb) {
-    ti = 0;
-    int base = 0;
-    for (;;) {
-      const BwdTile& T = p.tiles[KV.tile_idx[ti]];
-      const int nqb = (T.sq + kBM - 1) / kBM;
-      const int n = nqb * gsz;
-      if (it < base + n || ti + 1 == KV.ntiles) {
-        const int r = it - base;
-        hi = r / nqb;
-        qb = r % nqb;
-        return;
-      }
-      base += n;
-      ++ti;
-    }
-  };
-  int nitems = 0;
-  for (int i = 0; i < KV.ntiles; ++i) nitems += ((p.tiles[KV.tile_idx[i]].sq + kBM - 1) / kBM) * gsz;
-  auto cls_of = [&](int it) -> int {
-    int ti, hi, qb;
-    decode(it, ti, hi, qb);
-    const BwdTile& T = p.tiles[KV.tile_idx[ti]];
-    const int r0 = qb * kBM, r1 = min(T.sq, r0 + kBM);
-    const bool tail = keys_here < kBN || (r1 - r0) < kBM;
-    if (!p.mask) return tail ? 1 : 2;
-    int qmin, qmax;
-    pos_minmax_dev(T.qp, T.sq, r0, r1, qmin, qmax);
-    if (kmin > qmax) return 0;
-    if (kmax <= qmin && !tail) return 2;
-    return 1;
-  };
-  auto next_item = [&](int from) -> int {
-    for (int it = from; it < nitems; ++it)
-      if (cls_of(it) != 0) return it;
-    return nitems;
-  };
-
-  uint4 qreg[C::QLOADS], goreg[C::QLOADS];
-  float lse_r = 0.f, dd_r = 0.f;
-  int qp_r = 0;
-  auto gload = [&](int it) {
-    int ti, hi, qb;
-    decode(it, ti, hi, qb);
-    const BwdTile& T = p.tiles[KV.tile_idx[ti]];
-    const int h = p.heads_of[g0 + hi];
-    const int r0 = qb * kBM;
-    const __bf16* Qg = (const __bf16*)T.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
-    const __bf16* Gg = (const __bf16*)T.dout + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+  // ---- key blocks of every KV partition of the group ----
+  PartnerWalk walk;
+  walk.n = E.n;
+  int total = 0;
 #pragma unroll
-    for (int i = 0; i < C::QLOADS; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / C::CH, col = (c % C::CH) * 8;
-      const int t = r0 + row;
-      if (t < T.sq) {
-        qreg[i] = *(const uint4*)(Qg + (int64_t)t * p.q_ss + col);
-        goreg[i] = *(const uint4*)(Gg + (int64_t)t * p.q_ss + col);
-      } else {
-        qreg[i] = make_uint4(0, 0, 0, 0);
-        goreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (tid < kBM) {
-      const int t = r0 + tid;
-      if (t < T.sq) {
-        const float L = T.lse[(int64_t)b * p.l_sb + (int64_t)h * p.l_sh + t];
-        lse_r = (L == -INFINITY) ? INFINITY : L * 1.4426950408889634f;  // +inf makes P = 0 on empty rows
-        dd_r = T.dscratch[((int64_t)b * p.hq + h) * T.sq + t];
-        qp_r = p.mask ? pos_at_dev(T.qp, t) : 0;
-      } else {
-        lse_r = INFINITY;
-        dd_r = 0.f;
-        qp_r = INT32_MIN;
-      }
+  for (int i = 0; i < kBwdPerLaunch; ++i) {
+    walk.nb[i] = i < E.n ? (kvpart_at(partner_at(ei, i)).sk + kBN - 1) / kBN : 0;
+    total += walk.nb[i];
+  }
+  auto block_class = [&](int g, int pmin, int pmax) -> int {  // 0 empty, 1 partial, 2 full
+    int pi, kb;
+    walk.decode(g, pi, kb);
+    const BwdKVPart KV = kvpart_at(partner_at(ei, pi));
+    const bool tail = kb * kBN + kBN > KV.sk;
+    if constexpr (!MASKED) {
+      return tail ? 1 : 2;
+    } else {
+      int kmin, kmax;
+      pos_minmax_dev(KV.kp, KV.sk, kb * kBN, min(KV.sk, kb * kBN + kBN), kmin, kmax);
+      if (kmin > pmax) return 0;
+      if (kmax <= pmin && !tail) return 2;
+      return 1;
     }
   };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::QLOADS; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / C::CH, col = (c % C::CH) * 8;
-      *(uint4*)(qdo + buf * C::Q_ELEMS + row * C::QROW + col) = qreg[i];
-      *(uint4*)(qdo + (2 + buf) * C::Q_ELEMS + row * C::QROW + col) = goreg[i];
-    }
-    if (tid < kBM) {
-      lse2_s[buf][tid] = lse_r;
-      dd_s[buf][tid] = dd_r;
-      qpos_s[buf][tid] = qp_r;
+  auto next_block = [&](int from) -> int {
+    if constexpr (!MASKED) {
+      return from < total ? from : total;
+    } else {
+      for (int g = from; g < total; ++g)
+        if (block_class(g, wg_pmin, wg_pmax) != 0) return __builtin_amdgcn_readfirstlane(g);
+      return total;
     }
   };
 
-  f32x16 dk_acc[C::NC], dv_acc[C::NC];
+  // ---- direct-to-LDS loads of one K block and one V block ----
+  auto load_row = [&](int i) { return ((wave * LPW + i) * 64 + lane) / C::CH; };
+  auto load_col = [&](int i) { return ((((wave * LPW + i) * 64 + lane) % C::CH) ^ swz<D>(load_row(i))) * 8; };
+  const int k_ss = (int)p.k_ss;  // below 2^24 (checked by the caller)
+  uint32_t go[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) go[i] = (uint32_t)(load_row(i) * k_ss + load_col(i)) * 2u;
+  auto issue = [&](int st, int g) {
+    int pi, kb;
+    walk.decode(g, pi, kb);
+    const BwdKVPart KV = kvpart_at(partner_at(ei, pi));
+    const int64_t off = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + (int64_t)kb * kBN * p.k_ss;
+    const __bf16* kbase = (const __bf16*)KV.k + off;
+    const __bf16* vbase = (const __bf16*)KV.v + off;
+    const int valid = KV.sk - kb * kBN;
+    if (valid >= kBN) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        lds_dma16(kbase, go[i], lds_addr(&kv_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(vbase, go[i], lds_addr(&kv_s[1][st][(wave * LPW + i) * 512]));
+      }
+    } else {  // ragged last block: repeat the last row (finite; masked)
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const uint32_t o2 = (uint32_t)(min(load_row(i), valid - 1) * k_ss + load_col(i)) * 2u;
+        lds_dma16(kbase, o2, lds_addr(&kv_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(vbase, o2, lds_addr(&kv_s[1][st][(wave * LPW + i) * 512]));
+      }
+    }
+  };
+  auto wait_positions = [&](int n) {  // at most n later positions in flight
+    if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW));
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+
+  uint32_t kaddr[C::KS], ktr[C::NC][2], vaddr[C::KS], vtr_unused[C::NC][2];
+  tile_lane_addrs<D>(kv_s[0][0], lane, kaddr, ktr);
+  tile_lane_addrs<D>(kv_s[1][0], lane, vaddr, vtr_unused);
+
+  f32x16 acc[C::NC];  // dQ^T: lane's query, d = 32c + 8(e/4) + 4hl + e%4
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) acc[c] = f32x16{};
+  const float c2 = p.scale_log2;
+
+  // S^T and dP^T of one 32-key half (kb2) of the block in stage st
+  auto sdp_half = [&](int st, int kb2, f32x16& s, f32x16& dp) {
+    const uint32_t off = st * C::STAGE_BYTES + kb2 * 32 * D * 2;
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 kf = lds_read_b128(kaddr[ks] + off);
+      const bf16x8 vf = lds_read_b128(vaddr[ks] + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[ks], dp, 0, 0, 0);
+    }
+  };
+  // mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8
+  auto mask_half = [&](int g, int kb2, f32x16& s) {
+    const int cls = active ? block_class(g, w_pmin, w_pmax) : 1;
+    if (cls == 2) return;
+    int pi, kb;
+    walk.decode(g < total ? g : total - 1, pi, kb);
+    if (g >= total) kb += 1 << 20;  // past the end: every key masked
+    const BwdKVPart KV = kvpart_at(partner_at(ei, pi));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {  // branch-free: position at a clamped index, then a select
+      const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
+      bool ok = key < KV.sk;
+      if constexpr (MASKED) ok = ok & (pos_at_dev(KV.kp, min(key, KV.sk - 1)) <= qpos);
+      s[e] = ok ? s[e] : -INFINITY;
+    }
+  };
+  // one 32-key step: P, dS of the current half; S^T, dP^T of the next half under
+  // the exponentials; dQ^T += K^T dS^T; mask of the next half
+  auto half_step = [&](int st, int kb2, f32x16& sc, f32x16& dc, int ng, int nst, int nkb2, f32x16& sn, f32x16& dn) {
+    bf16x8 dsf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j * 8 + i], c2, -lse2));
+        v[i] = pe * (dc[j * 8 + i] - dd);
+      }
+      dsf[j] = pack_bf16x8(v);
+    }
+    sdp_half(nst, nkb2, sn, dn);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t off = st * C::STAGE_BYTES + (kb2 * 2 + j) * 16 * D * 2;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const bf16x8 kt = concat_bf16x4(lds_read_tr16(ktr[c][0] + off), lds_read_tr16(ktr[c][1] + off));
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[j], acc[c], 0, 0, 0);
+      }
+    }
+    mask_half(ng, nkb2, sn);
+  };
+
+  // ---- pipeline (the forward's): position j in stage j % 4, loaded 2 ahead ----
+  int bj0 = next_block(0);
+  int bj1 = bj0 < total ? next_block(bj0 + 1) : total;
+  int bj2 = bj1 < total ? next_block(bj1 + 1) : total;
+  if (bj0 < total) issue(0, bj0);
+  if (bj1 < total) issue(1, bj1);
+  if (bj2 < total) issue(2, bj2);
+  f32x16 sA, dA, sB, dB;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // also retires the fragment loads
+  if (bj0 < total) {
+    __syncthreads();
+    sdp_half(0, 0, sA, dA);
+    mask_half(bj0, 0, sA);
+  }
+#define MA_DQ_BLOCK(ST)                                                  \
+  {                                                                      \
+    half_step((ST), 0, sA, dA, bj0, (ST), 1, sB, dB);                    \
+    const int bj3 = bj2 < total ? next_block(bj2 + 1) : total;           \
+    wait_positions(bj2 < total ? 1 : 0);                                 \
+    __syncthreads();                                                     \
+    if (bj3 < total) issue(((ST) + 3) & 3, bj3);                         \
+    half_step((ST), 1, sB, dB, bj1, ((ST) + 1) & 3, 0, sA, dA);          \
+    bj0 = bj1;                                                           \
+    bj1 = bj2;                                                           \
+    bj2 = bj3;                                                           \
+    if (bj0 >= total) break;                                             \
+  }
+  while (bj0 < total) {
+    MA_DQ_BLOCK(0)
+    MA_DQ_BLOCK(1)
+    MA_DQ_BLOCK(2)
+    MA_DQ_BLOCK(3)
+  }
+#undef MA_DQ_BLOCK
+
+  if (!row_ok) return;
+  float* dQg = QP.dq + (int64_t)b * p.dq_sb + (int64_t)my_head * p.dq_sh + (int64_t)row * p.dq_ss;
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float4 v = make_float4(acc[c][4 * g] * p.scale, acc[c][4 * g + 1] * p.scale, acc[c][4 * g + 2] * p.scale,
+                             acc[c][4 * g + 3] * p.scale);
+      float4* dst = (float4*)(dQg + c * 32 + 8 * g + 4 * hl);
+      if (E.accumulate) {
+        const float4 o = *dst;
+        v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+      }
+      *dst = v;
+    }
+}
+
+// --------------------------------------------------------------- dK/dV kernel --
+template <int D, bool MASKED>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkv_kernel(const BwdParams p) {
+  using C = Cfg<D>;
+  constexpr int kWaves = 4, kKW = 32;
+  constexpr int LPW = kBN * C::CH / 64 / kWaves;
+  // Q stages, then dO stages; LSE2/D blocks
+  __shared__ __attribute__((aligned(1024))) __bf16 qd_s[2][kStages][C::BLK];
+  __shared__ __attribute__((aligned(1024))) float ld_s[kStages][2 * kBN];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  // ---- entry (KV group) / batch / KV head / key block ----
+  const int w = blockIdx.x;
+  int ei = 0;
+  while (ei + 1 < p.nentries && w >= entry_at(ei + 1).wg_begin) ++ei;
+  ei = __builtin_amdgcn_readfirstlane(ei);
+  const BwdEntry E = entry_at(ei);
+  const BwdKVPart KV = kvpart_at(E.self);
+  const int local = w - E.wg_begin;
+  const int kvh = local % p.hkv;
+  const int rest = local / p.hkv;
+  const int kblk = rest % E.chunks;
+  const int b = rest / E.chunks;
+  if (b >= p.batch) return;
+  const int g0 = kv_first_at(kvh);
+  const int gsz = kv_first_at(kvh + 1) - g0;
+  const int key0 = kblk * (kWaves * kKW);
+  const int wg_keys = min(kWaves * kKW, KV.sk - key0);
+  if (gsz <= 0 || wg_keys <= 0) return;
+  const int my_key = key0 + wave * kKW + l32;
+  const bool key_ok = my_key < KV.sk;
+  const bool wg_tail = wg_keys < kWaves * kKW;
+  int wg_kmin = 0, wg_kmax = 0, w_kmin = 0, w_kmax = 0, my_kpos = INT32_MAX;
+  if constexpr (MASKED) {
+    pos_minmax_dev(KV.kp, KV.sk, key0, key0 + wg_keys, wg_kmin, wg_kmax);
+    const int wk0 = min(KV.sk - 1, key0 + wave * kKW);
+    pos_minmax_dev(KV.kp, KV.sk, wk0, min(KV.sk, key0 + wave * kKW + kKW), w_kmin, w_kmax);
+    if (key_ok) my_kpos = pos_at_dev(KV.kp, my_key);
+  }
+
+  // ---- K^T and V^T fragments of this lane's key (B operands) ----
+  bf16x8 kf[C::KS], vf[C::KS];
+  {
+    const int64_t off = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + (int64_t)my_key * p.k_ss;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8 z = {};
+      kf[ks] = key_ok ? *(const bf16x8*)((const __bf16*)KV.k + off + ks * 16 + hl * 8) : z;
+      vf[ks] = key_ok ? *(const bf16x8*)((const __bf16*)KV.v + off + ks * 16 + hl * 8) : z;
+    }
+  }
+
+  // ---- query blocks: (Q partition, head of the group, 64-row block), flattened ----
+  PartnerWalk walk;  // blocks per partner = heads x 64-row blocks
+  walk.n = E.n;
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < kBwdPerLaunch; ++i) {
+    walk.nb[i] = i < E.n ? gsz * ((qpart_at(partner_at(ei, i)).sq + kBN - 1) / kBN) : 0;
+    total += walk.nb[i];
+  }
+  auto decode = [&](int g, int& pi, int& hi, int& qb) {
+    int blk;
+    walk.decode(g, pi, blk);
+    const int nqb = (qpart_at(partner_at(ei, pi)).sq + kBN - 1) / kBN;
+    hi = __builtin_amdgcn_readfirstlane(blk / nqb);
+    qb = __builtin_amdgcn_readfirstlane(blk % nqb);
+  };
+  auto block_class = [&](int g, int kmin, int kmax, bool ktail) -> int {  // 0 empty, 1 partial, 2 full
+    if constexpr (!MASKED) {
+      return ktail ? 1 : 2;
+    } else {
+      int pi, hi, qb;
+      decode(g, pi, hi, qb);
+      const BwdQPart QP = qpart_at(partner_at(ei, pi));
+      int qmin, qmax;
+      pos_minmax_dev(QP.qp, QP.sq, qb * kBN, min(QP.sq, qb * kBN + kBN), qmin, qmax);
+      if (kmin > qmax) return 0;
+      if (kmax <= qmin && !ktail) return 2;
+      return 1;
+    }
+  };
+  auto next_block = [&](int from) -> int {
+    if constexpr (!MASKED) {
+      return from < total ? from : total;
+    } else {
+      for (int g = from; g < total; ++g)
+        if (block_class(g, wg_kmin, wg_kmax, false) != 0) return __builtin_amdgcn_readfirstlane(g);
+      return total;
+    }
+  };
+  const bool w_ktail = key0 + wave * kKW + kKW > KV.sk;
+
+  // ---- direct-to-LDS loads of one Q block, one dO block and the LSE2/D block ----
+  auto load_row = [&](int i) { return ((wave * LPW + i) * 64 + lane) / C::CH; };
+  auto load_col = [&](int i) { return ((((wave * LPW + i) * 64 + lane) % C::CH) ^ swz<D>(load_row(i))) * 8; };
+  const int q_ss = (int)p.q_ss;  // below 2^24 (checked by the caller)
+  uint32_t go[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) go[i] = (uint32_t)(load_row(i) * q_ss + load_col(i)) * 2u;
+  auto issue = [&](int st, int g) {
+    int pi, hi, qb;
+    decode(g, pi, hi, qb);
+    const BwdQPart QP = qpart_at(partner_at(ei, pi));
+    const int h = head_of(g0 + hi);
+    const int64_t off = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)qb * kBN * p.q_ss;
+    const __bf16* qbase = (const __bf16*)QP.q + off;
+    const __bf16* gbase = (const __bf16*)QP.dout + off;
+    const int valid = QP.sq - qb * kBN;
+    if (valid >= kBN) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        lds_dma16(qbase, go[i], lds_addr(&qd_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(gbase, go[i], lds_addr(&qd_s[1][st][(wave * LPW + i) * 512]));
+      }
+    } else {  // ragged last block: repeat the last row (finite; its LSE2 is +inf so P = 0)
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const uint32_t o2 = (uint32_t)(min(load_row(i), valid - 1) * q_ss + load_col(i)) * 2u;
+        lds_dma16(qbase, o2, lds_addr(&qd_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(gbase, o2, lds_addr(&qd_s[1][st][(wave * LPW + i) * 512]));
+      }
+    }
+    // the 512-byte LSE2/D block: each wave brings 128 bytes with its first 8 lanes
+    const int nqb64 = (QP.sq + kBN - 1) / kBN;
+    const float* lblk = QP.lsed + (((int64_t)b * p.hq + h) * nqb64 + qb) * (2 * kBN);
+    if (lane < 8) lds_dma16(lblk, (uint32_t)(wave * 128 + lane * 16), lds_addr(&ld_s[st][wave * 32]));
+  };
+  auto wait_positions = [&](int n) {  // at most n later positions in flight
+    if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (2 * LPW + 1)));
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW + 1));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+
+  uint32_t qaddr[C::KS], qtr[C::NC][2], gaddr[C::KS], gtr[C::NC][2];
+  tile_lane_addrs<D>(qd_s[0][0], lane, qaddr, qtr);
+  tile_lane_addrs<D>(qd_s[1][0], lane, gaddr, gtr);
+  const uint32_t laddr = lds_lane_addr(&ld_s[0][8 * hl]);  // + 32u (+16) floats; D at +64 floats
+  constexpr uint32_t kLdStage = 2 * kBN * 4;
+
+  f32x16 dk_acc[C::NC], dv_acc[C::NC];  // rows = keys 8(e/4) + 4hl + e%4 of the wave, column d = 32c + l32
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) {
     dk_acc[c] = f32x16{};
@@ -283,132 +564,116 @@ bwd_main_kernel(const BwdParams p) {
   }
   const float c2 = p.scale_log2;
 
-  int it = next_item(0);
-  int buf = 0;
-  if (it < nitems) {
-    gload(it);
-    swrite(0);
-  }
-  __syncthreads();
-  int it_next = (it < nitems) ? next_item(it + 1) : nitems;
-  if (it_next < nitems) gload(it_next);
-
-  while (it < nitems) {
-    const int cls = cls_of(it);
-    const __bf16* Ql = qdo + buf * C::Q_ELEMS;
-    const __bf16* Gl = qdo + (2 + buf) * C::Q_ELEMS;
-    // S = Q K^T and dP = dO V^T for two 32-row query sub-blocks (one key per lane)
-    f32x16 s[2], dp[2];
+  // S and dP of one 32-query half (u) of the block in stage st
+  auto sdp_half = [&](int st, int u, f32x16& s, f32x16& dp) {
+    const uint32_t off = st * C::STAGE_BYTES + u * 32 * D * 2;
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      s[qs] = f32x16{};
-      dp[qs] = f32x16{};
-      const int qrow = qs * 32 + perm_row(l32);
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 qa = *(const bf16x8*)(Ql + qrow * C::QROW + ks * 16 + hl * 8);
-        const bf16x8 ga = *(const bf16x8*)(Gl + qrow * C::QROW + ks * 16 + hl * 8);
-        s[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s[qs], 0, 0, 0);
-        dp[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp[qs], 0, 0, 0);
-      }
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 qa = lds_read_b128(qaddr[ks] + off);
+      const bf16x8 ga = lds_read_b128(gaddr[ks] + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
     }
-    // P and dS; element e of lane half hl is query qs*32 + 16*(e/8) + 8*hl + e%8
-    bf16x8 pf[4], dsf[4];
+  };
+  // one 32-query step: element e of the lane is query 32u + 16(e/8) + 8hl + e%8
+  auto half_step = [&](int g, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu, f32x16& sn, f32x16& dn) {
+    const uint32_t lo = laddr + st * kLdStage + u * 32 * 4;
+    const f32x4 l0 = lds_read_f32x4(lo), l1 = lds_read_f32x4(lo + 16);
+    const f32x4 l2 = lds_read_f32x4(lo + 64), l3 = lds_read_f32x4(lo + 80);
+    const f32x4 d0 = lds_read_f32x4(lo + 256), d1 = lds_read_f32x4(lo + 272);
+    const f32x4 d2 = lds_read_f32x4(lo + 320), d3 = lds_read_f32x4(lo + 336);
+    const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
+                          l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
+    const float dv[16] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
+                          d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
+    float pe[16];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c2, -lv[e]));
+    const int cls = block_class(g, w_kmin, w_kmax, w_ktail);
+    if (cls != 2) {  // element mask: key allowed for query, key inside the partition
+      int pi, hi, qb;
+      decode(g, pi, hi, qb);
+      const BwdQPart QP = qpart_at(partner_at(ei, pi));
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int q0 = qs * 32 + half * 16 + hl * 8;
-        const f32x4 l0 = *(const f32x4*)(&lse2_s[buf][q0]);
-        const f32x4 l1 = *(const f32x4*)(&lse2_s[buf][q0 + 4]);
-        const f32x4 d0 = *(const f32x4*)(&dd_s[buf][q0]);
-        const f32x4 d1 = *(const f32x4*)(&dd_s[buf][q0 + 4]);
-        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-        const float dv8[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-        float pv[8], sv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = half * 8 + i;
-          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qs][e], c2, -lv[i]));
-          if (cls == 1) {
-            if (!(my_kpos <= qpos_s[buf][q0 + i])) pe = 0.f;
-          }
-          pv[i] = pe;
-          sv[i] = pe * (dp[qs][e] - dv8[i]);
+      for (int e = 0; e < 16; ++e) {  // branch-free: position at a clamped index, then a select
+        bool ok = key_ok;
+        if constexpr (MASKED) {
+          const int t = min(QP.sq - 1, qb * kBN + 32 * u + 16 * (e >> 3) + 8 * hl + (e & 7));
+          ok = ok & (my_kpos <= pos_at_dev(QP.qp, t));
         }
-        pf[qs * 2 + half] = pack_bf16x8(pv);
-        dsf[qs * 2 + half] = pack_bf16x8(sv);
+        pe[e] = ok ? pe[e] : 0.f;
       }
     }
-    // dV += P^T dO and dK += dS^T Q (B operands read transposed from LDS)
+    bf16x8 pf[2], dsf[2];
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
+    for (int j = 0; j < 2; ++j) {
+      float ds[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = j * 16 + (G >> 1) * 8 + (lam >> 2);
-        const int col = c * 32 + (G & 1) * 16 + (lam & 3) * 4;
-        const bf16x8 gt = concat_bf16x4(ds_read_tr16(Gl + row * C::QROW + col), ds_read_tr16(Gl + (row + 4) * C::QROW + col));
-        const bf16x8 qt = concat_bf16x4(ds_read_tr16(Ql + row * C::QROW + col), ds_read_tr16(Ql + (row + 4) * C::QROW + col));
+      for (int i = 0; i < 8; ++i) ds[i] = pe[j * 8 + i] * (dc[j * 8 + i] - dv[j * 8 + i]);
+      pf[j] = pack_bf16x8(&pe[j * 8]);
+      dsf[j] = pack_bf16x8(ds);
+    }
+    sdp_half(nst, nu, sn, dn);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t off = st * C::STAGE_BYTES + (u * 2 + j) * 16 * D * 2;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const bf16x8 gt = concat_bf16x4(lds_read_tr16(gtr[c][0] + off), lds_read_tr16(gtr[c][1] + off));
+        const bf16x8 qt = concat_bf16x4(lds_read_tr16(qtr[c][0] + off), lds_read_tr16(qtr[c][1] + off));
         dv_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[j], gt, dv_acc[c], 0, 0, 0);
         dk_acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsf[j], qt, dk_acc[c], 0, 0, 0);
       }
     }
-    // dS^T to LDS: this lane's key row, 8 consecutive queries per store
-    {
-      __bf16* Sl = dS_s[buf] + (wave * 32 + l32) * C::SROW;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *(bf16x8*)(Sl + j * 16 + hl * 8) = dsf[j];
-    }
-    // stage the next item, then fetch the one after it
-    int ti_cur, hi_cur, qb_cur;
-    decode(it, ti_cur, hi_cur, qb_cur);
-    const int it_after = (it_next < nitems) ? next_item(it_next + 1) : nitems;
-    if (it_next < nitems) swrite(buf ^ 1);
-    __syncthreads();
-    if (it_after < nitems) gload(it_after);
-    // dQ (this wave's units) = dS K over all 128 keys, added to global dQ
-    {
-      const BwdTile& T = p.tiles[KV.tile_idx[ti_cur]];
-      const int h = p.heads_of[g0 + hi_cur];
-      float* dQg = T.dq + (int64_t)b * p.dq_sb + (int64_t)h * p.dq_sh;
-      const __bf16* Sl = dS_s[buf];
-#pragma unroll
-      for (int u = 0; u < C::DQ_UNITS; ++u) {
-        const int qs = dq_qs0 + u * (kWaves / C::NC);
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const int row = kk * 16 + (G >> 1) * 8 + (lam >> 2);        // key
-          const int col = qs * 32 + (G & 1) * 16 + (lam & 3) * 4;      // query
-          const bf16x8 sa = concat_bf16x4(ds_read_tr16(Sl + row * C::SROW + col), ds_read_tr16(Sl + (row + 4) * C::SROW + col));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, ktf[kk], acc, 0, 0, 0);
-        }
-        // lane holds d = 32*c + l32 for query rows (i/4)*8 + hl*4 + i%4 of the sub-block
-        const int d = dq_c * 32 + l32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = qb_cur * kBM + qs * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-          if (t < T.sq) unsafeAtomicAdd(dQg + (int64_t)t * p.dq_ss + d, acc[i] * p.scale);
-        }
-      }
-    }
-    it = it_next;
-    it_next = it_after;
-    buf ^= 1;
-  }
+  };
 
-  // ---- dK (scaled) and dV: this wave's 32 keys; lane holds d = 32c + l32 ----
+  int bj0 = next_block(0);
+  int bj1 = bj0 < total ? next_block(bj0 + 1) : total;
+  int bj2 = bj1 < total ? next_block(bj1 + 1) : total;
+  if (bj0 < total) issue(0, bj0);
+  if (bj1 < total) issue(1, bj1);
+  if (bj2 < total) issue(2, bj2);
+  f32x16 sA, dA, sB, dB;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // also retires the fragment loads
+  if (bj0 < total) {
+    __syncthreads();
+    sdp_half(0, 0, sA, dA);
+  }
+#define MA_DKV_BLOCK(ST)                                                 \
+  {                                                                      \
+    half_step(bj0, (ST), 0, sA, dA, (ST), 1, sB, dB);                    \
+    const int bj3 = bj2 < total ? next_block(bj2 + 1) : total;           \
+    wait_positions(bj2 < total ? 1 : 0);                                 \
+    __syncthreads();                                                     \
+    if (bj3 < total) issue(((ST) + 3) & 3, bj3);                         \
+    half_step(bj0, (ST), 1, sB, dB, ((ST) + 1) & 3, 0, sA, dA);          \
+    bj0 = bj1;                                                           \
+    bj1 = bj2;                                                           \
+    bj2 = bj3;                                                           \
+    if (bj0 >= total) break;                                             \
+  }
+  while (bj0 < total) {
+    MA_DKV_BLOCK(0)
+    MA_DKV_BLOCK(1)
+    MA_DKV_BLOCK(2)
+    MA_DKV_BLOCK(3)
+  }
+#undef MA_DKV_BLOCK
+
+  // ---- dK (scaled) and dV of the wave's 32 keys ----
   float* dKg = KV.dk + (int64_t)b * p.dk_sb + (int64_t)kvh * p.dk_sh;
   float* dVg = KV.dv + (int64_t)b * p.dk_sb + (int64_t)kvh * p.dk_sh;
 #pragma unroll
   for (int c = 0; c < C::NC; ++c)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = key0 + wave * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + wave * kKW + (e >> 2) * 8 + hl * 4 + (e & 3);
       if (key < KV.sk) {
         const int64_t off = (int64_t)key * p.dk_ss + c * 32 + l32;
-        float kv = dk_acc[c][i] * p.scale, vv = dv_acc[c][i];
-        if (KV.accumulate) {
+        float kv = dk_acc[c][e] * p.scale, vv = dv_acc[c][e];
+        if (E.accumulate) {
           kv += dKg[off];
           vv += dVg[off];
         }
@@ -420,29 +685,44 @@ bwd_main_kernel(const BwdParams p) {
 
 }  // namespace
 
-int launch_bwd_preprocess(const BwdParams& p, int head_dim, void* stream) {
-  for (int t = 0; t < p.ntiles; ++t) {
-    if (p.tiles[t].sq <= 0) continue;
-    const int64_t rows = (int64_t)p.batch * p.tiles[t].sq * p.hq;
-    const int rpb = 256 / (head_dim / 8);
-    const int64_t blocks = (rows + rpb - 1) / rpb;
-    const int zero = p.tiles[t].zero_dq;
-    if (head_dim == 128)
-      hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p, t, zero);
-    else
-      hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p, t, zero);
-    const int e = (int)hipGetLastError();
-    if (e) return e;
-  }
-  return 0;
+int launch_bwd_preprocess(const BwdPreParams& p, int head_dim, void* stream) {
+  const int64_t nqb = (p.sq + kBN - 1) / kBN;
+  const int64_t rows = (int64_t)p.batch * nqb * kBN * p.hq;
+  const int rpb = 256 / (head_dim / 8);
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  if (blocks <= 0) return 0;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
 }
 
-int launch_bwd_main(const BwdParams& p, int head_dim, int total_wgs, void* stream) {
+int launch_bwd_dq(const BwdParams& p, int head_dim, int total_wgs, void* stream) {
   if (total_wgs <= 0) return 0;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(bwd_main_kernel<128>, dim3(total_wgs), dim3(kThreads), 0, (hipStream_t)stream, p);
-  else
-    hipLaunchKernelGGL(bwd_main_kernel<64>, dim3(total_wgs), dim3(kThreads), 0, (hipStream_t)stream, p);
+  hipStream_t s = (hipStream_t)stream;
+  dim3 g(total_wgs), blk(512);
+  if (head_dim == 128) {
+    if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), g, blk, 0, s, p);
+  } else {
+    if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<64, false>), g, blk, 0, s, p);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_bwd_dkv(const BwdParams& p, int head_dim, int total_wgs, void* stream) {
+  if (total_wgs <= 0) return 0;
+  hipStream_t s = (hipStream_t)stream;
+  dim3 g(total_wgs), blk(256);
+  if (head_dim == 128) {
+    if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<128, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkv_kernel<128, false>), g, blk, 0, s, p);
+  } else {
+    if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<64, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkv_kernel<64, false>), g, blk, 0, s, p);
+  }
   return (int)hipGetLastError();
 }
 

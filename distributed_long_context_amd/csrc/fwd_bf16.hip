@@ -61,62 +61,6 @@ struct FwdCfg {
   static constexpr int LPW = kBN * CH / 64 / kWaves;  // direct-to-LDS loads per wave per tensor
 };
 
-// XOR mask applied to the 16-byte chunk index of LDS row `row` (period 16 rows).
-// D=128 (one row = 64 banks): rows 0..15 map a chunk to 16 distinct chunks, and
-// rows 4k..4k+3 to distinct 64-byte groups.  D=64 (two rows per bank line): the
-// same two properties over (row parity, chunk).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-__device__ __forceinline__ int perm_key(int m) {  // swap bits 2 and 3
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-__device__ __forceinline__ float xhalf_max(float x) {  // max(x[l], x[l ^ 32])
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {  // x[l] + x[l ^ 32]
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Byte address of an LDS location, made opaque to the optimiser so that later
-// constant offsets (stage, slice) fold into the 16-bit immediate of the DS
-// instruction instead of creating one address register per constant.
-__device__ __forceinline__ uint32_t lds_lane_addr(const void* p) {
-  uint32_t a = (uint32_t)(uintptr_t)(const lds_char*)p;
-  asm volatile("" : "+v"(a));
-  return a;
-}
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane i's bytes land at LDS byte address lds_dst + 16 i.  Written as inline asm
-// so that the compiler does not add vmcnt(0) waits in front of every LDS read;
-// the kernel orders these loads itself with s_waitcnt vmcnt and a barrier.
-__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff_bytes, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff_bytes), "s"(gbase), "s"(lds_dst) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_char*)p; }
-__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
-  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
-}
-__device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
-  typedef short i16x4 __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                        (__attribute__((address_space(3))) i16x4*)(uintptr_t)addr));
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of this
-// wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left free)
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
 template <int D, bool MASKED>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -135,7 +79,9 @@ fwd_bf16_kernel(const FwdParams p) {
   const int w = blockIdx.x;
   int ti = 0;
   while (ti + 1 < p.ntiles && w >= p.tiles[ti + 1].wg_begin) ++ti;
-  const FwdTile& T = p.tiles[ti];
+  // by value, with a provably uniform index: the parameter block stays in the
+  // kernel-argument segment (scalar loads) instead of being copied to scratch
+  const FwdTile T = p.tiles[__builtin_amdgcn_readfirstlane(ti)];
   const int local = w - T.wg_begin;
   const int kvh = local % p.hkv;
   const int rest = local / p.hkv;
@@ -250,23 +196,9 @@ fwd_bf16_kernel(const FwdParams p) {
   };
 
   // ---- per-lane LDS byte addresses of the K and V^T fragments (stage 0, first slice) ----
-  uint32_t kaddr[C::KS];  // K row perm(l32) (+32 rows for the second 32-key half), chunk 2ks+hl
-  {
-    const int row = perm_key(l32);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      kaddr[ks] = lds_lane_addr(&kv_s[0][0][row * D + (((2 * ks + hl) ^ swz<D>(row)) << 3)]);
-  }
-  const int G = lane >> 4, lam = lane & 15;
-  uint32_t vaddr[C::NC][2];  // V rows (G>>1)*8 + lam/4 (+4), columns c*32 + (G&1)*16 + (lam&3)*4 (+16 rows per slice)
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = (G >> 1) * 8 + (lam >> 2) + h * 4;
-      const int col = c * 32 + (G & 1) * 16 + (lam & 3) * 4;
-      vaddr[c][h] = lds_lane_addr(&kv_s[1][0][row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7)]);
-    }
+  uint32_t kaddr[C::KS], kaddr_tr_unused[C::NC][2], vaddr_b128_unused[C::KS], vaddr[C::NC][2];
+  tile_lane_addrs<D>(kv_s[0][0], lane, kaddr, kaddr_tr_unused);
+  tile_lane_addrs<D>(kv_s[1][0], lane, vaddr_b128_unused, vaddr);
   constexpr uint32_t kStageBytes = C::BLK * 2;
 
   // ---- accumulators ----
@@ -291,14 +223,11 @@ fwd_bf16_kernel(const FwdParams p) {
   // element mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8
   auto mask_half = [&](int kb, int kb2, f32x16& s) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 16; ++e) {  // branch-free: position at a clamped index, then a select
       const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-      if constexpr (MASKED) {
-        const int kp = key < T.sk ? pos_at_dev(T.kp, key) : INT32_MAX;
-        if (!(kp <= qpos)) s[e] = -INFINITY;
-      } else {
-        if (key >= T.sk) s[e] = -INFINITY;
-      }
+      bool ok = key < T.sk;
+      if constexpr (MASKED) ok = ok & (pos_at_dev(T.kp, min(key, T.sk - 1)) <= qpos);
+      s[e] = ok ? s[e] : -INFINITY;
     }
   };
 

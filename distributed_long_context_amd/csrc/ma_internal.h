@@ -75,50 +75,69 @@ struct MergeParams {
 int launch_merge(const MergeParams& p, int dtype, int head_dim, void* stream);
 
 // ---- backward ----
-constexpr int kBwdTilesPerLaunch = 8;
+// The backward runs per (Q partition, KV partition) pair ([Mesh] section 3.5).
+// Tiles sharing a dq buffer form a Q group (same Q partition), tiles sharing a
+// dk/dv buffer form a KV group.  The dQ kernel takes one Q group per work entry
+// and walks all its KV partitions; the dK/dV kernel takes one KV group per
+// entry and walks all its Q partitions; neither needs atomics.
+constexpr int kBwdPerLaunch = 8;
 
-struct BwdTile {
+struct BwdQPart {        // a Q partition and its dq buffer
   const void* q;
-  const void* o;
   const void* dout;
-  const float* lse;
+  const float* lsed;     // workspace: per (b, h, 64-row block) [LSE*log2(e) x 64, D x 64] fp32
   float* dq;
-  float* dscratch;  // D = rowsum(dO*O), [B, Hq, sq] float32 in the workspace
   int32_t sq;
-  int32_t zero_dq;  // clear dq in the preprocessing pass (overwrite mode)
   KPos qp;
 };
 
-struct BwdKV {  // one KV partition with the tiles that read it
+struct BwdKVPart {       // a KV partition and its dk, dv buffers
   const void* k;
   const void* v;
   float* dk;
   float* dv;
   int32_t sk;
-  int32_t ntiles;
-  int32_t wg_begin;    // first workgroup of this KV partition in the launch
-  int32_t accumulate;  // add dK/dV to the buffers instead of overwriting
-  int32_t tile_idx[kBwdTilesPerLaunch];
   KPos kp;
 };
 
+struct BwdEntry {        // one group: its own partition and the partner partitions it meets
+  int32_t self;          // index into qparts (dQ launch) or kvparts (dK/dV launch)
+  int32_t n;             // number of partners
+  int32_t partner[kBwdPerLaunch];
+  int32_t wg_begin;      // first workgroup of this entry in the launch
+  int32_t chunks;        // workgroups per (batch, KV head)
+  int32_t accumulate;    // add to the output buffers instead of overwriting
+};
+
 struct BwdParams {
-  int32_t nkv, ntiles;
+  int32_t nentries;
   int32_t batch, hq, hkv, gmax;
   int32_t mask;
-  int32_t accumulate;
   float scale, scale_log2;
   int64_t q_sb, q_ss, q_sh;    // q, o, dout
   int64_t k_sb, k_ss, k_sh;    // k, v
   int64_t dq_sb, dq_ss, dq_sh;
   int64_t dk_sb, dk_ss, dk_sh;
-  int64_t l_sb, l_sh;
   uint8_t heads_of[MA_MAX_HEADS];
   uint8_t kv_first[MA_MAX_HEADS + 1];
-  BwdTile tiles[kBwdTilesPerLaunch];
-  BwdKV kvs[kBwdTilesPerLaunch];
+  BwdQPart qparts[kBwdPerLaunch];
+  BwdKVPart kvparts[kBwdPerLaunch];
+  BwdEntry entries[kBwdPerLaunch];
 };
-int launch_bwd_preprocess(const BwdParams& p, int head_dim, void* stream);
-int launch_bwd_main(const BwdParams& p, int head_dim, int total_wgs, void* stream);
+
+// LSE*log2(e) (+inf for rows without an allowed key) and D = rowsum(dO*O) of a Q
+// partition, in the blocked layout the main kernels stage into LDS.
+struct BwdPreParams {
+  int32_t batch, hq, sq;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* lsed;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t l_sb, l_sh;
+};
+int launch_bwd_preprocess(const BwdPreParams& p, int head_dim, void* stream);
+int launch_bwd_dq(const BwdParams& p, int head_dim, int total_wgs, void* stream);
+int launch_bwd_dkv(const BwdParams& p, int head_dim, int total_wgs, void* stream);
 
 }  // namespace ma

@@ -165,3 +165,49 @@ def test_bwd_distributed_share():
     check_grad("dQ share", dq, dq_r)
     check_grad("dK", dk, dk_r)
     check_grad("dV", dv, dv_r)
+
+
+@pytest.mark.parametrize("nkv,mode", [(3, ma.MA_MASK_NONE), (10, ma.MA_MASK_CAUSAL)])
+def test_bwd_q_tile_meets_many_kv(nkv, mode):
+    # One Q partition against nkv KV partitions that all name the same dq buffer: dQ is the
+    # sum of the shares ([Mesh] section 3.5, dQ_i accumulated over the KV partitions); each KV
+    # partition gets its own dK/dV.  With 10 partitions the dQ work is split into pieces.
+    log(f"[bwd 1 q x {nkv} kv] mode={mode}")
+    sq, sk, hq, hkv, d = 130, 96, 8, 2, 128
+    wid = 1600 + nkv
+    causal = mode != ma.MA_MASK_NONE
+    q, qv = gen(wid, synthetic.T_Q, 0, (1, sq, hq, d))
+    do, dov = gen(wid, synthetic.T_DO, 0, (1, sq, hq, d))
+    scale = np.float32(1 / math.sqrt(d))
+    qp = Pos([(0, nkv * sk // 2, 1)])
+    qpos = positions(qp, sq) if causal else None
+    ks, kvals, kps = [], [], []
+    for j in range(nkv):
+        k, kv = gen(wid, synthetic.T_K, j, (1, sk, hkv, d))
+        v, vv = gen(wid, synthetic.T_V, j, (1, sk, hkv, d))
+        kp = Pos([(0, j * sk, 1)])
+        ks.append((k, v))
+        kvals.append((kv, vv))
+        kps.append(kp)
+    # the row's final O and LSE over all KV partitions (merge of the partials)
+    parts = [attn_tile(qv, kv, vv, scale, None, causal, qpos, positions(kp, sk) if causal else None)
+             for (kv, vv), kp in zip(kvals, kps)]
+    O, L = merge(parts)
+    o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+    dq = torch.full((1, sq, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    tiles, outs = [], []
+    for (k, v), kp in zip(ks, kps):
+        dk = torch.full((1, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+        dv = torch.full_like(dk, float("nan"))
+        tiles.append(BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv, qp, kp))
+        outs.append((dk, dv))
+    ma.mesh_attn_tile_bwd(tiles, float(scale), mode)
+    torch.cuda.synchronize()
+    dq_ref = None
+    for ((kv, vv), kp), (dk, dv) in zip(zip(kvals, kps), outs):
+        dq_r, dk_r, dv_r = attn_tile_bwd(qv, kv, vv, o_used, dov, l_used, scale, None, causal, qpos,
+                                         positions(kp, sk) if causal else None)
+        dq_ref = dq_r if dq_ref is None else dq_ref + dq_r
+        check_grad("dK", dk, dk_r)
+        check_grad("dV", dv, dv_r)
+    check_grad("dQ (sum of shares)", dq, dq_ref)
