@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle sample")
     ap.add_argument("--parts", default="fwd,merge,bwd", help="kernels in the step (all by default)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the timed steps, one plain device copy of this many MiB (outside the timed "
+                         "region): the reference launch for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -81,6 +84,90 @@ def cpu_baseline(rows, scale):
                       f"{len(os.sched_getaffinity(0))} host cores visible)"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tile_bwd_gqa_tile_8k.md")
+KERNEL_SOURCES = ["bwd.hip", "fwd_bf16.hip", "merge.hip", "api.hip", "ma_device.h", "ma_internal.h"]
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources the measured kernels are built from (changes invalidate stored counters)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "distributed_long_context_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per tile-backward launch from the committed counter summary, or None when the
+    summary is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("    ") and ":" in line:
+            k, v = line.strip().split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["tile_bwd_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_mib, command):
+    """Write the HBM-traffic summary of the tile backward from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the plain device copy of copy_mib MiB made by --calib-copy-mb."""
+    import csv
+    import collections
+
+    def per_kernel(path):
+        by_dispatch = collections.OrderedDict()
+        for r in csv.DictReader(open(path)):
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            by_dispatch[key] = by_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+        agg = collections.OrderedDict()
+        for (_, name), v in by_dispatch.items():
+            agg.setdefault(name, []).append(v)
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy_kib = copy_mib * 1024.0
+    copy_name = next(k for k in fetch if "copyBuffer" in k or "copy" in k.lower())
+    f_scale, w_scale = copy_kib / fetch[copy_name], copy_kib / write[copy_name]
+    short = lambda n: n.replace("ma::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    bwd = [k for k in fetch if any(t in k for t in ("bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkv_kernel"))]
+    total = sum(fetch[k] * f_scale + write[k] * w_scale for k in bwd) * 1024
+    lines = ["# HBM traffic of the tile backward, gqa-tile-8k (counters)", "",
+             "Workload: one non-causal tile, Q 8192 x KV 8192 tokens, 32/8 heads, head_dim 128, bf16.",
+             "Two rocprofv3 runs of the same command, one counter each (KiB per dispatch, averaged over",
+             "the dispatches of each kernel):", "",
+             "    " + command.replace("PMC", "FETCH_SIZE"), "    " + command.replace("PMC", "WRITE_SIZE"), "",
+             f"Calibration: the plain device copy of {copy_mib} MiB ({short(copy_name)}) reads FETCH_SIZE "
+             f"{fetch[copy_name]:.0f} KiB and WRITE_SIZE {write[copy_name]:.0f} KiB, so the factors are "
+             f"{f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+             "| Kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MiB read | scaled MiB written |",
+             "|---|---|---|---|---|"]
+    for k in fetch:
+        if k == copy_name or k not in write:
+            continue
+        lines.append(f"| {short(k)} | {fetch[k]:.0f} | {write[k]:.0f} | {fetch[k] * f_scale / 1024:.1f} | "
+                     f"{write[k] * w_scale / 1024:.1f} |")
+    lines += ["", "The tile backward entry point launches bwd_pre, bwd_dq and bwd_dkv once each; their sum is "
+              "the traffic per launch that bench.py reports while the kernel sources are unchanged:", "",
+              f"    tile_bwd_bytes_per_launch: {int(round(total))}",
+              f"    source_sha256: {kernel_source_hash()}", ""]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {TRAFFIC_FILE}: {total / 2**20:.1f} MiB per launch")
+
+
 def incoming_lse():
     """LSE of the incoming partial: ln(8192) + 0.5 + N(0,1), float32 (seeded)."""
     import numpy as np
@@ -90,6 +177,10 @@ def incoming_lse():
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        # bench.py --summarize-pmc FETCH_CSV WRITE_CSV COPY_MIB "COMMAND (with PMC for the counter)"
+        summarize_pmc(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5])
+        return
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share on one GPU; --gpus above 1 is not supported "
@@ -167,6 +258,15 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
     merge_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
     bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / len(evs)
@@ -194,6 +294,9 @@ def main():
     else:
         rl = {"bound": "mfma", "achieved": res_parts[dom]["TFLOP/s"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
               "frac": res_parts[dom]["frac_bf16_peak"], "traffic": None, "kernel": dom}
+        if dom == "tile_bwd":
+            rl["kernel"] = "tile_bwd (mesh_attn_tile_bwd: bwd_pre + bwd_dq + bwd_dkv)"
+            rl["traffic"] = stored_traffic()
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
