@@ -161,14 +161,19 @@ def mesh_attn_merge(o_in: Sequence, lse_in: Sequence, o_out, lse_out, stream=Non
         raise ValueError("need k >= 1 matching O and LSE partials")
     B, S, H, d = o_out.shape
     dt = _dtype_code(o_out)
-    for x in list(o_in) + [o_out]:
-        if tuple(x.shape) != (B, S, H, d) or _dtype_code(x) != dt or x.stride() != o_out.stride():
-            raise ValueError("all O tensors must share shape, dtype and strides")
-        _check_dev(x, "o")
-    for x in list(lse_in) + [lse_out]:
-        if tuple(x.shape) != (B, H, S) or x.dtype != _torch().float32 or x.stride() != lse_out.stride():
+    _check_dev(o_out, "o_out")
+    _check_dev(lse_out, "lse_out")
+    # one comparison per property and partial (the checks run on every call)
+    oshape, ostride, odtype, odev = o_out.shape, o_out.stride(), o_out.dtype, o_out.device
+    for x in o_in:
+        if x.shape != oshape or x.stride() != ostride or x.dtype != odtype or x.device != odev:
+            raise ValueError("all O tensors must share shape, dtype, strides and device")
+    lshape, lstride, f32 = lse_out.shape, lse_out.stride(), _torch().float32
+    if tuple(lshape) != (B, H, S) or lse_out.dtype != f32:
+        raise ValueError("all LSE tensors must be float32 [B, H, S] with equal strides")
+    for x in lse_in:
+        if x.shape != lshape or x.stride() != lstride or x.dtype != f32 or x.device != odev:
             raise ValueError("all LSE tensors must be float32 [B, H, S] with equal strides")
-        _check_dev(x, "lse")
     optr = (C.c_void_p * k)(*[x.data_ptr() for x in o_in])
     lptr = (C.c_void_p * k)(*[x.data_ptr() for x in lse_in])
     a = _abi.ma_merge_args()
