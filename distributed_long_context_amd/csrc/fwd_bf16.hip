@@ -38,6 +38,7 @@
 //    compare global positions element by element.
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 #include "ma_internal.h"
 #include "ma_device.h"
@@ -261,7 +262,19 @@ fwd_bf16_kernel(const FwdParams p) {
   // the half's PV MFMAs while the next half is masked and its row max taken.
   // A half past the last block reads a stale stage; half_max masks it to -inf
   // (no key of a block index >= nkb is allowed), so it never changes the state.
-  auto half_step = [&](int st, int kb2, f32x16& sc, int nkb_, int nst, int nkb2, f32x16& sn) {
+  // Without element masks (no position mask, key count a multiple of 64) the row
+  // max of the next half needs no branch, so the whole step is one straight-line
+  // region the scheduler can interleave; a half past the last block then only
+  // has its max forced to -inf.
+  auto half_max_plain = [&](bool valid, f32x16& s) {
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+    const float m = xhalf_max(mx) * c2;
+    mb2 = valid ? m : -INFINITY;
+  };
+
+  auto half_step = [&](auto may_mask, int st, int kb2, f32x16& sc, int nkb_, int nst, int nkb2, f32x16& sn) {
     const float mref = (m2 == -INFINITY) ? 0.0f : m2;
     bf16x8 pf[2];
 #pragma unroll
@@ -286,7 +299,8 @@ fwd_bf16_kernel(const FwdParams p) {
         oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[half], oacc[c], 0, 0, 0);
       }
     }
-    half_max(nkb_, nkb2, sn);
+    if constexpr (decltype(may_mask)::value) half_max(nkb_, nkb2, sn);
+    else half_max_plain(nkb_ < nkb, sn);
   };
 
   // ---- pipeline over the blocks with any allowed pair for the workgroup ----
@@ -294,46 +308,55 @@ fwd_bf16_kernel(const FwdParams p) {
   // position j+1 (the second half of position j), its loads have landed (j+2 may
   // still be in flight) and position j+3 is issued into the stage that the
   // previous block's steps finished reading.
-  int bj0 = next_block(0);
-  int bj1 = bj0 < nkb ? next_block(bj0 + 1) : nkb;
-  int bj2 = bj1 < nkb ? next_block(bj1 + 1) : nkb;
-  if (bj0 < nkb) issue(0, bj0);
-  if (bj1 < nkb) issue(1, bj1);
-  if (bj2 < nkb) issue(2, bj2);
-  f32x16 sA, sB;
-  // one full wait here also retires the query loads, so the compiler needs no
-  // vmcnt waits inside the loop
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  if (bj0 < nkb) {
-    __syncthreads();
-    s_half(0, 0, sA);
-    half_max(bj0, 0, sA);
-    maybe_rescale();
+  auto pipeline = [&](auto may_mask) {
+    int bj0 = next_block(0);
+    int bj1 = bj0 < nkb ? next_block(bj0 + 1) : nkb;
+    int bj2 = bj1 < nkb ? next_block(bj1 + 1) : nkb;
+    if (bj0 < nkb) issue(0, bj0);
+    if (bj1 < nkb) issue(1, bj1);
+    if (bj2 < nkb) issue(2, bj2);
+    f32x16 sA, sB;
+    // one full wait here also retires the query loads, so the compiler needs no
+    // vmcnt waits inside the loop
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (bj0 < nkb) {
+      __syncthreads();
+      s_half(0, 0, sA);
+      if constexpr (decltype(may_mask)::value) half_max(bj0, 0, sA);
+      else half_max_plain(true, sA);
+      maybe_rescale();
+    }
+#define MA_FWD_BLOCK(ST)                                                          \
+  {                                                                               \
+    /* first half: next scores are the second half of the same block */          \
+    half_step(may_mask, (ST), 0, sA, bj0, (ST), 1, sB);                           \
+    maybe_rescale();                                                              \
+    /* second half: next scores come from the next block (stage ST+1) */         \
+    const int bj3 = bj2 < nkb ? next_block(bj2 + 1) : nkb;                        \
+    wait_positions(bj2 < nkb ? 1 : 0);                                            \
+    __syncthreads();                                                              \
+    if (bj3 < nkb) issue(((ST) + 3) & 3, bj3);                                    \
+    half_step(may_mask, (ST), 1, sB, bj1, ((ST) + 1) & 3, 0, sA);                 \
+    maybe_rescale();                                                              \
+    bj0 = bj1;                                                                    \
+    bj1 = bj2;                                                                    \
+    bj2 = bj3;                                                                    \
+    if (bj0 >= nkb) break;                                                        \
   }
-#define MA_FWD_BLOCK(ST)                                                        \
-  {                                                                             \
-    /* first half: next scores are the second half of the same block */        \
-    half_step((ST), 0, sA, bj0, (ST), 1, sB);                                    \
-    maybe_rescale();                                                            \
-    /* second half: next scores come from the next block (stage ST+1) */       \
-    const int bj3 = bj2 < nkb ? next_block(bj2 + 1) : nkb;                      \
-    wait_positions(bj2 < nkb ? 1 : 0);                                          \
-    __syncthreads();                                                            \
-    if (bj3 < nkb) issue(((ST) + 3) & 3, bj3);                                  \
-    half_step((ST), 1, sB, bj1, ((ST) + 1) & 3, 0, sA);                          \
-    maybe_rescale();                                                            \
-    bj0 = bj1;                                                                  \
-    bj1 = bj2;                                                                  \
-    bj2 = bj3;                                                                  \
-    if (bj0 >= nkb) break;                                                      \
-  }
-  while (bj0 < nkb) {
-    MA_FWD_BLOCK(0)
-    MA_FWD_BLOCK(1)
-    MA_FWD_BLOCK(2)
-    MA_FWD_BLOCK(3)
-  }
+    while (bj0 < nkb) {
+      MA_FWD_BLOCK(0)
+      MA_FWD_BLOCK(1)
+      MA_FWD_BLOCK(2)
+      MA_FWD_BLOCK(3)
+    }
 #undef MA_FWD_BLOCK
+  };
+  if constexpr (MASKED) {
+    pipeline(std::true_type{});
+  } else {
+    if (T.sk % kBN != 0) pipeline(std::true_type{});  // ragged last block needs the key mask
+    else pipeline(std::false_type{});
+  }
 
   if (!active) return;
   // ---- epilogue: normalise, store O (bf16) and LSE (fp32, natural log) ----
