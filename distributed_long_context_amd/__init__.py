@@ -16,7 +16,7 @@ from ._abi import (MA_OK, MA_ERR_INVALID, MA_ERR_UNSUPPORTED, MA_ERR_LAUNCH, MA_
                    MA_MAX_MERGE, MeshAttnError, lib)
 
 __all__ = [
-    "mesh_attn_tile_fwd", "mesh_attn_merge", "mesh_attn_tile_bwd", "mesh_attn_tile_bwd_workspace_size",
+    "mesh_attn_tile_fwd", "mesh_attn_merge", "mesh_attn_reduce_add", "mesh_attn_tile_bwd", "mesh_attn_tile_bwd_workspace_size",
     "mesh_attn_map_mesh_tile", "mesh_attn_map_groups", "mesh_attn_map_zigzag", "mesh_attn_pos_contiguous",
     "mesh_attn_pos_zigzag", "mesh_attn_pos_striped", "mesh_attn_pos_at", "mesh_attn_classify",
     "mesh_attn_count_allowed", "mesh_attn_build_worklist", "mesh_attn_version", "Pos", "Tile", "BwdTile",
@@ -106,8 +106,9 @@ class Tile:
 
 
 def mesh_attn_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
-                       stream=None) -> None:
-    """Partial (O, LSE) of every tile, enqueued on `stream` (default: current stream)."""
+                       stream=None, accumulate: bool = False) -> None:
+    """Partial (O, LSE) of every tile, enqueued on `stream` (default: current stream).
+    With accumulate=True each tile's result is folded into the (O, LSE) its buffers hold."""
     tiles = list(tiles)
     if not tiles:
         return
@@ -141,7 +142,7 @@ def mesh_attn_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_
         c.q_pos, c.k_pos = _pos_c(t.q_pos), _pos_c(t.k_pos)
     a = _abi.ma_tile_fwd_args()
     a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.mask_mode = dt, B, Hq, Hkv, d, int(mask_mode)
-    a.scale, a.ntiles = float(scale), len(tiles)
+    a.scale, a.ntiles, a.accumulate = float(scale), len(tiles), 1 if accumulate else 0
     hm_keep, a.head_map = _head_map_c(head_map, Hq)
     a.tiles = C.cast(arr, C.POINTER(_abi.ma_tile))
     a.q_stride[:] = _bshd_strides(t0.q, "q")
@@ -183,6 +184,29 @@ def mesh_attn_merge(o_in: Sequence, lse_in: Sequence, o_out, lse_out, stream=Non
     a.o_stride[:] = _bshd_strides(o_out, "o_out")
     a.lse_stride[:] = (lse_out.stride(0), lse_out.stride(1))
     _abi.check(lib().mesh_attn_merge(C.byref(a), _stream_ptr(stream)), "mesh_attn_merge")
+
+
+# ------------------------------------------------------------- add-reduce --
+
+def mesh_attn_reduce_add(inputs: Sequence, out, stream=None) -> None:
+    """out = sum of the k float32 tensors in `inputs` (same shape, contiguous), added in list order."""
+    k = len(inputs)
+    if k < 1:
+        raise ValueError("need at least one input")
+    torch = _torch()
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor")
+    _check_dev(out, "out")
+    for i, x in enumerate(inputs):
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.shape != out.shape:
+            raise ValueError(f"input {i}: must be contiguous float32 of out's shape")
+        _check_dev(x, f"input {i}")
+    ptrs = (C.c_void_p * k)(*[x.data_ptr() for x in inputs])
+    a = _abi.ma_reduce_args()
+    a.k, a.n = k, out.numel()
+    a.in_ = C.cast(ptrs, C.POINTER(C.c_void_p))
+    a.out = out.data_ptr()
+    _abi.check(lib().mesh_attn_reduce_add(C.byref(a), _stream_ptr(stream)), "mesh_attn_reduce_add")
 
 
 # --------------------------------------------------------------- backward --

@@ -35,7 +35,8 @@ class ma_tile(C.Structure):
 
 class ma_tile_fwd_args(C.Structure):
     _fields_ = [("dtype", I32), ("batch", I32), ("hq", I32), ("hkv", I32), ("head_dim", I32), ("mask_mode", I32),
-                ("scale", F32), ("ntiles", I32), ("head_map", C.POINTER(I32)), ("tiles", C.POINTER(ma_tile)),
+                ("scale", F32), ("ntiles", I32), ("accumulate", I32), ("reserved", I32),
+                ("head_map", C.POINTER(I32)), ("tiles", C.POINTER(ma_tile)),
                 ("q_stride", I64 * 3), ("k_stride", I64 * 3), ("v_stride", I64 * 3), ("o_stride", I64 * 3),
                 ("lse_stride", I64 * 2)]
 
@@ -44,6 +45,10 @@ class ma_merge_args(C.Structure):
     _fields_ = [("dtype", I32), ("batch", I32), ("seqlen", I32), ("heads", I32), ("head_dim", I32), ("k", I32),
                 ("o_in", C.POINTER(VP)), ("lse_in", C.POINTER(VP)), ("o_out", VP), ("lse_out", VP),
                 ("o_stride", I64 * 3), ("lse_stride", I64 * 2)]
+
+
+class ma_reduce_args(C.Structure):
+    _fields_ = [("k", I32), ("reserved", I32), ("n", I64), ("in_", C.POINTER(VP)), ("out", VP)]
 
 
 class ma_bwd_tile(C.Structure):
@@ -63,6 +68,7 @@ class ma_tile_bwd_args(C.Structure):
 SIGNATURES = {
     "mesh_attn_tile_fwd": (I32, [C.POINTER(ma_tile_fwd_args), VP]),
     "mesh_attn_merge": (I32, [C.POINTER(ma_merge_args), VP]),
+    "mesh_attn_reduce_add": (I32, [C.POINTER(ma_reduce_args), VP]),
     "mesh_attn_tile_bwd_workspace_size": (C.c_size_t, [C.POINTER(ma_tile_bwd_args)]),
     "mesh_attn_tile_bwd": (I32, [C.POINTER(ma_tile_bwd_args), VP, C.c_size_t, VP]),
     "mesh_attn_map_mesh_tile": (I32, [I32, I32, I32, I32, I32, C.POINTER(I32), C.POINTER(I32)]),

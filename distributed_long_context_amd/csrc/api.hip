@@ -116,6 +116,7 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   if (rc) return rc;
   if (!a->head_map && a->hq % a->hkv) return set_error(MA_ERR_INVALID, "hq must be a multiple of hkv when head_map is NULL");
   if (a->ntiles < 0 || a->ntiles > MA_MAX_TILES) return set_error(MA_ERR_INVALID, "ntiles out of range");
+  if (a->accumulate != 0 && a->accumulate != 1) return set_error(MA_ERR_INVALID, "accumulate must be 0 or 1");
   if (a->ntiles == 0) return MA_OK;
   if (!a->tiles) return set_error(MA_ERR_INVALID, "null tile list");
   if (!strides_ok(a->q_stride, 3, a->dtype) || !strides_ok(a->k_stride, 3, a->dtype) ||
@@ -134,6 +135,7 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   p.hq = a->hq;
   p.hkv = a->hkv;
   p.mask = a->mask_mode != MA_MASK_NONE;
+  p.accumulate = a->accumulate;
   p.scale = a->scale;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   p.q_sb = a->q_stride[0]; p.q_ss = a->q_stride[1]; p.q_sh = a->q_stride[2];
@@ -166,8 +168,16 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   };
   for (int i = 0; i < a->ntiles; ++i) {
     const ma_tile& t = a->tiles[i];
+    // a tile naming the output of one already in this launch waits for it (list order)
+    for (int j = 0; j < n; ++j)
+      if (p.tiles[j].o == t.o || p.tiles[j].lse == t.lse) {
+        rc = flush();
+        if (rc) return rc;
+        break;
+      }
     if (a->mask_mode != MA_MASK_NONE &&
         mesh_attn_classify(&t.q_pos, t.sq, &t.k_pos, t.sk, a->mask_mode) == MA_TILE_EMPTY) {
+      if (a->accumulate) continue;  // nothing to fold in
       int e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss,
                                 p.o_sh, p.l_sb, p.l_sh, stream);
       rc = check_hip(e, "fill launch");
@@ -234,6 +244,26 @@ int mesh_attn_merge(const ma_merge_args* a, void* stream) {
   p.o_out = a->o_out;
   p.lse_out = a->lse_out;
   return check_hip(launch_merge(p, a->dtype, a->head_dim, stream), "merge launch");
+}
+
+int mesh_attn_reduce_add(const ma_reduce_args* a, void* stream) {
+  if (!a) return set_error(MA_ERR_INVALID, "null args");
+  if (a->k < 1 || a->k > MA_MAX_MERGE) return set_error(MA_ERR_INVALID, "k must be in 1..MA_MAX_MERGE");
+  if (a->n < 0) return set_error(MA_ERR_INVALID, "n must be >= 0");
+  if (a->n == 0) return MA_OK;
+  if (!a->in || !a->out) return set_error(MA_ERR_INVALID, "null pointer");
+  if (!aligned16(a->out)) return set_error(MA_ERR_INVALID, "out must be 16-byte aligned");
+  ReduceParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int r = 0; r < a->k; ++r) {
+    if (!a->in[r]) return set_error(MA_ERR_INVALID, "null input pointer");
+    if (!aligned16(a->in[r])) return set_error(MA_ERR_INVALID, "inputs must be 16-byte aligned");
+    p.in[r] = a->in[r];
+  }
+  p.k = a->k;
+  p.n = a->n;
+  p.out = a->out;
+  return check_hip(launch_reduce_add(p, stream), "reduce_add launch");
 }
 
 }  // extern "C"

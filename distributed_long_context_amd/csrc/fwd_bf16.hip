@@ -359,25 +359,48 @@ fwd_bf16_kernel(const FwdParams p) {
   }
 
   if (!active) return;
-  // ---- epilogue: normalise, store O (bf16) and LSE (fp32, natural log) ----
+  // ---- epilogue: normalise, store O (bf16) and LSE (fp32, natural log), or fold them
+  // into the pair the buffers hold ----
   __bf16* Og = (__bf16*)T.o + (int64_t)b * p.o_sb + (int64_t)my_head * p.o_sh;
   float* Lg = T.lse + (int64_t)b * p.l_sb + (int64_t)my_head * p.l_sh;
   const float ltot = xhalf_sum(lsum);
   const int row = q0 + l32;
+  if (row >= T.sq) return;
   const bool has = ltot > 0.0f;
-  const float inv = has ? 1.0f / ltot : 0.0f;
-  if (row < T.sq) {
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * inv;
-        *(bf16x4*)(Og + (int64_t)row * p.o_ss + c * 32 + g * 8 + hl * 4) = pack_bf16x4(v4);
-      }
-    if (hl == 0) Lg[row] = has ? (m2 + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f : -INFINITY;
+  float lse = has ? (m2 + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f : -INFINITY;
+  float wn = has ? 1.0f / ltot : 0.0f;  // weight of this tile's unnormalised sums
+  float wo = 0.0f;                      // weight of the output already held (accumulate)
+  __bf16* orow = Og + (int64_t)row * p.o_ss;
+  if (p.accumulate) {
+    // fold into (O_old, lse_old): L = ln(e^lse_old + e^lse), O = e^(lse_old-L) O_old + e^(lse-L) O
+    const float lo = Lg[row];
+    const float mx = fmaxf(lo, lse);
+    if (mx == -INFINITY) {
+      wn = 0.0f;
+    } else {
+      const float eo = __expf(lo - mx), en = __expf(lse - mx);
+      const float sum = eo + en;
+      wo = eo / sum;
+      wn *= en / sum;
+      lse = mx + __logf(sum);
+    }
   }
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __bf16* dst = orow + c * 32 + g * 8 + hl * 4;
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * wn;
+      if (p.accumulate) {
+        const bf16x4 old = *(const bf16x4*)dst;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = __builtin_fmaf(wo, (float)old[i], v4[i]);
+      }
+      *(bf16x4*)dst = pack_bf16x4(v4);
+    }
+  if (hl == 0) Lg[row] = lse;
 }
 
 }  // namespace

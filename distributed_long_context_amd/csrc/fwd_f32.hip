@@ -117,12 +117,38 @@ __global__ void __launch_bounds__(kRows) fwd_f32_kernel(const FwdParams p) {
   }
   if (!ok) return;
   const bool has = l > 0.f;
-  const float inv = has ? 1.0f / l : 0.f;
+  float lse = has ? (m2 + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+  float wn = has ? 1.0f / l : 0.f;  // weight of this tile's unnormalised sums
+  float wo = 0.f;                   // weight of the output already held (accumulate)
   float* Og = (float*)T.o + (int64_t)b * p.o_sb + (int64_t)head * p.o_sh + (int64_t)row * p.o_ss;
+  float* Lp = T.lse + (int64_t)b * p.l_sb + (int64_t)head * p.l_sh + row;
+  if (p.accumulate) {
+    // fold into (O_old, lse_old): L = ln(e^lse_old + e^lse), O = e^(lse_old-L) O_old + e^(lse-L) O
+    const float lo = *Lp;
+    const float mx = fmaxf(lo, lse);
+    if (mx == -INFINITY) {
+      wn = 0.f;
+    } else {
+      const float eo = __expf(lo - mx), en = __expf(lse - mx);
+      const float sum = eo + en;
+      wo = eo / sum;
+      wn *= en / sum;
+      lse = mx + __logf(sum);
+    }
+  }
 #pragma unroll
-  for (int c = 0; c < D; c += 4) *(float4*)(Og + c) = make_float4(o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv);
-  T.lse[(int64_t)b * p.l_sb + (int64_t)head * p.l_sh + row] =
-      has ? (m2 + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+  for (int c = 0; c < D; c += 4) {
+    float4 r = make_float4(o[c] * wn, o[c + 1] * wn, o[c + 2] * wn, o[c + 3] * wn);
+    if (p.accumulate) {
+      const float4 old = *(const float4*)(Og + c);
+      r.x = __builtin_fmaf(wo, old.x, r.x);
+      r.y = __builtin_fmaf(wo, old.y, r.y);
+      r.z = __builtin_fmaf(wo, old.z, r.z);
+      r.w = __builtin_fmaf(wo, old.w, r.w);
+    }
+    *(float4*)(Og + c) = r;
+  }
+  *Lp = lse;
 }
 
 // O = 0 and LSE = -inf for a whole tile (the result of a tile with no allowed pair).

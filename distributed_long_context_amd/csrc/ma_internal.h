@@ -43,6 +43,7 @@ struct FwdParams {
   int32_t batch, hq, hkv;
   int32_t mask;           // 0 none, 1 causal on positions
   int32_t gmax;           // largest number of query heads sharing one KV head
+  int32_t accumulate;     // fold into the (O, LSE) held by the output buffers
   float scale;            // softmax scale
   float scale_log2;       // scale * log2(e)
   int64_t q_sb, q_ss, q_sh;
@@ -73,6 +74,15 @@ struct MergeParams {
   const float* lse_in[MA_MAX_MERGE];
 };
 int launch_merge(const MergeParams& p, int dtype, int head_dim, void* stream);
+
+// ---- add-reduce ----
+struct ReduceParams {
+  int32_t k;
+  int64_t n;
+  float* out;
+  const float* in[MA_MAX_MERGE];
+};
+int launch_reduce_add(const ReduceParams& p, void* stream);
 
 // ---- backward ----
 // The backward runs per (Q partition, KV partition) pair ([Mesh] section 3.5).

@@ -110,9 +110,21 @@ typedef struct {
  *   LSE[t] = ln sum_{u allowed} exp(s[t,u])
  *   O[t]   = sum_{u allowed} exp(s[t,u] - LSE[t]) v[u]
  * Accumulation is fp32; bf16 O is rounded to nearest even at the store.
- * Every tile writes its own (O, LSE) over its whole [sq] range.  A tile that is
- * EMPTY under the mask is not computed: its O is filled with 0 and its LSE with
- * -inf (callers normally leave EMPTY tiles out; see mesh_attn_classify).
+ * accumulate = 0: every tile writes its own (O, LSE) over its whole [sq] range.
+ * A tile that is EMPTY under the mask is not computed: its O is filled with 0
+ * and its LSE with -inf (callers normally leave EMPTY tiles out; see
+ * mesh_attn_classify).
+ * accumulate = 1: the tile's result is folded into the (O, LSE) pair already
+ * held by its o and lse buffers, the running update of [Mesh] section 2.2 and
+ * of [CHARM+] appendix A, Algorithm 2 (CompAttention updates out in place):
+ *   L = ln(exp(lse_old) + exp(lse_tile));
+ *   O = exp(lse_old - L) O_old + exp(lse_tile - L) O_tile;
+ * with (0, -inf) when both are -inf.  The buffers must hold a valid pair (for
+ * example the first tile's output, or O = 0 and LSE = -inf); EMPTY tiles leave
+ * them unchanged.  The arithmetic is fp32 and O is rounded once, at the store.
+ * In either mode, tiles of one call that name the same o are applied in list
+ * order (each waits for the one before), so a ring of KV partitions can be
+ * handed over as one call.
  * --------------------------------------------------------------------------- */
 typedef struct {
   const void* q;  /* device, [B, sq, Hq, d], dtype */
@@ -135,6 +147,8 @@ typedef struct {
   int32_t mask_mode;  /* MA_MASK_* */
   float scale;        /* softmax scale, e.g. 1/sqrt(d) ([Mesh] section 2.1) */
   int32_t ntiles;     /* 0..MA_MAX_TILES (0 is a no-op) */
+  int32_t accumulate; /* 0: write (O, LSE); 1: fold into the (O, LSE) held by the buffers */
+  int32_t reserved;   /* 0 */
   const int32_t* head_map;  /* host, hq entries in [0, hkv), or NULL */
   const ma_tile* tiles;     /* host array of ntiles */
   int64_t q_stride[3];      /* b, s, h (elements) - shared by all tiles */
@@ -172,6 +186,25 @@ typedef struct {
 } ma_merge_args;
 
 int mesh_attn_merge(const ma_merge_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Add-reduce of partial gradients.  [Mesh] section 3.5: the partial dQ_i and
+ * dKV_j of the per-pair backward calls are summed across the GPUs that hold
+ * them (a reduce-scatter with addition); this is the per-GPU summation step
+ * of that reduce: out[e] = sum_r in_r[e] for e < n, in fp32, added in the
+ * order r = 0, 1, ..., k-1 (the same bits on every call).  Every pointer is
+ * 16-byte aligned; out may equal in[0] (in place), other overlaps are
+ * undefined.  n = 0 is a no-op.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+  int32_t k;               /* 1..MA_MAX_MERGE inputs */
+  int32_t reserved;        /* 0 */
+  int64_t n;               /* float32 elements per input, >= 0 */
+  const float* const* in;  /* host array of k device pointers */
+  float* out;              /* device, n floats */
+} ma_reduce_args;
+
+int mesh_attn_reduce_add(const ma_reduce_args* args, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Tile backward.  [Mesh] section 3.5: the backward kernel runs per pair with

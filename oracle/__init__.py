@@ -17,8 +17,9 @@ Sources (cited by title and section; the pages are the authority):
 
 Modules:
 
-* ``attention`` - the forward tile (partial O and LSE), the LSE merge and the
-  tile backward, each written as the plain definition in float64.
+* ``attention`` - the forward tile (partial O and LSE), the LSE merge, the
+  tile backward and the add-reduce of partial gradients, each written as the
+  plain definition in float64.
 * ``layout``   - token positions (contiguous, zigzag, striped), the assignment
   matrix with basic tiling and KV partition rotation, footprints, groups, and
   tile classification by brute-force enumeration.
@@ -28,5 +29,5 @@ itself (brute force, closed forms, invariants, values printed on the pages).
 No function here is "parity unpinned".
 """
 
-from .attention import attn_tile, merge, attn_tile_bwd, attn_bwd_multi  # noqa: F401
+from .attention import attn_tile, merge, attn_tile_bwd, attn_bwd_multi, reduce_add  # noqa: F401
 from . import layout  # noqa: F401

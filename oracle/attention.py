@@ -128,6 +128,19 @@ def merge(parts):
     return O, lse
 
 
+def reduce_add(parts):
+    """Element-wise sum of partial gradient buffers, in float64.
+
+    [Mesh] §3.5: the per-pair backward leaves partial dQ_i (one per KV partition
+    met) and partial dKV_j (one per Q partition met) that are combined by a
+    reduce-scatter whose operation is addition.  parts: list of equal-shape arrays.
+    """
+    out = np.zeros(np.shape(parts[0]), dtype=np.float64)
+    for p in parts:
+        out = out + _f64(p)
+    return out
+
+
 def attn_tile_bwd(q, k, v, o, do, lse, scale, head_map=None, causal=False, q_pos=None, k_pos=None):
     """Gradients of one pair's attention given the stored O, LSE and dO.
 

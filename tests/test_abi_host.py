@@ -49,6 +49,7 @@ def _fwd_args(**kw):
     (dict(scale=float("nan")), _abi.MA_ERR_INVALID),
     (dict(ntiles=1), _abi.MA_ERR_INVALID),  # null tile list
     (dict(ntiles=-1), _abi.MA_ERR_INVALID),
+    (dict(accumulate=2), _abi.MA_ERR_INVALID),
 ])
 def test_tile_fwd_rejects_bad_arguments(kw, code):
     a = _fwd_args(**kw)

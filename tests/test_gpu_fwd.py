@@ -227,3 +227,69 @@ def test_merge_in_place():
     torch.cuda.synchronize()
     check_close("O", host_f64(Os[0]), Oref, BF16_O_TOL, normalised_also=False)
     check_close("LSE", host_f64(Ls[0]), Lref, BF16_LSE_TOL)
+
+
+def _ring_case(wid, P, n, hq, hkv, d, dtype):
+    """One query partition (positions 3P..4P) and n KV partitions at positions jP..(j+1)P."""
+    q, qv = gen(wid, synthetic.T_Q, 3, (1, P, hq, d), dtype)
+    ks = [gen(wid, synthetic.T_K, j, (1, P, hkv, d), dtype) for j in range(n)]
+    vs = [gen(wid, synthetic.T_V, j, (1, P, hkv, d), dtype) for j in range(n)]
+    return q, qv, ks, vs
+
+
+@pytest.mark.parametrize("dtype,d,mode,one_call", [("bf16", 128, ma.MA_MASK_CAUSAL, False),
+                                                    ("bf16", 64, ma.MA_MASK_CAUSAL, True),
+                                                    ("bf16", 128, ma.MA_MASK_NONE, True),
+                                                    ("f32", 64, ma.MA_MASK_CAUSAL, False)])
+def test_fwd_accumulate_ring_equals_unsplit(dtype, d, mode, one_call):
+    # ring order 3, 4, 5, 0, 1, 2 around a query partition at positions [3P, 4P): under the causal
+    # mask tile 3 is PARTIAL (the diagonal), 4 and 5 are EMPTY (no-ops when accumulating) and 0-2 FULL.
+    P, n, hq, hkv = 200, 6, 8, 2
+    log(f"[fwd accumulate ring] dtype={dtype} d={d} mode={mode} one_call={one_call}")
+    q, qv, ks, vs = _ring_case(900 + d, P, n, hq, hkv, d, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o = torch.full((1, P, hq, d), float("nan"), dtype=tdt, device=DEV)
+    lse = torch.full((1, hq, P), float("nan"), dtype=torch.float32, device=DEV)
+    qp = Pos([(0, 3 * P, 1)])
+    order = [3, 4, 5, 0, 1, 2]
+    tiles = [Tile(q, ks[j][0], vs[j][0], o, lse, qp, Pos([(0, j * P, 1)])) for j in order]
+    scale = 1.0 / math.sqrt(d)
+    if one_call:
+        o.zero_()
+        lse.fill_(float("-inf"))
+        ma.mesh_attn_tile_fwd(tiles, scale, mode, accumulate=True)
+    else:
+        ma.mesh_attn_tile_fwd(tiles[:1], scale, mode)
+        for t in tiles[1:]:
+            ma.mesh_attn_tile_fwd([t], scale, mode, accumulate=True)
+    torch.cuda.synchronize()
+    kall = np.concatenate([ks[j][1] for j in range(n)], axis=1)
+    vall = np.concatenate([vs[j][1] for j in range(n)], axis=1)
+    causal = mode != ma.MA_MASK_NONE
+    Oref, Lref = attn_tile(qv, kall, vall, np.float32(scale), None, causal,
+                           positions(qp, P) if causal else None, np.arange(n * P, dtype=np.int64) if causal else None)
+    tol_o, tol_l = (BF16_O_TOL, BF16_LSE_TOL) if dtype == "bf16" else (F32_TOL, F32_TOL)
+    check_close("O", host_f64(o), Oref, tol_o, normalised_also=False)
+    check_close("LSE", host_f64(lse), Lref, tol_l)
+
+
+def test_fwd_accumulate_into_incoming_partial():
+    # the buffers start with a seeded incoming partial (with rows at -inf); the result must be the
+    # oracle merge of that partial with the tile's own attention
+    B, P, hq, hkv, d = 1, 150, 4, 1, 128
+    log("[fwd accumulate incoming]")
+    (q, k, v, o, lse), (qv, kv, vv) = make_case(950, P, 300, hq, hkv, d)
+    o_in, ov = gen(950, synthetic.T_O_IN, 0, (B, P, hq, d))
+    lv = (synthetic.normal_f32(950, synthetic.T_LSE_IN, 0, (B, hq, P)) + 6).astype(np.float32)
+    lv[0, 1, :20] = -np.inf
+    ov[0, :20, 1] = 0.0
+    o_in[0, :20, 1] = 0
+    o.copy_(o_in)
+    lse.copy_(torch.from_numpy(lv))
+    qp, kp = Pos([(0, 100, 1)]), Pos([(0, 0, 1)])  # causal: query rows 0..149 see keys up to 100+t
+    ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, qp, kp)], 0.08, ma.MA_MASK_CAUSAL, accumulate=True)
+    torch.cuda.synchronize()
+    Ot, Lt = attn_tile(qv, kv, vv, np.float32(0.08), None, True, positions(qp, P), positions(kp, 300))
+    Oref, Lref = merge([(ov, lv.astype(np.float64)), (Ot, Lt)])
+    check_close("O", host_f64(o), Oref, BF16_O_TOL, normalised_also=False)
+    check_close("LSE", host_f64(lse), Lref, BF16_LSE_TOL)

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from oracle import attn_tile, attn_tile_bwd, attn_bwd_multi, merge
+from oracle import attn_tile, attn_tile_bwd, attn_bwd_multi, merge, reduce_add
 from oracle import layout
 
 RNG = np.random.default_rng(99)
@@ -112,3 +112,25 @@ def test_fully_masked_rows_have_zero_gradient():
     assert np.isinf(L[0, 0, :2]).all()
     dq, dk, dv = attn_tile_bwd(q, k, v, O, do, L, 1.0, None, True, qp, kp)
     assert np.all(dq[0, :2] == 0) and np.isfinite(dk).all() and np.isfinite(dv).all()
+
+
+def test_reduce_add_is_exact_on_integers():
+    # small integers are exact in float64, so the sum must equal Python's integer sum
+    parts = [np.arange(12).reshape(3, 4) * (r + 1) - 7 * r for r in range(5)]
+    want = [[sum(int(p[i, j]) for p in parts) for j in range(4)] for i in range(3)]
+    assert np.array_equal(reduce_add(parts), np.array(want, dtype=np.float64))
+    assert np.array_equal(reduce_add(parts[:1]), parts[0].astype(np.float64))
+
+
+def test_reduce_add_of_kv_partials_gives_unsplit_dq():
+    # [Mesh] section 3.5: partial dQ of each (Q_i, KV_j) pair, added, is the gradient of the whole row
+    Sq, Sk, n = 9, 12, 4
+    q = RNG.standard_normal((1, Sq, 2, 3)); k = RNG.standard_normal((1, Sk, 1, 3)); v = RNG.standard_normal((1, Sk, 1, 3))
+    do = RNG.standard_normal((1, Sq, 2, 3))
+    O, L = attn_tile(q, k, v, 0.7)
+    dq, _, _ = attn_tile_bwd(q, k, v, O, do, L, 0.7)
+    b = Sk // n
+    parts = [attn_tile_bwd(q, k[:, j*b:(j+1)*b], v[:, j*b:(j+1)*b], O, do, L, 0.7)[0] for j in range(n)]
+    assert np.max(np.abs(reduce_add(parts) - dq)) < 1e-13
+    # dropping one partial must be visible
+    assert np.max(np.abs(reduce_add(parts[1:]) - dq)) > 1e-3
