@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle sample")
     ap.add_argument("--parts", default="fwd,merge,bwd", help="kernels in the step (all by default)")
+    ap.add_argument("--workloads", default="zigzag,mesh,bwd4",
+                    help="the other workloads timed after the step (comma list; 'none' for none): "
+                         "zigzag = causal zigzag share of S=131072, mesh = Mesh 8x8 tile of S=1048576, "
+                         "bwd4 = backward of 4 Q partitions x one KV partition of 8192")
+    ap.add_argument("--workload-reps", type=int, default=2, help="timed repetitions per workload entry")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB (outside the timed "
                          "region): the reference launch for scaling HBM byte counters")
@@ -174,6 +179,180 @@ def incoming_lse():
     import synthetic
     mu = math.log(SK) + 0.5
     return (synthetic.normal_f32(WORKLOAD_ID, synthetic.T_LSE_IN, 0, (1, HQ, SQ)) + np.float32(mu)).astype(np.float32)
+
+
+def _timed(fn, reps, warmup=1):
+    """Mean milliseconds of fn() over `reps` runs after `warmup`, from events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return sum(ts) / len(ts)
+
+
+def _tf(flop, ms):
+    t = flop / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(t, 1), "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4), "flop": flop}
+
+
+def _gb(nbytes, ms):
+    g = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(g, 1), "frac_hbm_peak": round(g / PEAK_HBM_GBPS, 4), "bytes": nbytes}
+
+
+def measure_workloads(names, reps):
+    """Times the other workloads of the hot path on the device, inputs resident in HBM.
+
+    Inputs are N(0,1) drawn on the device from a seeded generator (the same distributions as the parity
+    tests' host-drawn inputs, a different stream of numbers); O and LSE given to the backward have a real
+    forward's magnitudes.  Algorithmic work counts allowed pairs only (4*d*Hq forward, 10*d*Hq backward)
+    and merge/reduce bytes as each input read once plus each output written once."""
+    import torch
+    import distributed_long_context_amd as ma
+    from distributed_long_context_amd import BwdTile, Tile
+
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    scale = float(1.0 / math.sqrt(D))
+
+    def randn(shape, dtype=torch.bfloat16, mul=1.0, add=0.0):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * mul + add).to(dtype)
+
+    def out(sq):
+        return (torch.empty((1, sq, HQ, D), dtype=torch.bfloat16, device=dev),
+                torch.empty((1, HQ, sq), dtype=torch.float32, device=dev))
+
+    res = {}
+    if "zigzag" in names:
+        N, r, C = 16, 5, 4096
+        qchunks = ma.mesh_attn_map_zigzag(N, r)
+        nkv = max(qchunks) + 1
+        Q = {c: randn((1, C, HQ, D)) for c in qchunks}
+        kg = randn((1, nkv * C, HKV, D))
+        vg = randn((1, nkv * C, HKV, D))
+        K = [kg[:, j * C:(j + 1) * C] for j in range(nkv)]
+        V = [vg[:, j * C:(j + 1) * C] for j in range(nkv)]
+        qpos = [ma.mesh_attn_pos_contiguous(c * C) for c in qchunks]
+        kpos = [ma.mesh_attn_pos_contiguous(j * C) for j in range(nkv)]
+        wl = ma.mesh_attn_build_worklist(qpos, [C, C], kpos, [C] * nkv, ma.MA_MASK_CAUSAL)
+        pairs = sum(ma.mesh_attn_count_allowed(qpos[i], C, kpos[j], C, ma.MA_MASK_CAUSAL) for i, j, _ in wl)
+        tiles = [Tile(Q[qchunks[i]], K[j], V[j], *out(C), qpos[i], kpos[j]) for i, j, _ in wl]
+        groups = [[t for t, (ii, _, _) in zip(tiles, wl) if ii == i] for i in range(2)]
+        merged = [out(C) for _ in qchunks]
+        fused = [out(C) for _ in qchunks]
+        ftiles = [Tile(Q[c], kg[:, :(c + 1) * C], vg[:, :(c + 1) * C], *fused[i], qpos[i], ma.mesh_attn_pos_contiguous(0))
+                  for i, c in enumerate(qchunks)]
+        part_bytes = C * HQ * D * 2 + HQ * C * 4
+        merge_bytes = sum((len(g) + 1) * part_bytes for g in groups)
+
+        def merges():
+            for g, m in zip(groups, merged):
+                ma.mesh_attn_merge([t.o for t in g], [t.lse for t in g], m[0], m[1])
+
+        w = {"tiles": len(wl), "allowed_pairs_per_head": pairs}
+        w["fwd_tiles"] = _tf(4.0 * D * HQ * pairs, _timed(lambda: ma.mesh_attn_tile_fwd(tiles, scale, ma.MA_MASK_CAUSAL), reps))
+        w["merge_6_and_27"] = _gb(merge_bytes, _timed(merges, reps))
+        w["fwd_fused_gathered_kv"] = _tf(4.0 * D * HQ * pairs,
+                                         _timed(lambda: ma.mesh_attn_tile_fwd(ftiles, scale, ma.MA_MASK_CAUSAL), reps))
+        # backward of the share: dQ of both chunks, partial dK/dV of KV chunks 0..26
+        dO = {c: randn((1, C, HQ, D)) for c in qchunks}
+        O = {c: randn((1, C, HQ, D), mul=0.02) for c in qchunks}
+        L = {c: randn((1, HQ, C), torch.float32, 0.3, math.log(c * C + C / 2) + 0.5) for c in qchunks}
+        dq = {c: torch.empty((1, C, HQ, D), dtype=torch.float32, device=dev) for c in qchunks}
+        dk = [torch.empty((1, C, HKV, D), dtype=torch.float32, device=dev) for _ in range(nkv)]
+        dv = [torch.empty_like(x) for x in dk]
+        btiles = [BwdTile(Q[qchunks[i]], K[j], V[j], O[qchunks[i]], dO[qchunks[i]], L[qchunks[i]], dq[qchunks[i]],
+                          dk[j], dv[j], qpos[i], kpos[j]) for i, j, _ in wl]
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        w["bwd_tiles"] = _tf(10.0 * D * HQ * pairs,
+                             _timed(lambda: ma.mesh_attn_tile_bwd(btiles, scale, ma.MA_MASK_CAUSAL, workspace=ws), reps))
+        res["zigzag-causal-128k-r5"] = w
+        del Q, kg, vg, K, V, tiles, groups, merged, fused, ftiles, dO, O, L, dq, dk, dv, btiles, ws
+        torch.cuda.empty_cache()
+    if "mesh" in names:
+        n, a, b, g, P = 64, 8, 8, 9, 16384
+        qparts, kparts = ma.mesh_attn_map_mesh_tile(n, a, b, g, True)
+        Q = {i: randn((1, P, HQ, D)) for i in qparts}
+        kg = randn((1, b * P, HKV, D))
+        vg = randn((1, b * P, HKV, D))
+        K = {j: kg[:, t * P:(t + 1) * P] for t, j in enumerate(kparts)}
+        V = {j: vg[:, t * P:(t + 1) * P] for t, j in enumerate(kparts)}
+        tiles = {(i, j): Tile(Q[i], K[j], V[j], *out(P)) for i in qparts for j in kparts}
+        mu = math.log(b * P) + 0.5
+        inc = [(randn((1, P, HQ, D), mul=0.01), randn((1, HQ, P), torch.float32, 1.0, mu)) for _ in range(a - 1)]
+        merged = {i: out(P) for i in qparts}
+        pairs = len(tiles) * P * P
+        part_bytes = P * HQ * D * 2 + HQ * P * 4
+        merge_bytes = (7 * (8 + 1) + (15 + 1)) * part_bytes
+
+        def merges():
+            for i in qparts:
+                os_ = [tiles[(i, j)].o for j in kparts]
+                ls_ = [tiles[(i, j)].lse for j in kparts]
+                if i == g:
+                    os_ += [x[0] for x in inc]
+                    ls_ += [x[1] for x in inc]
+                ma.mesh_attn_merge(os_, ls_, merged[i][0], merged[i][1])
+
+        fused = {i: out(P) for i in qparts}
+        ftiles = [Tile(Q[i], kg, vg, *fused[i]) for i in qparts]
+
+        def fused_step():
+            ma.mesh_attn_tile_fwd(ftiles, scale, ma.MA_MASK_NONE)
+            ma.mesh_attn_merge([fused[g][0]] + [x[0] for x in inc], [fused[g][1]] + [x[1] for x in inc],
+                               fused[g][0], fused[g][1])
+
+        w = {"tiles": len(tiles), "allowed_pairs_per_head": pairs}
+        w["fwd_tiles"] = _tf(4.0 * D * HQ * pairs,
+                             _timed(lambda: ma.mesh_attn_tile_fwd(list(tiles.values()), scale, ma.MA_MASK_NONE), reps))
+        w["merge_7x8_and_15"] = _gb(merge_bytes, _timed(merges, reps))
+        w["fwd_fused_gathered_kv_plus_owned_merge"] = _tf(4.0 * D * HQ * pairs, _timed(fused_step, reps))
+        del tiles, merged, fused, ftiles
+        torch.cuda.empty_cache()
+        # backward of the 8 x 8 tile: dQ_i over the 8 KV partitions, dK/dV_j over the 8 Q partitions
+        dO = {i: randn((1, P, HQ, D)) for i in qparts}
+        O = {i: randn((1, P, HQ, D), mul=0.01) for i in qparts}
+        L = {i: randn((1, HQ, P), torch.float32, 0.3, mu) for i in qparts}
+        dq = {i: torch.empty((1, P, HQ, D), dtype=torch.float32, device=dev) for i in qparts}
+        dk = {j: torch.empty((1, P, HKV, D), dtype=torch.float32, device=dev) for j in kparts}
+        dv = {j: torch.empty_like(dk[j]) for j in kparts}
+        btiles = [BwdTile(Q[i], K[j], V[j], O[i], dO[i], L[i], dq[i], dk[j], dv[j]) for i in qparts for j in kparts]
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        w["bwd_tiles"] = _tf(10.0 * D * HQ * pairs,
+                             _timed(lambda: ma.mesh_attn_tile_bwd(btiles, scale, ma.MA_MASK_NONE, workspace=ws), 1))
+        # the addition of the gradient reduce-scatter: 8 partial dQ of one Q partition (fp32) summed
+        parts = [dq[i] for i in qparts]
+        red = torch.empty_like(parts[0])
+        w["reduce_add_8_dq"] = _gb(9 * parts[0].numel() * 4, _timed(lambda: ma.mesh_attn_reduce_add(parts, red), reps))
+        res["mesh-8x8-1m-g9"] = w
+        del Q, kg, vg, K, V, inc, dO, O, L, dq, dk, dv, btiles, ws, parts, red
+        torch.cuda.empty_cache()
+    if "bwd4" in names:
+        S, nq = 8192, 4
+        k = randn((1, S, HKV, D))
+        v = randn((1, S, HKV, D))
+        dk = torch.empty((1, S, HKV, D), dtype=torch.float32, device=dev)
+        dv = torch.empty_like(dk)
+        btiles = []
+        for _ in range(nq):
+            btiles.append(BwdTile(randn((1, S, HQ, D)), k, v, randn((1, S, HQ, D), mul=0.02), randn((1, S, HQ, D)),
+                                  randn((1, HQ, S), torch.float32, 0.3, math.log(S) + 0.5),
+                                  torch.empty((1, S, HQ, D), dtype=torch.float32, device=dev), dk, dv))
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        res["gqa-bwd-4x8k"] = {"bwd_tiles": _tf(10.0 * D * HQ * nq * S * S, _timed(
+            lambda: ma.mesh_attn_tile_bwd(btiles, scale, ma.MA_MASK_NONE, workspace=ws), reps))}
+        del k, v, dk, dv, btiles, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -307,6 +486,11 @@ def main():
                    "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "mask": "none", "steps_parts": sorted(parts)},
         "roofline": rl, "parts": res_parts,
     }
+    names = set(args.workloads.split(",")) - {"none", ""}
+    if names:
+        del q, k, v, dO, o_in, lse_in, o, lse, o_m, lse_m, dq, dk, dv, bwd_tiles, ws
+        torch.cuda.empty_cache()
+        out["workloads"] = measure_workloads(names, args.workload_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, np.float32(scale))
     print(json.dumps(out), flush=True)

@@ -86,6 +86,13 @@ def test_zigzag_causal_128k_rank5_forward_and_merge():
         o, lse = empty_out(C)
         ma.mesh_attn_merge([t.o for t in mine], [t.lse for t in mine], o, lse)
         merged.append((o, lse))
+    # the same share with the KV chunks gathered into one buffer: one causal tile per Q chunk, no merge
+    kg = torch.cat([x[0] for x in K], dim=1)
+    vg = torch.cat([x[0] for x in V], dim=1)
+    fused = [empty_out(C) for _ in qchunks]
+    ftiles = [Tile(Q[c][0], kg[:, :(c + 1) * C], vg[:, :(c + 1) * C], fused[i][0], fused[i][1], qpos[i],
+                   ma.mesh_attn_pos_contiguous(0)) for i, c in enumerate(qchunks)]
+    ma.mesh_attn_tile_fwd(ftiles, float(SCALE), ma.MA_MASK_CAUSAL)
     torch.cuda.synchronize()
     kall = np.concatenate([x[1] for x in K], axis=1)
     vall = np.concatenate([x[1] for x in V], axis=1)
@@ -96,6 +103,9 @@ def test_zigzag_causal_128k_rank5_forward_and_merge():
         Oref, Lref = attn_tile(Q[c][1], kall, vall, SCALE, None, True, qp, kp_all, rows=rows)
         check_close(f"merged O chunk {c}", host_f64(merged[i][0])[:, rows], Oref, BF16_O_TOL)
         check_close(f"merged LSE chunk {c}", host_f64(merged[i][1])[:, :, rows], Lref, BF16_LSE_TOL)
+        # fused: one tile per Q chunk over the gathered KV buffer (chunks 0..c, one contiguous range)
+        check_close(f"fused O chunk {c}", host_f64(fused[i][0])[:, rows], Oref, BF16_O_TOL)
+        check_close(f"fused LSE chunk {c}", host_f64(fused[i][1])[:, :, rows], Lref, BF16_LSE_TOL)
         # the diagonal (partially masked) tile's own partial
         t = [t for t, (ii, jj, _) in zip(tiles, wl) if ii == i and jj == c][0]
         Ot, Lt = attn_tile(Q[c][1], K[c][1], V[c][1], SCALE, None, True, qp, positions(kpos[c], C), rows=rows)
@@ -150,6 +160,15 @@ def test_mesh_8x8_1m_forward_and_merge():
         o, lse = empty_out(P)
         ma.mesh_attn_merge(os_, ls_, o, lse)
         merged[i] = (o, lse)
+    # the same share with the 8 KV partitions gathered into one buffer: one tile per Q partition, and
+    # only the owned partition's merge with the 7 incoming partials
+    kg = torch.cat([K[j][0] for j in kparts], dim=1)
+    vg = torch.cat([V[j][0] for j in kparts], dim=1)
+    fused = {i: empty_out(P) for i in qparts}
+    ma.mesh_attn_tile_fwd([Tile(Q[i][0], kg, vg, fused[i][0], fused[i][1]) for i in qparts], float(SCALE),
+                          ma.MA_MASK_NONE)
+    ma.mesh_attn_merge([fused[g][0]] + [x[0] for x in inc], [fused[g][1]] + [x[2] for x in inc],
+                       fused[g][0], fused[g][1])
     torch.cuda.synchronize()
     kall = np.concatenate([K[j][1] for j in kparts], axis=1)
     vall = np.concatenate([V[j][1] for j in kparts], axis=1)
@@ -162,6 +181,8 @@ def test_mesh_8x8_1m_forward_and_merge():
             Oref, Lref = Oloc, Lloc
         check_close(f"merged O Q{i}", host_f64(merged[i][0])[:, rows], Oref, BF16_O_TOL)
         check_close(f"merged LSE Q{i}", host_f64(merged[i][1])[:, :, rows], Lref, BF16_LSE_TOL)
+        check_close(f"fused O Q{i}", host_f64(fused[i][0])[:, rows], Oref, BF16_O_TOL)
+        check_close(f"fused LSE Q{i}", host_f64(fused[i][1])[:, :, rows], Lref, BF16_LSE_TOL)
     # one partial tile on its own
     i, j = qparts[3], kparts[5]
     rows = sample_rows(P, 99)
@@ -215,3 +236,70 @@ def test_gqa_bwd_4x8k():
     check("dK[keys]", host_f64(dk)[:, keys], dk_r)
     check("dV[keys]", host_f64(dv)[:, keys], dv_r)
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+def test_zigzag_causal_128k_rank5_backward():
+    # Backward of the causal zigzag share: dQ for chunks {5, 26}, partial dK/dV for KV chunks 0..26,
+    # 33 computed pairs in one call (EMPTY pairs skipped, the two diagonal pairs masked per element).
+    # O and LSE are seeded stored inputs with a real forward's magnitudes (O ~ 0.02 N(0,1),
+    # LSE ~ ln(allowed keys) + 0.5 + 0.3 N(0,1)); both sides read the same values.
+    wid, N, r, C = 6, 16, 5, 4096
+    log("[workload zigzag-causal-128k backward]")
+    qchunks = ma.mesh_attn_map_zigzag(N, r)
+    nkv = max(qchunks) + 1
+    K = [gen(wid, synthetic.T_K, j, (1, C, HKV, D)) for j in range(nkv)]
+    V = [gen(wid, synthetic.T_V, j, (1, C, HKV, D)) for j in range(nkv)]
+    qpos = [ma.mesh_attn_pos_contiguous(c * C) for c in qchunks]
+    kpos = [ma.mesh_attn_pos_contiguous(j * C) for j in range(nkv)]
+    wl = ma.mesh_attn_build_worklist(qpos, [C, C], kpos, [C] * nkv, ma.MA_MASK_CAUSAL)
+    assert len(wl) == 33
+    dk = [torch.empty((1, C, HKV, D), dtype=torch.float32, device=DEV) for _ in range(nkv)]
+    dv = [torch.empty_like(x) for x in dk]
+    host, dev_in = [], []
+    for i, c in enumerate(qchunks):
+        q, qv = gen(wid, synthetic.T_Q, c, (1, C, HQ, D))
+        do, dov = gen(wid, synthetic.T_DO, c, (1, C, HQ, D))
+        ob = synthetic.f32_to_bf16_bits(synthetic.normal_f32(wid, synthetic.T_O_IN, c, (1, C, HQ, D)) * np.float32(0.02))
+        ov = synthetic.bf16_bits_to_f32(ob).astype(np.float64)
+        n_allowed = (c * C + np.arange(C) + 1).astype(np.float32)
+        lv = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, c, (1, HQ, C)) * np.float32(0.3)
+              + np.log(n_allowed)[None, None, :] + np.float32(0.5)).astype(np.float32)
+        dq = torch.empty((1, C, HQ, D), dtype=torch.float32, device=DEV)
+        dev_in.append((q, dev_bf16(ob), do, torch.from_numpy(lv).to(DEV), dq))
+        host.append(dict(q=qv, o=ov, do=dov, lse=lv.astype(np.float64), q_pos=positions(qpos[i], C)))
+    tiles = [BwdTile(dev_in[i][0], K[j][0], V[j][0], dev_in[i][1], dev_in[i][2], dev_in[i][3], dev_in[i][4],
+                     dk[j], dv[j], qpos[i], kpos[j]) for i, j, _ in wl]
+    ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(tiles, float(SCALE))), dtype=torch.uint8,
+                     device=DEV)
+    ma.mesh_attn_tile_bwd(tiles, float(SCALE), ma.MA_MASK_CAUSAL, workspace=ws)
+    torch.cuda.synchronize()
+
+    def check(name, got, ref):
+        scale = max(float(np.max(np.abs(ref))), 1e-3)
+        err = float(np.max(np.abs(got - ref)))
+        log(f"  {name}: max_abs_err={err:.3e} max|ref|={scale:.3e} rel={err/scale:.2e}")
+        assert np.isfinite(got).all() and err <= 2e-2 * scale
+
+    kall = np.concatenate([x[1] for x in K], axis=1)
+    vall = np.concatenate([x[1] for x in V], axis=1)
+    kp_all = np.arange(nkv * C, dtype=np.int64)
+    for i, h in enumerate(host):
+        rows = sample_rows(C, wid + 10 * i, extra=8)
+        dq_r, _, _ = attn_tile_bwd(h["q"][:, rows], kall, vall, h["o"][:, rows], h["do"][:, rows],
+                                   h["lse"][:, :, rows], SCALE, None, True, h["q_pos"][rows], kp_all)
+        check(f"dQ chunk {qchunks[i]}", host_f64(dev_in[i][4])[:, rows], dq_r)
+    # dK/dV on sampled keys of KV chunks met by both Q chunks (0, 5: diagonal of chunk 5), by one (13),
+    # and the diagonal of chunk 26
+    for j in (0, 5, 13, 26):
+        keys = sample_rows(C, wid + 100 + j, extra=6)
+        kp = positions(kpos[j], C)[keys]
+        dk_r = dv_r = 0
+        for h in host:
+            _, a_, b_ = attn_tile_bwd(h["q"], K[j][1][:, keys], V[j][1][:, keys], h["o"], h["do"], h["lse"], SCALE,
+                                      None, True, h["q_pos"], kp)
+            dk_r = dk_r + a_
+            dv_r = dv_r + b_
+        check(f"dK chunk {j}", host_f64(dk[j])[:, keys], dk_r)
+        check(f"dV chunk {j}", host_f64(dv[j])[:, keys], dv_r)
+    for j in range(nkv):
+        assert torch.isfinite(dk[j]).all() and torch.isfinite(dv[j]).all()
