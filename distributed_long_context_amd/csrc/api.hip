@@ -157,26 +157,44 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   }
 
   const bool bf16 = a->dtype == MA_BF16;
-  int n = 0, wg = 0;
-  auto flush = [&]() -> int {
-    if (n == 0) return MA_OK;
-    p.ntiles = n;
-    int e = bf16 ? launch_fwd_bf16(p, a->head_dim, wg, stream) : launch_fwd_f32(p, a->head_dim, wg, stream);
-    n = 0;
-    wg = 0;
+  // Tiles go to one of three launches by how much masking they need: FULL tiles
+  // (and every tile without a mask) run the unmasked kernel, PARTIAL tiles whose
+  // key positions are one segment the single-segment variant, the rest the
+  // general one.  A tile naming the output of one already queued waits for it.
+  FwdParams bp[3];
+  int bn[3] = {0, 0, 0}, bwg[3] = {0, 0, 0};
+  for (int m = 0; m < 3; ++m) {
+    bp[m] = p;
+    bp[m].mask = m;
+  }
+  auto flush = [&](int m) -> int {
+    if (bn[m] == 0) return MA_OK;
+    bp[m].ntiles = bn[m];
+    int e = bf16 ? launch_fwd_bf16(bp[m], a->head_dim, bwg[m], stream) : launch_fwd_f32(bp[m], a->head_dim, bwg[m], stream);
+    bn[m] = 0;
+    bwg[m] = 0;
     return check_hip(e, "tile_fwd launch");
+  };
+  auto flush_all = [&]() -> int {
+    for (int m = 0; m < 3; ++m) {
+      int r = flush(m);
+      if (r) return r;
+    }
+    return MA_OK;
   };
   for (int i = 0; i < a->ntiles; ++i) {
     const ma_tile& t = a->tiles[i];
-    // a tile naming the output of one already in this launch waits for it (list order)
-    for (int j = 0; j < n; ++j)
-      if (p.tiles[j].o == t.o || p.tiles[j].lse == t.lse) {
-        rc = flush();
-        if (rc) return rc;
-        break;
-      }
-    if (a->mask_mode != MA_MASK_NONE &&
-        mesh_attn_classify(&t.q_pos, t.sq, &t.k_pos, t.sk, a->mask_mode) == MA_TILE_EMPTY) {
+    bool dup = false;
+    for (int m = 0; m < 3 && !dup; ++m)
+      for (int j = 0; j < bn[m]; ++j)
+        if (bp[m].tiles[j].o == t.o || bp[m].tiles[j].lse == t.lse) dup = true;
+    if (dup) {
+      rc = flush_all();
+      if (rc) return rc;
+    }
+    const int cls = a->mask_mode == MA_MASK_NONE ? MA_TILE_FULL
+                                                 : mesh_attn_classify(&t.q_pos, t.sq, &t.k_pos, t.sk, a->mask_mode);
+    if (cls == MA_TILE_EMPTY) {
       if (a->accumulate) continue;  // nothing to fold in
       int e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss,
                                 p.o_sh, p.l_sb, p.l_sh, stream);
@@ -184,11 +202,13 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       if (rc) return rc;
       continue;
     }
-    FwdTile& ft = p.tiles[n];
+    const int m = cls == MA_TILE_FULL ? 0 : (t.k_pos.nseg == 1 ? 1 : 2);
+    FwdTile& ft = bp[m].tiles[bn[m]];
+    std::memset(&ft, 0, sizeof(ft));
     ft.q = t.q; ft.k = t.k; ft.v = t.v; ft.o = t.o; ft.lse = t.lse;
     ft.sq = (int32_t)t.sq;
     ft.sk = (int32_t)t.sk;
-    if (a->mask_mode != MA_MASK_NONE) {
+    if (m != 0) {
       to_kpos(t.q_pos, ft.qp);
       to_kpos(t.k_pos, ft.kp);
     } else {
@@ -205,16 +225,16 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       ft.chunks = (int32_t)((t.sq + 63) / 64);
       wgs = (int64_t)a->batch * a->hq * ft.chunks;
     }
-    if (wgs + wg >= INT32_MAX) return set_error(MA_ERR_INVALID, "tile too large for one launch");
-    ft.wg_begin = wg;
-    wg += (int)wgs;
-    ++n;
-    if (n == kFwdTilesPerLaunch) {
-      rc = flush();
+    if (wgs + bwg[m] >= INT32_MAX) return set_error(MA_ERR_INVALID, "tile too large for one launch");
+    ft.wg_begin = bwg[m];
+    bwg[m] += (int)wgs;
+    ++bn[m];
+    if (bn[m] == kFwdTilesPerLaunch) {
+      rc = flush(m);
       if (rc) return rc;
     }
   }
-  return flush();
+  return flush_all();
 }
 
 int mesh_attn_merge(const ma_merge_args* a, void* stream) {

@@ -35,7 +35,12 @@
 //  * Masks are resolved per 64-key block ([Mesh] section 3.7 pair classes):
 //    blocks with no allowed pair for the workgroup are never loaded, blocks with
 //    every pair allowed run unmasked, the rest (and the ragged last block)
-//    compare global positions element by element.
+//    compare global positions element by element.  Tiles that are FULL as a
+//    whole run the kernel without masks.  When the key positions are one
+//    segment (contiguous or striped) they grow with the key index, so a lane
+//    keeps only the index of its last allowed key, a wave the count of leading
+//    blocks it sees whole and the workgroup the count of blocks with any allowed
+//    pair; no position data stays live in the loop.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <type_traits>
@@ -62,11 +67,16 @@ struct FwdCfg {
   static constexpr int LPW = kBN * CH / 64 / kWaves;  // direct-to-LDS loads per wave per tensor
 };
 
-template <int D, bool MASKED>
+// MODE 0: no position mask.  MODE 1: the key positions are one segment
+// (global = kgb + t * kst, nondecreasing), so every mask decision reduces to the
+// last allowed key index of a query position.  MODE 2: any position maps.
+template <int D, int MODE>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(const FwdParams p) {
   using C = FwdCfg<D>;
+  constexpr bool MASKED = MODE != 0;
+  constexpr bool SEG1 = MODE == 1;
   // K stages in the first half, V stages in the second: kv_s[0][st] is K, kv_s[1][st] is V
   __shared__ __attribute__((aligned(1024))) __bf16 kv_s[2][kStages][C::BLK];
 
@@ -138,7 +148,19 @@ fwd_bf16_kernel(const FwdParams p) {
   }
 
   // ---- block classes: 0 empty, 1 partial (element mask), 2 full ----
-  const int nkb = (T.sk + kBN - 1) / kBN;
+  const int nkb_all = (T.sk + kBN - 1) / kBN;
+  // one key segment: this lane's last allowed key (-1: none), the number of
+  // leading blocks every row of the wave may see whole, and the number of
+  // blocks with any allowed pair for the workgroup (the rest follow them)
+  int klast = T.sk - 1, kfull_w = 0, nkb_wg = nkb_all;
+  if constexpr (SEG1) {
+    const int kgb = T.kp.gb[0], kst = T.kp.st[0];
+    auto last_key = [&](int pq) { return pq < kgb ? -1 : min(T.sk - 1, (pq - kgb) / kst); };
+    klast = last_key(qpos);
+    kfull_w = active ? (last_key(w_pmin) + 1) / kBN : 0;
+    nkb_wg = (last_key(wg_pmax) + kBN) / kBN;
+  }
+  const int nkb = nkb_wg;
   auto block_class = [&](int kb, int pmin, int pmax) -> int {
     const bool tail = kb * kBN + kBN > T.sk;
     if constexpr (!MASKED) {
@@ -152,7 +174,7 @@ fwd_bf16_kernel(const FwdParams p) {
     }
   };
   auto next_block = [&](int from) -> int {
-    if constexpr (!MASKED) {
+    if constexpr (!MASKED || SEG1) {
       return from < nkb ? from : nkb;
     } else {
       for (int kb = from; kb < nkb; ++kb)
@@ -226,8 +248,13 @@ fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {  // branch-free: position at a clamped index, then a select
       const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-      bool ok = key < T.sk;
-      if constexpr (MASKED) ok = ok & (pos_at_dev(T.kp, min(key, T.sk - 1)) <= qpos);
+      bool ok;
+      if constexpr (SEG1) {
+        ok = key <= klast;
+      } else {
+        ok = key < T.sk;
+        if constexpr (MASKED) ok = ok & (pos_at_dev(T.kp, min(key, T.sk - 1)) <= qpos);
+      }
       s[e] = ok ? s[e] : -INFINITY;
     }
   };
@@ -235,8 +262,12 @@ fwd_bf16_kernel(const FwdParams p) {
   // mask (when the block is not fully allowed for this wave) and row max of a half, in log2 units
   float mb2 = -INFINITY;
   auto half_max = [&](int kb, int kb2, f32x16& s) {
-    const int cls = active ? block_class(kb, w_pmin, w_pmax) : 1;
-    if (cls != 2) mask_half(kb, kb2, s);  // partial, or empty for this wave only
+    if constexpr (SEG1) {
+      if (kb >= kfull_w) mask_half(kb, kb2, s);
+    } else {
+      const int cls = active ? block_class(kb, w_pmin, w_pmax) : 1;
+      if (cls != 2) mask_half(kb, kb2, s);  // partial, or empty for this wave only
+    }
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
@@ -410,11 +441,13 @@ int launch_fwd_bf16(const FwdParams& p, int head_dim, int total_wgs, void* strea
   dim3 grid(total_wgs), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
   if (head_dim == 128) {
-    if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, s, p);
+    if (p.mask == 1) hipLaunchKernelGGL((fwd_bf16_kernel<128, 1>), grid, block, 0, s, p);
+    else if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<128, 2>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 0>), grid, block, 0, s, p);
   } else {
-    if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
+    if (p.mask == 1) hipLaunchKernelGGL((fwd_bf16_kernel<64, 1>), grid, block, 0, s, p);
+    else if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<64, 2>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 0>), grid, block, 0, s, p);
   }
   return (int)hipGetLastError();
 }

@@ -41,7 +41,7 @@ struct FwdTile {
 struct FwdParams {
   int32_t ntiles;
   int32_t batch, hq, hkv;
-  int32_t mask;           // 0 none, 1 causal on positions
+  int32_t mask;           // 0 none; 1 causal, one key segment; 2 causal, any positions
   int32_t gmax;           // largest number of query heads sharing one KV head
   int32_t accumulate;     // fold into the (O, LSE) held by the output buffers
   float scale;            // softmax scale
