@@ -431,27 +431,41 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
   }
 
   // 2) dQ launches (entries = Q groups with their KV partitions), then dK/dV launches
-  //    (entries = KV groups with their Q partitions).  A group with more than 8
-  //    partners is split into pieces; a later piece adds to the earlier ones and
-  //    runs in a later launch.  Each launch holds at most 8 entries, 8 partitions
-  //    of either side, and one piece per group.
+  //    (entries = KV groups with their Q partitions).  A group's partners are split
+  //    by pair class: FULL pairs run in unmasked launches, PARTIAL (and EMPTY) pairs
+  //    in masked ones, FULL first.  A group with more than 8 partners of one kind is
+  //    split further; every piece after a group's first adds to the earlier ones and
+  //    runs in a later launch.  Each launch holds at most 8 entries, 8 partitions of
+  //    either side, and one piece per group, all of one mask kind.
+  std::vector<int> tile_cls(a->ntiles, MA_TILE_FULL);
+  if (a->mask_mode != MA_MASK_NONE)
+    for (int i = 0; i < a->ntiles; ++i)
+      tile_cls[i] = mesh_attn_classify(&a->tiles[i].q_pos, a->tiles[i].sq, &a->tiles[i].k_pos, a->tiles[i].sk,
+                                       a->mask_mode);
   for (int side = 0; side < 2; ++side) {
     const bool dq_side = side == 0;
     const auto& own = dq_side ? grp.qg : grp.kvg;
-    struct Piece { int group; std::vector<int> partners; int accumulate; };
+    struct Piece { int group; std::vector<int> partners; int accumulate; bool masked; };
     std::vector<Piece> pieces;
     for (int gi = 0; gi < (int)own.size(); ++gi) {
-      std::vector<int> partners;
+      std::vector<int> full, other;  // partner groups of FULL pairs; of PARTIAL or EMPTY pairs
       for (int ti : own[gi]) {
         const int pg = dq_side ? grp.kv_of[ti] : grp.q_of[ti];
-        if (std::find(partners.begin(), partners.end(), pg) == partners.end()) partners.push_back(pg);
+        auto& lst = tile_cls[ti] == MA_TILE_FULL ? full : other;
+        if (std::find(lst.begin(), lst.end(), pg) == lst.end()) lst.push_back(pg);
       }
-      for (size_t s0 = 0; s0 < partners.size(); s0 += kBwdPerLaunch) {
-        Piece pc;
-        pc.group = gi;
-        pc.partners.assign(partners.begin() + s0, partners.begin() + std::min(partners.size(), s0 + kBwdPerLaunch));
-        pc.accumulate = (s0 == 0) ? (a->accumulate ? 1 : 0) : 1;
-        pieces.push_back(pc);
+      bool first = true;
+      for (int kind = 0; kind < 2; ++kind) {
+        const auto& lst = kind == 0 ? full : other;
+        for (size_t s0 = 0; s0 < lst.size(); s0 += kBwdPerLaunch) {
+          Piece pc;
+          pc.group = gi;
+          pc.partners.assign(lst.begin() + s0, lst.begin() + std::min(lst.size(), s0 + kBwdPerLaunch));
+          pc.accumulate = first ? (a->accumulate ? 1 : 0) : 1;
+          pc.masked = kind == 1;
+          first = false;
+          pieces.push_back(pc);
+        }
       }
     }
     std::vector<bool> done(pieces.size(), false);
@@ -459,7 +473,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
     while (remaining > 0) {
       BwdParams p = base;
       std::vector<int> own_tab, part_tab, groups_in;
-      int ne = 0, wg = 0;
+      int ne = 0, wg = 0, kind = -1;  // kind: mask kind of this launch, set by its first piece
       for (size_t pi = 0; pi < pieces.size() && ne < kBwdPerLaunch; ++pi) {
         if (done[pi]) continue;
         const Piece& pc = pieces[pi];
@@ -469,6 +483,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
         for (size_t pj = 0; pj < pi; ++pj)
           if (!done[pj] && pieces[pj].group == pc.group) earlier_pending = true;
         if (earlier_pending) continue;
+        if (kind >= 0 && kind != (pc.masked ? 1 : 0)) continue;
         std::vector<int> new_part = part_tab;
         for (int x : pc.partners)
           if (std::find(new_part.begin(), new_part.end(), x) == new_part.end()) new_part.push_back(x);
@@ -477,6 +492,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
         part_tab = new_part;
         if (own_new) own_tab.push_back(pc.group);
         groups_in.push_back(pc.group);
+        kind = pc.masked ? 1 : 0;
         BwdEntry& en = p.entries[ne];
         en.self = (int32_t)(std::find(own_tab.begin(), own_tab.end(), pc.group) - own_tab.begin());
         en.n = (int32_t)pc.partners.size();
@@ -500,6 +516,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
         --remaining;
       }
       p.nentries = ne;
+      p.mask = kind == 1 ? 1 : 0;
       for (size_t i = 0; i < own_tab.size(); ++i) {
         if (dq_side) p.qparts[i] = qparts[own_tab[i]];
         else p.kvparts[i] = kvparts[own_tab[i]];
