@@ -318,6 +318,29 @@ def measure_workloads(names, reps):
         w["fwd_fused_gathered_kv_plus_owned_merge"] = _tf(4.0 * D * HQ * pairs, _timed(fused_step, reps))
         del tiles, merged, fused, ftiles
         torch.cuda.empty_cache()
+        # GOO replay: k_Q = k_KV = 4 chunks per partition; the compute tasks C-i-j (gathered Q chunk i of
+        # 8 x 4096 rows against gathered KV chunk j of 8 x 4096 keys) run in the greedy plan's order, each
+        # folded into its Q chunk's (O, LSE) by the forward's accumulate mode
+        kq = kkv = 4
+        cq, ck = P // kq, P // kkv
+        gq = [torch.cat([Q[i][:, c * cq:(c + 1) * cq] for i in qparts], dim=1) for c in range(kq)]
+        gk = [torch.cat([K[j][:, c * ck:(c + 1) * ck] for j in kparts], dim=1) for c in range(kkv)]
+        gv = [torch.cat([V[j][:, c * ck:(c + 1) * ck] for j in kparts], dim=1) for c in range(kkv)]
+        acc = [out(a * cq) for _ in range(kq)]
+        plan = ma.mesh_attn_goo_plan(kq, kkv, 0.5, 1.0, 0.5, 0.5, 1.0)
+        order = [(i, j) for _, comp in plan for _, i, j in comp]
+
+        def goo_replay():
+            first = set()
+            for i, j in order:
+                ma.mesh_attn_tile_fwd([Tile(gq[i], gk[j], gv[j], acc[i][0], acc[i][1])], scale, ma.MA_MASK_NONE,
+                                      accumulate=i in first)
+                first.add(i)
+
+        w["fwd_goo_replay_4x4"] = _tf(4.0 * D * HQ * pairs, _timed(goo_replay, reps))
+        w["fwd_goo_replay_4x4"]["tasks"] = len(order)
+        del gq, gk, gv, acc
+        torch.cuda.empty_cache()
         # backward of the 8 x 8 tile: dQ_i over the 8 KV partitions, dK/dV_j over the 8 Q partitions
         dO = {i: randn((1, P, HQ, D)) for i in qparts}
         O = {i: randn((1, P, HQ, D), mul=0.01) for i in qparts}

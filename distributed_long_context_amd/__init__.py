@@ -19,7 +19,7 @@ __all__ = [
     "mesh_attn_tile_fwd", "mesh_attn_merge", "mesh_attn_reduce_add", "mesh_attn_tile_bwd", "mesh_attn_tile_bwd_workspace_size",
     "mesh_attn_map_mesh_tile", "mesh_attn_map_groups", "mesh_attn_map_zigzag", "mesh_attn_pos_contiguous",
     "mesh_attn_pos_zigzag", "mesh_attn_pos_striped", "mesh_attn_pos_at", "mesh_attn_classify",
-    "mesh_attn_count_allowed", "mesh_attn_build_worklist", "mesh_attn_version", "Pos", "Tile", "BwdTile",
+    "mesh_attn_count_allowed", "mesh_attn_build_worklist", "mesh_attn_goo_plan", "mesh_attn_version", "Pos", "Tile", "BwdTile",
     "MA_F32", "MA_BF16", "MA_MASK_NONE", "MA_MASK_CAUSAL", "MA_MASK_STRIPED_ZIGZAG", "MA_TILE_EMPTY",
     "MA_TILE_PARTIAL", "MA_TILE_FULL", "MeshAttnError", "lib",
 ]
@@ -371,3 +371,30 @@ def mesh_attn_build_worklist(q_pos: Sequence[Pos], sq: Sequence[int], k_pos: Seq
 
 def mesh_attn_version() -> int:
     return int(lib().mesh_attn_version())
+
+
+# -------------------------------------------------------------- GOO plan --
+
+_GOO_NAMES = {1: "AG-Q", 2: "AG-KV", 3: "RS-Q"}
+
+
+def mesh_attn_goo_plan(k_q: int, k_kv: int, t_ag_q: float, t_ag_kv: float, t_rs_q: float, t_c, gamma: float):
+    """Greedy GOO schedule: a list of steps (comm task or None, [("C", i, j), ...]); a comm task is
+    ("AG-Q", i), ("AG-KV", j) or ("RS-Q", i).  t_c: one compute time or a k_q x k_kv nested list."""
+    n = int(k_q) * int(k_kv)
+    if isinstance(t_c, (list, tuple)):
+        flat = [float(x) for row in t_c for x in row]
+    else:
+        flat = [float(t_c)] * max(n, 0)
+    tc = (C.c_double * max(1, len(flat)))(*flat)
+    cap = max(1, 2 * int(k_q) + int(k_kv) + max(n, 0))
+    steps = (_abi.ma_goo_step * cap)()
+    r = lib().mesh_attn_goo_plan(int(k_q), int(k_kv), float(t_ag_q), float(t_ag_kv), float(t_rs_q), tc,
+                                 float(gamma), cap, steps)
+    if r < 0:
+        raise MeshAttnError(-r, "mesh_attn_goo_plan")
+    out = []
+    for s in steps[:r]:
+        comm = None if s.comm_type == 0 else (_GOO_NAMES[s.comm_type], s.comm_index)
+        out.append((comm, [("C", c // k_kv, c % k_kv) for c in s.compute[:s.ncompute]]))
+    return out

@@ -51,6 +51,13 @@ class ma_reduce_args(C.Structure):
     _fields_ = [("k", I32), ("reserved", I32), ("n", I64), ("in_", C.POINTER(VP)), ("out", VP)]
 
 
+MA_GOO_MAX_COMPUTE = 16
+
+
+class ma_goo_step(C.Structure):
+    _fields_ = [("comm_type", I32), ("comm_index", I32), ("ncompute", I32), ("compute", I32 * MA_GOO_MAX_COMPUTE)]
+
+
 class ma_bwd_tile(C.Structure):
     _fields_ = [("q", VP), ("k", VP), ("v", VP), ("o", VP), ("dout", VP), ("lse", VP), ("dq", VP), ("dk", VP),
                 ("dv", VP), ("sq", I64), ("sk", I64), ("q_pos", ma_pos), ("k_pos", ma_pos)]
@@ -69,6 +76,8 @@ SIGNATURES = {
     "mesh_attn_tile_fwd": (I32, [C.POINTER(ma_tile_fwd_args), VP]),
     "mesh_attn_merge": (I32, [C.POINTER(ma_merge_args), VP]),
     "mesh_attn_reduce_add": (I32, [C.POINTER(ma_reduce_args), VP]),
+    "mesh_attn_goo_plan": (I32, [I32, I32, C.c_double, C.c_double, C.c_double, C.POINTER(C.c_double), C.c_double,
+                                 I32, C.POINTER(ma_goo_step)]),
     "mesh_attn_tile_bwd_workspace_size": (C.c_size_t, [C.POINTER(ma_tile_bwd_args)]),
     "mesh_attn_tile_bwd": (I32, [C.POINTER(ma_tile_bwd_args), VP, C.c_size_t, VP]),
     "mesh_attn_map_mesh_tile": (I32, [I32, I32, I32, I32, I32, C.POINTER(I32), C.POINTER(I32)]),

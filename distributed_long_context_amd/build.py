@@ -28,7 +28,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 FAST_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"], "bwd.hip": ["-fno-honor-nans"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
-SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_f32.hip", "merge.hip", "reduce.hip", "bwd.hip", "mapper.cpp"]
+SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_f32.hip", "merge.hip", "reduce.hip", "bwd.hip", "mapper.cpp", "goo.cpp"]
 
 
 def _compile(src: str) -> str:

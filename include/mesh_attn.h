@@ -310,6 +310,43 @@ int32_t mesh_attn_build_worklist(int32_t nq, const ma_pos* q_pos, const int64_t*
                                  int32_t mask_mode, int32_t max_out,
                                  int32_t* out_q, int32_t* out_k, int32_t* out_class);
 
+/* ---------------------------------------------------------------------------
+ * GOO step planner (host only).  [Mesh] section 3.4 (2-D Greedy Overlapping
+ * Optimization): the Q partitions of a GPU's tile are cut into k_q chunks and
+ * the KV partitions into k_kv chunks, giving communication tasks AG-Q-i, RS-Q-i
+ * (i < k_q), AG-KV-j (j < k_kv) and compute tasks C-i-j.  C-i-j is ready when
+ * AG-Q-i and AG-KV-j are done, RS-Q-i when every C-i-j is done.  Each step runs
+ * one communication task with compute tasks that were ready when it began, and
+ * finishes before the next.  The communication task is the candidate with the
+ * largest profit = (compute time it makes ready) / (its own time); candidates
+ * are the lowest-index unscheduled chunk of each type (RS-Q once ready), ties
+ * go to AG-KV, then AG-Q, then RS-Q.  Ready compute tasks join in (i, j) order
+ * while their summed time is below gamma * (the step's communication time).
+ * With no communication task possible and computation ready, a compute-only step
+ * runs one ready task.  Deterministic: every GPU given the same costs gets the
+ * same schedule, as the section requires.
+ *
+ * Returns the number of steps written (at most 2 k_q + k_kv + k_q k_kv), or
+ * -MA_ERR_INVALID (k_q, k_kv < 1 or k_q k_kv > MA_GOO_MAX_COMPUTE, a
+ * communication time <= 0, a compute time or gamma < 0 or not finite, null
+ * pointers, max_steps too small).  No allocation; t_c and steps are host arrays.
+ * --------------------------------------------------------------------------- */
+#define MA_GOO_MAX_COMPUTE 16
+#define MA_GOO_NONE 0   /* compute-only step */
+#define MA_GOO_AG_Q 1
+#define MA_GOO_AG_KV 2
+#define MA_GOO_RS_Q 3
+
+typedef struct {
+  int32_t comm_type;   /* MA_GOO_* */
+  int32_t comm_index;  /* chunk index of the communication task (0 in a compute-only step) */
+  int32_t ncompute;    /* compute tasks in the step */
+  int32_t compute[MA_GOO_MAX_COMPUTE];  /* C-i-j written as i * k_kv + j, in the order taken */
+} ma_goo_step;
+
+int32_t mesh_attn_goo_plan(int32_t k_q, int32_t k_kv, double t_ag_q, double t_ag_kv, double t_rs_q,
+                           const double* t_c, double gamma, int32_t max_steps, ma_goo_step* steps);
+
 /* diagnostics */
 const char* mesh_attn_last_error(void);
 int mesh_attn_version(void);
