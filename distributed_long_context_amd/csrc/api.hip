@@ -411,7 +411,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
     if (a->mask_mode != MA_MASK_NONE) to_kpos(t.q_pos, q.qp);
     else q.qp.nseg = 1;
     BwdPreParams pp;
-    pp.batch = a->batch; pp.hq = a->hq; pp.sq = (int32_t)t.sq;
+    pp.batch = a->batch; pp.hq = a->hq; pp.sq = (int32_t)t.sq; pp.scale = a->scale;
     pp.o = t.o; pp.dout = t.dout; pp.lse = t.lse; pp.lsed = (float*)((char*)workspace + off);
     pp.q_sb = a->q_stride[0]; pp.q_ss = a->q_stride[1]; pp.q_sh = a->q_stride[2];
     pp.l_sb = a->lse_stride[0]; pp.l_sh = a->lse_stride[1];

@@ -71,8 +71,11 @@ __device__ __forceinline__ int kv_first_at(int i) { return kernarg_byte(offsetof
 
 // ---------------------------------------------------------------- preprocess --
 // One thread per 8 elements of a row; rows are (b, 64-row block, t%64, h) so that
-// a block of threads reads contiguous O/dO bytes.  Rows past sq in the last block
-// get LSE2 = +inf and D = 0.
+// a block of threads reads contiguous O/dO bytes.  Stored per row: -LSE/scale and
+// -D.  With them a score accumulator that starts at -LSE/scale ends at
+// S - LSE/scale, so P = exp2(scale*log2(e) * acc), and a dP accumulator that
+// starts at -D ends at dP - D, the factor of dS.  Rows without an allowed key and
+// rows past sq in the last block get -inf (P = 0) and 0.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdPreParams p) {
   constexpr int TPR = D / 8;
@@ -101,14 +104,14 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdPreParams p) {
 #pragma unroll
   for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
   if ((threadIdx.x % TPR) == 0) {
-    float l2 = INFINITY;
+    float nl = -INFINITY;
     if (ok) {
       const float L = p.lse[b * p.l_sb + (int64_t)h * p.l_sh + t];
-      l2 = (L == -INFINITY) ? INFINITY : L * 1.4426950408889634f;
+      nl = (L == -INFINITY) ? -INFINITY : -L / p.scale;
     }
     float* blk = p.lsed + ((b * p.hq + h) * nqb + t / kBN) * (2 * kBN);
-    blk[t % kBN] = l2;
-    blk[kBN + t % kBN] = ok ? acc : 0.f;
+    blk[t % kBN] = nl;
+    blk[kBN + t % kBN] = ok ? -acc : 0.f;
   }
 }
 
@@ -189,7 +192,7 @@ bwd_dq_kernel(const BwdParams p) {
 
   // ---- Q and dO fragments (B operands), LSE2 and D of this lane's query ----
   bf16x8 qf[C::KS], gf[C::KS];
-  float lse2 = INFINITY, dd = 0.f;
+  float nl2 = -INFINITY, nd = 0.f;  // -LSE*log2(e) and -D of this lane's query
   int qpos = INT32_MIN;
   const int row = q0 + l32;
   const bool row_ok = active && row < QP.sq;
@@ -206,8 +209,8 @@ bwd_dq_kernel(const BwdParams p) {
     if (row_ok) {
       const int nqb64 = (QP.sq + kBN - 1) / kBN;
       const float* blk = QP.lsed + (((int64_t)b * p.hq + my_head) * nqb64 + row / kBN) * (2 * kBN);
-      lse2 = blk[row % kBN];
-      dd = blk[kBN + row % kBN];
+      nl2 = blk[row % kBN] * p.scale_log2;
+      nd = blk[kBN + row % kBN];
       if constexpr (MASKED) qpos = pos_at_dev(QP.qp, row);
     }
   }
@@ -329,8 +332,8 @@ bwd_dq_kernel(const BwdParams p) {
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j * 8 + i], c2, -lse2));
-        v[i] = pe * (dc[j * 8 + i] - dd);
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j * 8 + i], c2, nl2));
+        v[i] = pe * (dc[j * 8 + i] + nd);
       }
       dsf[j] = pack_bf16x8(v);
     }
@@ -552,11 +555,20 @@ bwd_dkv_kernel(const BwdParams p) {
   }
   const float c2 = p.scale_log2;
 
-  // S and dP of one 32-query half (u) of the block in stage st
+  // S - LSE/scale and dP - D of one 32-query half (u) of the block in stage st:
+  // the accumulators start at the row values of the LSE2/D block
   auto sdp_half = [&](int st, int u, f32x16& s, f32x16& dp) {
     const uint32_t off = st * C::STAGE_BYTES + u * 32 * D * 2;
-    s = f32x16{};
-    dp = f32x16{};
+    const uint32_t lo = laddr + st * kLdStage + u * 32 * 4;
+    const f32x4 l0 = lds_read_f32x4(lo), l1 = lds_read_f32x4(lo + 16);
+    const f32x4 l2 = lds_read_f32x4(lo + 64), l3 = lds_read_f32x4(lo + 80);
+    const f32x4 d0 = lds_read_f32x4(lo + 256), d1 = lds_read_f32x4(lo + 272);
+    const f32x4 d2 = lds_read_f32x4(lo + 320), d3 = lds_read_f32x4(lo + 336);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = l0[i]; s[4 + i] = l1[i]; s[8 + i] = l2[i]; s[12 + i] = l3[i];
+      dp[i] = d0[i]; dp[4 + i] = d1[i]; dp[8 + i] = d2[i]; dp[12 + i] = d3[i];
+    }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const bf16x8 qa = lds_read_b128(qaddr[ks] + off);
@@ -576,18 +588,9 @@ bwd_dkv_kernel(const BwdParams p) {
     // one wave per SIMD: ask the scheduler to interleave the LDS reads with the
     // MFMAs (measured: 14% faster than the default schedule for this kernel)
     __builtin_amdgcn_iglp_opt(0);
-    const uint32_t lo = laddr + st * kLdStage + u * 32 * 4;
-    const f32x4 l0 = lds_read_f32x4(lo), l1 = lds_read_f32x4(lo + 16);
-    const f32x4 l2 = lds_read_f32x4(lo + 64), l3 = lds_read_f32x4(lo + 80);
-    const f32x4 d0 = lds_read_f32x4(lo + 256), d1 = lds_read_f32x4(lo + 272);
-    const f32x4 d2 = lds_read_f32x4(lo + 320), d3 = lds_read_f32x4(lo + 336);
-    const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
-                          l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
-    const float dv[16] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
-                          d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
     float pe[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c2, -lv[e]));
+    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(sc[e] * c2);
     if constexpr (decltype(masked)::value) {
       int pi, hi, qb;
       decode(g, pi, hi, qb);
@@ -603,7 +606,7 @@ bwd_dkv_kernel(const BwdParams p) {
     for (int j = 0; j < 2; ++j) {
       float ds[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ds[i] = pe[j * 8 + i] * (dc[j * 8 + i] - dv[j * 8 + i]);
+      for (int i = 0; i < 8; ++i) ds[i] = pe[j * 8 + i] * dc[j * 8 + i];
       pf[j] = pack_bf16x8(&pe[j * 8]);
       dsf[j] = pack_bf16x8(ds);
     }

@@ -68,10 +68,11 @@ extern "C" int32_t mesh_attn_goo_plan(int32_t kq, int32_t kkv, double t_agq, dou
       const double p = 0.0;  // an output reduce-scatter makes no compute ready
       if (p > best) { best = p; type = MA_GOO_RS_Q; index = ir; }
     }
+    if (type == MA_GOO_NONE && !avail) break;  // nothing left
+    if (ns >= max_steps) return -set_error(MA_ERR_INVALID, "goo_plan: internal step count exceeded");
     ma_goo_step& st = steps[ns];
     std::memset(&st, 0, sizeof(st));
     if (type == MA_GOO_NONE) {
-      if (!avail) break;  // nothing left
       int c = 0;
       while (!(avail >> c & 1u)) ++c;
       st.ncompute = 1;

@@ -139,6 +139,7 @@ struct BwdParams {
 // partition, in the blocked layout the main kernels stage into LDS.
 struct BwdPreParams {
   int32_t batch, hq, sq;
+  float scale;
   const void* o;
   const void* dout;
   const float* lse;

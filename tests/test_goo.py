@@ -110,3 +110,19 @@ def test_library_planner_rejects_bad_arguments():
             ma.mesh_attn_goo_plan(args[0], args[1], 1.0, 1.0, 1.0, 1.0, 1.0)
     with pytest.raises(ma.MeshAttnError):
         ma.mesh_attn_goo_plan(2, 2, 0.0, 1.0, 1.0, 1.0, 1.0)  # a communication time must be > 0
+
+
+def test_library_planner_fills_its_step_array_exactly():
+    # k_Q = k_KV = 1: AG-KV-0, AG-Q-0, a compute-only step, RS-Q-0 -- as many steps as the bound
+    # 2 k_Q + k_KV + k_Q k_KV, so the planner must not touch the array past them
+    import distributed_long_context_amd as ma
+    import ctypes as C
+    from distributed_long_context_amd import _abi
+    steps = (_abi.ma_goo_step * 5)()
+    for s in steps:
+        s.comm_type = 77
+    tc = (C.c_double * 1)(0.5)
+    r = ma.lib().mesh_attn_goo_plan(1, 1, 0.5, 1.0, 0.5, tc, 1.0, 4, steps)
+    assert r == 4
+    assert steps[4].comm_type == 77  # the slot after the last step is untouched
+    assert [s.comm_type for s in steps[:4]] == [2, 1, 0, 3]
