@@ -279,6 +279,55 @@ bwd_dq_kernel(const BwdParams p) {
       }
     }
   };
+  // Without position masks every block is visited in order: a cursor (partner,
+  // block) and the current partner's bases replace the per-block decode; issue_at
+  // returns the block's valid key count for the tail mask.
+  int c_pi = 0, c_kb = 0, c_nkb = 0, c_sk = 0;
+  const __bf16* c_k = nullptr;
+  const __bf16* c_v = nullptr;
+  auto cur_load = [&]() {
+    const BwdKVPart KV = kvpart_at(partner_at(ei, c_pi));
+    c_sk = KV.sk;
+    c_nkb = (KV.sk + kBN - 1) / kBN;
+    const int64_t off = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+    c_k = (const __bf16*)KV.k + off;
+    c_v = (const __bf16*)KV.v + off;
+  };
+  auto issue_next = [&](int st) -> int {
+    const int64_t roff = (int64_t)c_kb * kBN * p.k_ss;
+    const __bf16* kbase = c_k + roff;
+    const __bf16* vbase = c_v + roff;
+    const int valid = c_sk - c_kb * kBN;
+    if (valid >= kBN) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        lds_dma16(kbase, go[i], lds_addr(&kv_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(vbase, go[i], lds_addr(&kv_s[1][st][(wave * LPW + i) * 512]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const uint32_t o2 = (uint32_t)(min(load_row(i), valid - 1) * k_ss + load_col(i)) * 2u;
+        lds_dma16(kbase, o2, lds_addr(&kv_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(vbase, o2, lds_addr(&kv_s[1][st][(wave * LPW + i) * 512]));
+      }
+    }
+    if (++c_kb == c_nkb) {
+      c_kb = 0;
+      ++c_pi;
+      if (c_pi < E.n) cur_load();
+    }
+    return valid;
+  };
+  auto issue_at = [&](int st, int g) -> int {
+    if constexpr (MASKED) {
+      issue(st, g);
+      return kBN;
+    } else {
+      return issue_next(st);
+    }
+  };
+  if constexpr (!MASKED) cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
@@ -307,8 +356,19 @@ bwd_dq_kernel(const BwdParams p) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[ks], dp, 0, 0, 0);
     }
   };
-  // mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8
-  auto mask_half = [&](int g, int kb2, f32x16& s) {
+  // mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8.  Without
+  // position masks only the keys past a partition's end are masked: nv is the
+  // number of valid keys of the block (64 or more: none masked; 0 past the end).
+  auto mask_half = [&](int g, int nv, int kb2, f32x16& s) {
+    if constexpr (!MASKED) {
+      if (nv >= kBN) return;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
+        s[e] = kk < nv ? s[e] : -INFINITY;
+      }
+      return;
+    }
     const int cls = active ? block_class(g, w_pmin, w_pmax) : 1;
     if (cls == 2) return;
     int pi, kb;
@@ -325,7 +385,8 @@ bwd_dq_kernel(const BwdParams p) {
   };
   // one 32-key step: P, dS of the current half; S^T, dP^T of the next half under
   // the exponentials; dQ^T += K^T dS^T; mask of the next half
-  auto half_step = [&](int st, int kb2, f32x16& sc, f32x16& dc, int ng, int nst, int nkb2, f32x16& sn, f32x16& dn) {
+  auto half_step = [&](int st, int kb2, f32x16& sc, f32x16& dc, int ng, int nv, int nst, int nkb2, f32x16& sn,
+                       f32x16& dn) {
     bf16x8 dsf[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -347,34 +408,39 @@ bwd_dq_kernel(const BwdParams p) {
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[j], acc[c], 0, 0, 0);
       }
     }
-    mask_half(ng, nkb2, sn);
+    mask_half(ng, nv, nkb2, sn);
   };
 
   // ---- pipeline (the forward's): position j in stage j % 4, loaded 2 ahead ----
   int bj0 = next_block(0);
   int bj1 = bj0 < total ? next_block(bj0 + 1) : total;
   int bj2 = bj1 < total ? next_block(bj1 + 1) : total;
-  if (bj0 < total) issue(0, bj0);
-  if (bj1 < total) issue(1, bj1);
-  if (bj2 < total) issue(2, bj2);
+  // nv0..nv2: valid key counts of positions bj0..bj2 (0 when past the end)
+  int nv0 = 0, nv1 = 0, nv2 = 0;
+  if (bj0 < total) nv0 = issue_at(0, bj0);
+  if (bj1 < total) nv1 = issue_at(1, bj1);
+  if (bj2 < total) nv2 = issue_at(2, bj2);
   f32x16 sA, dA, sB, dB;
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // also retires the fragment loads
   if (bj0 < total) {
     __syncthreads();
     sdp_half(0, 0, sA, dA);
-    mask_half(bj0, 0, sA);
+    mask_half(bj0, nv0, 0, sA);
   }
 #define MA_DQ_BLOCK(ST)                                                  \
   {                                                                      \
-    half_step((ST), 0, sA, dA, bj0, (ST), 1, sB, dB);                    \
+    half_step((ST), 0, sA, dA, bj0, nv0, (ST), 1, sB, dB);               \
     const int bj3 = bj2 < total ? next_block(bj2 + 1) : total;           \
     wait_positions(bj2 < total ? 1 : 0);                                 \
     __syncthreads();                                                     \
-    if (bj3 < total) issue(((ST) + 3) & 3, bj3);                         \
-    half_step((ST), 1, sB, dB, bj1, ((ST) + 1) & 3, 0, sA, dA);          \
+    const int nv3 = bj3 < total ? issue_at(((ST) + 3) & 3, bj3) : 0;     \
+    half_step((ST), 1, sB, dB, bj1, nv1, ((ST) + 1) & 3, 0, sA, dA);     \
     bj0 = bj1;                                                           \
     bj1 = bj2;                                                           \
     bj2 = bj3;                                                           \
+    nv0 = nv1;                                                           \
+    nv1 = nv2;                                                           \
+    nv2 = nv3;                                                           \
     if (bj0 >= total) break;                                             \
   }
   while (bj0 < total) {
@@ -535,6 +601,59 @@ bwd_dkv_kernel(const BwdParams p) {
     const float* lblk = QP.lsed + (((int64_t)b * p.hq + h) * nqb64 + qb) * (2 * kBN);
     if (lane < 8) lds_dma16(lblk, (uint32_t)(wave * 128 + lane * 16), lds_addr(&ld_s[st][wave * 32]));
   };
+  // Without position masks every block is visited in order, so the walk keeps a
+  // cursor (partner, head, 64-row block) and the bases of the current (partner,
+  // head), refreshed only when those change: no decode, division or parameter
+  // load per block (a scalar load would also make the wave wait for all of its
+  // LDS reads).
+  int c_pi = 0, c_hi = 0, c_qb = 0, c_nqb = 0, c_sq = 0;
+  const __bf16* c_q = nullptr;
+  const __bf16* c_g = nullptr;
+  const float* c_l = nullptr;
+  auto cur_load = [&]() {
+    const BwdQPart QP = qpart_at(partner_at(ei, c_pi));
+    c_sq = QP.sq;
+    c_nqb = (QP.sq + kBN - 1) / kBN;
+    const int h = head_of(g0 + c_hi);
+    const int64_t off = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+    c_q = (const __bf16*)QP.q + off;
+    c_g = (const __bf16*)QP.dout + off;
+    c_l = QP.lsed + ((int64_t)b * p.hq + h) * c_nqb * (2 * kBN);
+  };
+  auto issue_next = [&](int st) {
+    const int64_t roff = (int64_t)c_qb * kBN * p.q_ss;
+    const __bf16* qbase = c_q + roff;
+    const __bf16* gbase = c_g + roff;
+    const int valid = c_sq - c_qb * kBN;
+    if (valid >= kBN) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        lds_dma16(qbase, go[i], lds_addr(&qd_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(gbase, go[i], lds_addr(&qd_s[1][st][(wave * LPW + i) * 512]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const uint32_t o2 = (uint32_t)(min(load_row(i), valid - 1) * q_ss + load_col(i)) * 2u;
+        lds_dma16(qbase, o2, lds_addr(&qd_s[0][st][(wave * LPW + i) * 512]));
+        lds_dma16(gbase, o2, lds_addr(&qd_s[1][st][(wave * LPW + i) * 512]));
+      }
+    }
+    if (lane < 8) lds_dma16(c_l + c_qb * (2 * kBN), (uint32_t)(wave * 128 + lane * 16), lds_addr(&ld_s[st][wave * 32]));
+    if (++c_qb == c_nqb) {
+      c_qb = 0;
+      if (++c_hi == gsz) {
+        c_hi = 0;
+        ++c_pi;
+      }
+      if (c_pi < E.n) cur_load();
+    }
+  };
+  auto issue_at = [&](int st, int g) {
+    if constexpr (MASKED) issue(st, g);
+    else issue_next(st);
+  };
+  if constexpr (!MASKED) cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (2 * LPW + 1)));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW + 1));
@@ -636,9 +755,9 @@ bwd_dkv_kernel(const BwdParams p) {
   int bj0 = next_block(0);
   int bj1 = bj0 < total ? next_block(bj0 + 1) : total;
   int bj2 = bj1 < total ? next_block(bj1 + 1) : total;
-  if (bj0 < total) issue(0, bj0);
-  if (bj1 < total) issue(1, bj1);
-  if (bj2 < total) issue(2, bj2);
+  if (bj0 < total) issue_at(0, bj0);
+  if (bj1 < total) issue_at(1, bj1);
+  if (bj2 < total) issue_at(2, bj2);
   f32x16 sA, dA, sB, dB;
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // also retires the fragment loads
   if (bj0 < total) {
@@ -651,7 +770,7 @@ bwd_dkv_kernel(const BwdParams p) {
     const int bj3 = bj2 < total ? next_block(bj2 + 1) : total;           \
     wait_positions(bj2 < total ? 1 : 0);                                 \
     __syncthreads();                                                     \
-    if (bj3 < total) issue(((ST) + 3) & 3, bj3);                         \
+    if (bj3 < total) issue_at(((ST) + 3) & 3, bj3);                      \
     half_step(bj0, (ST), 1, sB, dB, ((ST) + 1) & 3, 0, sA, dA);          \
     bj0 = bj1;                                                           \
     bj1 = bj2;                                                           \
