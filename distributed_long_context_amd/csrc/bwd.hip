@@ -361,7 +361,7 @@ bwd_dq_kernel(const BwdParams p) {
   // number of valid keys of the block (64 or more: none masked; 0 past the end).
   auto mask_half = [&](int g, int nv, int kb2, f32x16& s) {
     if constexpr (!MASKED) {
-      if (nv >= kBN) return;
+      if (__builtin_expect(__builtin_amdgcn_readfirstlane(nv) >= kBN, 1)) return;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
