@@ -486,28 +486,32 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
-    merge_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
-    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / len(evs)
+    def mean_median(i):
+        ts = sorted(e[i].elapsed_time(e[i + 1]) for e in evs)
+        mid = len(ts) // 2
+        return sum(ts) / len(ts), (ts[mid] if len(ts) % 2 else 0.5 * (ts[mid - 1] + ts[mid]))
+
+    (fwd_ms, fwd_med), (merge_ms, merge_med), (bwd_ms, bwd_med) = mean_median(0), mean_median(1), mean_median(2)
     step_flop = (fwd_flop if "fwd" in parts else 0) + (bwd_flop if "bwd" in parts else 0)
     value = step_flop / (ms_step * 1e-3) / 1e12
 
     res_parts = {}
     if "fwd" in parts:
         t = fwd_flop / (fwd_ms * 1e-3) / 1e12
-        res_parts["tile_fwd"] = {"ms": round(fwd_ms, 4), "TFLOP/s": round(t, 1), "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4),
-                                 "flop": fwd_flop}
+        res_parts["tile_fwd"] = {"ms": round(fwd_ms, 4), "ms_median": round(fwd_med, 4), "TFLOP/s": round(t, 1),
+                                 "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4), "flop": fwd_flop}
     if "merge" in parts:
         g = merge_bytes / (merge_ms * 1e-3) / 1e9
-        res_parts["merge"] = {"ms": round(merge_ms, 4), "GB/s": round(g, 1), "frac_hbm_peak": round(g / PEAK_HBM_GBPS, 4),
-                              "bytes": merge_bytes, "k": 2}
+        res_parts["merge"] = {"ms": round(merge_ms, 4), "ms_median": round(merge_med, 4), "GB/s": round(g, 1),
+                              "frac_hbm_peak": round(g / PEAK_HBM_GBPS, 4), "bytes": merge_bytes, "k": 2}
         gc = merge_bytes / (merge_cold_ms * 1e-3) / 1e9
         res_parts["merge_mall_flushed"] = {"ms": round(merge_cold_ms, 4), "GB/s": round(gc, 1),
                                            "frac_hbm_peak": round(gc / PEAK_HBM_GBPS, 4), "bytes": merge_bytes, "k": 2}
     if "bwd" in parts:
         t = bwd_flop / (bwd_ms * 1e-3) / 1e12
-        res_parts["tile_bwd"] = {"ms": round(bwd_ms, 4), "TFLOP/s": round(t, 1), "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4),
-                                 "flop": bwd_flop, "includes": "D=rowsum(dO*O) preprocessing"}
+        res_parts["tile_bwd"] = {"ms": round(bwd_ms, 4), "ms_median": round(bwd_med, 4), "TFLOP/s": round(t, 1),
+                                 "frac_bf16_peak": round(t / PEAK_BF16_TFLOPS, 4), "flop": bwd_flop,
+                                 "includes": "D=rowsum(dO*O) preprocessing"}
     # dominant kernel by time
     dom = max(((n, p["ms"]) for n, p in res_parts.items() if n != "merge_mall_flushed"), key=lambda x: x[1])[0]
     if dom == "merge":
