@@ -17,10 +17,11 @@
 // taken in groups of G (2, 4 or 8, the smallest that covers k up to 8) whose
 // loads are all issued before any use: indices past k repeat the last partial
 // (a valid address) and get weight 0, so there are no branches between the
-// loads.  The partial outputs are read once, so their loads are marked
-// nontemporal (streaming): with the MALL flushed before each merge that took
-// the 2-way merge of 8192 rows x 32 heads from 3.1 to 5.0 TB/s and the 27-way
-// merge of 4096 x 32 from 3.8 to 4.5 TB/s on MI355X.
+// loads.  The partial outputs are read once and the merged output is not read
+// again by this kernel, so loads and stores are marked nontemporal (streaming):
+// with the MALL flushed before each merge that took the 2-way merge of 8192
+// rows x 32 heads from 3.1 to 5.4 TB/s and the 27-way merge of 4096 x 32 from
+// 3.8 to 4.7 TB/s on MI355X (the 8-way merges of 16384 x 32 stay near 5.0).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -104,8 +105,13 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeParams p) {
     for (int e = 0; e < NE; ++e) acc[e] *= inv;
     // every lane of this row has read all partials (same wave) before the row's
     // first lane writes, so o_out == o_in[0] and lse_out == lse_in[0] are safe
-    if (BF16) *(bf16x8*)((__bf16*)p.o_out + off) = pack_bf16x8(acc);
-    else *(float4*)((float*)p.o_out + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    if (BF16) {
+      const bf16x8 pk = pack_bf16x8(acc);
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pk), (u32x4*)((__bf16*)p.o_out + off));
+    } else {
+      const u32x4 v = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+      __builtin_nontemporal_store(v, (u32x4*)((float*)p.o_out + off));
+    }
     if (c == 0) p.lse_out[lbase + t] = has ? m + __logf(s) : -INFINITY;
   }
 }
