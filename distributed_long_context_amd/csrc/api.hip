@@ -445,7 +445,8 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
   for (int side = 0; side < 2; ++side) {
     const bool dq_side = side == 0;
     const auto& own = dq_side ? grp.qg : grp.kvg;
-    struct Piece { int group; std::vector<int> partners; int accumulate; bool masked; };
+    // kind 0: unmasked; 1: masked, every partner's positions one segment; 2: masked, any positions
+    struct Piece { int group; std::vector<int> partners; int accumulate; int kind; };
     std::vector<Piece> pieces;
     for (int gi = 0; gi < (int)own.size(); ++gi) {
       std::vector<int> full, other;  // partner groups of FULL pairs; of PARTIAL or EMPTY pairs
@@ -462,7 +463,15 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
           pc.group = gi;
           pc.partners.assign(lst.begin() + s0, lst.begin() + std::min(lst.size(), s0 + kBwdPerLaunch));
           pc.accumulate = first ? (a->accumulate ? 1 : 0) : 1;
-          pc.masked = kind == 1;
+          pc.kind = 0;
+          if (kind == 1) {
+            pc.kind = 1;
+            for (int pg : pc.partners) {
+              // the partners' positions: KV partitions on the dQ side, Q partitions on the dK/dV side
+              const ma_bwd_tile& pt = a->tiles[dq_side ? grp.kvg[pg][0] : grp.qg[pg][0]];
+              if ((dq_side ? pt.k_pos.nseg : pt.q_pos.nseg) != 1) pc.kind = 2;
+            }
+          }
           first = false;
           pieces.push_back(pc);
         }
@@ -483,7 +492,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
         for (size_t pj = 0; pj < pi; ++pj)
           if (!done[pj] && pieces[pj].group == pc.group) earlier_pending = true;
         if (earlier_pending) continue;
-        if (kind >= 0 && kind != (pc.masked ? 1 : 0)) continue;
+        if (kind >= 0 && kind != pc.kind) continue;
         std::vector<int> new_part = part_tab;
         for (int x : pc.partners)
           if (std::find(new_part.begin(), new_part.end(), x) == new_part.end()) new_part.push_back(x);
@@ -492,7 +501,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
         part_tab = new_part;
         if (own_new) own_tab.push_back(pc.group);
         groups_in.push_back(pc.group);
-        kind = pc.masked ? 1 : 0;
+        kind = pc.kind;
         BwdEntry& en = p.entries[ne];
         en.self = (int32_t)(std::find(own_tab.begin(), own_tab.end(), pc.group) - own_tab.begin());
         en.n = (int32_t)pc.partners.size();
@@ -516,7 +525,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
         --remaining;
       }
       p.nentries = ne;
-      p.mask = kind == 1 ? 1 : 0;
+      p.mask = kind;
       for (size_t i = 0; i < own_tab.size(); ++i) {
         if (dq_side) p.qparts[i] = qparts[own_tab[i]];
         else p.kvparts[i] = kvparts[own_tab[i]];

@@ -115,6 +115,13 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdPreParams p) {
   }
 }
 
+// mask of a block on an in-order walk: whole (uniform), else the lane's last
+// allowed row or key index relative to the block start
+struct BlkMask {
+  int whole;
+  int lim;
+};
+
 // ------------------------------------------------------ walks over partners --
 // Blocks of an entry's partners, flattened: position g -> (partner index, block).
 struct PartnerWalk {
@@ -136,11 +143,18 @@ struct PartnerWalk {
 };
 
 // ---------------------------------------------------------------- dQ kernel --
-template <int D, bool MASKED>
+// MODE 0: no position mask.  MODE 1: the key positions of every KV partition are
+// one segment (they grow with the key index), so a lane's mask is the index of
+// its last allowed key and the blocks with any allowed pair for the workgroup are
+// a prefix of each partition.  MODE 2: any position maps.
+template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(const BwdParams p) {
   using C = Cfg<D>;
+  constexpr bool MASKED = MODE != 0;
+  constexpr bool SEG1 = MODE == 1;
+  constexpr bool WALK = MODE != 2;  // blocks visited in order with a cursor
   constexpr int kWaves = 8, kQW = 32;
   constexpr int LPW = kBN * C::CH / 64 / kWaves;  // direct-to-LDS loads per wave per tensor
   // K stages, then V stages
@@ -216,13 +230,22 @@ bwd_dq_kernel(const BwdParams p) {
   }
 
   // ---- key blocks of every KV partition of the group ----
+  // one key segment: the last key index allowed at query position pq (-1: none)
+  auto last_key = [&](const BwdKVPart& KV, int pq) {
+    const int gb = KV.kp.gb[0], st = KV.kp.st[0];
+    return pq < gb ? -1 : min(KV.sk - 1, (pq - gb) / st);
+  };
+  auto part_blocks = [&](const BwdKVPart& KV) {
+    if constexpr (SEG1) return (last_key(KV, wg_pmax) + kBN) / kBN;
+    else return (KV.sk + kBN - 1) / kBN;
+  };
   PartnerWalk walk;
   walk.n = E.n;
   int total = 0;
 #pragma unroll
   for (int i = 0; i < kBwdPerLaunch; ++i) {
     walk.pre[i] = total;
-    total += i < E.n ? (kvpart_at(partner_at(ei, i)).sk + kBN - 1) / kBN : 0;
+    total += i < E.n ? part_blocks(kvpart_at(partner_at(ei, i))) : 0;
   }
   auto block_class = [&](int g, int pmin, int pmax) -> int {  // 0 empty, 1 partial, 2 full
     int pi, kb;
@@ -240,7 +263,7 @@ bwd_dq_kernel(const BwdParams p) {
     }
   };
   auto next_block = [&](int from) -> int {
-    if constexpr (!MASKED) {
+    if constexpr (WALK) {
       return from < total ? from : total;
     } else {
       for (int g = from; g < total; ++g)
@@ -279,21 +302,30 @@ bwd_dq_kernel(const BwdParams p) {
       }
     }
   };
-  // Without position masks every block is visited in order: a cursor (partner,
-  // block) and the current partner's bases replace the per-block decode; issue_at
-  // returns the block's valid key count for the tail mask.
-  int c_pi = 0, c_kb = 0, c_nkb = 0, c_sk = 0;
+  // On the walk (no position masks, or one key segment per partition) the blocks
+  // are visited in order: a cursor (partner, block) and the current partner's
+  // bases and mask data replace the per-block decode; issue_at returns the mask of
+  // the block it loads.
+  int c_pi = 0, c_kb = 0, c_nkb = 0, c_sk = 0, c_kfull = 0, c_klast = 0;
   const __bf16* c_k = nullptr;
   const __bf16* c_v = nullptr;
   auto cur_load = [&]() {
-    const BwdKVPart KV = kvpart_at(partner_at(ei, c_pi));
-    c_sk = KV.sk;
-    c_nkb = (KV.sk + kBN - 1) / kBN;
-    const int64_t off = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-    c_k = (const __bf16*)KV.k + off;
-    c_v = (const __bf16*)KV.v + off;
+    for (;;) {
+      const BwdKVPart KV = kvpart_at(partner_at(ei, c_pi));
+      c_sk = KV.sk;
+      c_nkb = part_blocks(KV);
+      const int64_t off = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+      c_k = (const __bf16*)KV.k + off;
+      c_v = (const __bf16*)KV.v + off;
+      if constexpr (SEG1) {
+        c_klast = last_key(KV, qpos);
+        c_kfull = active ? (last_key(KV, w_pmin) + 1) / kBN : 0;
+      }
+      if (c_nkb > 0 || c_pi + 1 >= E.n) break;
+      ++c_pi;  // no allowed pair with this partition
+    }
   };
-  auto issue_next = [&](int st) -> int {
+  auto issue_next = [&](int st) -> BlkMask {
     const int64_t roff = (int64_t)c_kb * kBN * p.k_ss;
     const __bf16* kbase = c_k + roff;
     const __bf16* vbase = c_v + roff;
@@ -312,22 +344,30 @@ bwd_dq_kernel(const BwdParams p) {
         lds_dma16(vbase, o2, lds_addr(&kv_s[1][st][(wave * LPW + i) * 512]));
       }
     }
+    BlkMask bm;
+    if constexpr (SEG1) {
+      bm.whole = c_kb < c_kfull;
+      bm.lim = c_klast - c_kb * kBN;
+    } else {
+      bm.whole = valid >= kBN;
+      bm.lim = valid - 1;
+    }
     if (++c_kb == c_nkb) {
       c_kb = 0;
       ++c_pi;
       if (c_pi < E.n) cur_load();
     }
-    return valid;
+    return bm;
   };
-  auto issue_at = [&](int st, int g) -> int {
-    if constexpr (MASKED) {
-      issue(st, g);
-      return kBN;
-    } else {
+  auto issue_at = [&](int st, int g) -> BlkMask {
+    if constexpr (WALK) {
       return issue_next(st);
+    } else {
+      issue(st, g);
+      return BlkMask{1, kBN - 1};
     }
   };
-  if constexpr (!MASKED) cur_load();
+  if constexpr (WALK) cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
@@ -356,16 +396,17 @@ bwd_dq_kernel(const BwdParams p) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[ks], dp, 0, 0, 0);
     }
   };
-  // mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8.  Without
-  // position masks only the keys past a partition's end are masked: nv is the
-  // number of valid keys of the block (64 or more: none masked; 0 past the end).
-  auto mask_half = [&](int g, int nv, int kb2, f32x16& s) {
-    if constexpr (!MASKED) {
-      if (__builtin_expect(__builtin_amdgcn_readfirstlane(nv) >= kBN, 1)) return;
+  // mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8.  On the
+  // walk the block carries its mask: whole (no key masked), or the lane's last
+  // allowed key index within the block (keys past a partition's end included;
+  // -1 past the end of the walk: every key masked).
+  auto mask_half = [&](int g, const BlkMask& bm, int kb2, f32x16& s) {
+    if constexpr (WALK) {
+      if (__builtin_expect(bm.whole, 1)) return;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-        s[e] = kk < nv ? s[e] : -INFINITY;
+        s[e] = kk <= bm.lim ? s[e] : -INFINITY;
       }
       return;
     }
@@ -385,8 +426,8 @@ bwd_dq_kernel(const BwdParams p) {
   };
   // one 32-key step: P, dS of the current half; S^T, dP^T of the next half under
   // the exponentials; dQ^T += K^T dS^T; mask of the next half
-  auto half_step = [&](int st, int kb2, f32x16& sc, f32x16& dc, int ng, int nv, int nst, int nkb2, f32x16& sn,
-                       f32x16& dn) {
+  auto half_step = [&](int st, int kb2, f32x16& sc, f32x16& dc, int ng, const BlkMask& nv, int nst, int nkb2,
+                       f32x16& sn, f32x16& dn) {
     bf16x8 dsf[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -415,8 +456,8 @@ bwd_dq_kernel(const BwdParams p) {
   int bj0 = next_block(0);
   int bj1 = bj0 < total ? next_block(bj0 + 1) : total;
   int bj2 = bj1 < total ? next_block(bj1 + 1) : total;
-  // nv0..nv2: valid key counts of positions bj0..bj2 (0 when past the end)
-  int nv0 = 0, nv1 = 0, nv2 = 0;
+  // nv0..nv2: masks of positions bj0..bj2 (every key masked when past the end)
+  BlkMask nv0{0, -1}, nv1{0, -1}, nv2{0, -1};
   if (bj0 < total) nv0 = issue_at(0, bj0);
   if (bj1 < total) nv1 = issue_at(1, bj1);
   if (bj2 < total) nv2 = issue_at(2, bj2);
@@ -433,7 +474,7 @@ bwd_dq_kernel(const BwdParams p) {
     const int bj3 = bj2 < total ? next_block(bj2 + 1) : total;           \
     wait_positions(bj2 < total ? 1 : 0);                                 \
     __syncthreads();                                                     \
-    const int nv3 = bj3 < total ? issue_at(((ST) + 3) & 3, bj3) : 0;     \
+    const BlkMask nv3 = bj3 < total ? issue_at(((ST) + 3) & 3, bj3) : BlkMask{0, -1}; \
     half_step((ST), 1, sB, dB, bj1, nv1, ((ST) + 1) & 3, 0, sA, dA);     \
     bj0 = bj1;                                                           \
     bj1 = bj2;                                                           \
@@ -469,11 +510,18 @@ bwd_dq_kernel(const BwdParams p) {
 }
 
 // --------------------------------------------------------------- dK/dV kernel --
-template <int D, bool MASKED>
+// MODE 0: no position mask.  MODE 1: the query positions of every Q partition
+// are one segment (they grow with the row index), so a lane's mask is the index
+// of the first row allowed to see its key and the blocks with any allowed pair
+// for the workgroup are a suffix of each (partition, head).  MODE 2: any maps.
+template <int D, int MODE>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkv_kernel(const BwdParams p) {
   using C = Cfg<D>;
+  constexpr bool MASKED = MODE != 0;
+  constexpr bool SEG1 = MODE == 1;
+  constexpr bool WALK = MODE != 2;
   constexpr int kWaves = 4, kKW = 32;
   constexpr int LPW = kBN * C::CH / 64 / kWaves;
   // Q stages, then dO stages; LSE2/D blocks
@@ -527,13 +575,27 @@ bwd_dkv_kernel(const BwdParams p) {
   }
 
   // ---- query blocks: (Q partition, head of the group, 64-row block), flattened ----
+  // one query segment: the first row index whose position is at or after key
+  // position kp (sq: none)
+  auto first_row = [&](const BwdQPart& QP, int kp) {
+    const int gb = QP.qp.gb[0], st = QP.qp.st[0];
+    return kp <= gb ? 0 : (int)min((int64_t)QP.sq, ((int64_t)kp - gb + st - 1) / st);
+  };
+  // 64-row blocks of a partition, and the first one with any allowed pair for the workgroup
+  auto part_qb0 = [&](const BwdQPart& QP) {
+    if constexpr (SEG1) return first_row(QP, wg_kmin) / kBN;
+    else return 0;
+  };
   PartnerWalk walk;  // blocks per partner = heads x 64-row blocks
   walk.n = E.n;
   int total = 0;
 #pragma unroll
   for (int i = 0; i < kBwdPerLaunch; ++i) {
     walk.pre[i] = total;
-    total += i < E.n ? gsz * ((qpart_at(partner_at(ei, i)).sq + kBN - 1) / kBN) : 0;
+    if (i < E.n) {
+      const BwdQPart QP = qpart_at(partner_at(ei, i));
+      total += gsz * ((QP.sq + kBN - 1) / kBN - part_qb0(QP));
+    }
   }
   auto decode = [&](int g, int& pi, int& hi, int& qb) {
     int blk;
@@ -557,7 +619,7 @@ bwd_dkv_kernel(const BwdParams p) {
     }
   };
   auto next_block = [&](int from) -> int {
-    if constexpr (!MASKED) {
+    if constexpr (WALK) {
       return from < total ? from : total;
     } else {
       for (int g = from; g < total; ++g)
@@ -601,26 +663,37 @@ bwd_dkv_kernel(const BwdParams p) {
     const float* lblk = QP.lsed + (((int64_t)b * p.hq + h) * nqb64 + qb) * (2 * kBN);
     if (lane < 8) lds_dma16(lblk, (uint32_t)(wave * 128 + lane * 16), lds_addr(&ld_s[st][wave * 32]));
   };
-  // Without position masks every block is visited in order, so the walk keeps a
-  // cursor (partner, head, 64-row block) and the bases of the current (partner,
-  // head), refreshed only when those change: no decode, division or parameter
-  // load per block (a scalar load would also make the wave wait for all of its
-  // LDS reads).
-  int c_pi = 0, c_hi = 0, c_qb = 0, c_nqb = 0, c_sq = 0;
+  // On the walk (no position masks, or one query segment per partition) the
+  // blocks are visited in order, so a cursor (partner, head, 64-row block) and the
+  // bases and mask data of the current (partner, head), refreshed only when those
+  // change, replace the per-block decode: no division or parameter load per block
+  // (a scalar load would also make the wave wait for all of its LDS reads).
+  int c_pi = 0, c_hi = 0, c_qb = 0, c_qb0 = 0, c_nqb = 0, c_sq = 0, c_qfull = 0, c_tfirst = 0;
   const __bf16* c_q = nullptr;
   const __bf16* c_g = nullptr;
   const float* c_l = nullptr;
-  auto cur_load = [&]() {
-    const BwdQPart QP = qpart_at(partner_at(ei, c_pi));
-    c_sq = QP.sq;
-    c_nqb = (QP.sq + kBN - 1) / kBN;
+  auto cur_load = [&]() {  // bases of (c_pi, c_hi); the cursor starts at the first block with work
+    for (;;) {
+      const BwdQPart QP = qpart_at(partner_at(ei, c_pi));
+      c_sq = QP.sq;
+      c_nqb = (QP.sq + kBN - 1) / kBN;
+      c_qb0 = part_qb0(QP);
+      if constexpr (SEG1) {
+        c_tfirst = key_ok ? first_row(QP, my_kpos) : 0;
+        c_qfull = (first_row(QP, w_kmax) + kBN - 1) / kBN;
+      }
+      if (c_qb0 < c_nqb || c_pi + 1 >= E.n) break;
+      ++c_pi;  // no allowed pair with this partition
+    }
+    c_qb = c_qb0;
     const int h = head_of(g0 + c_hi);
+    const BwdQPart QP = qpart_at(partner_at(ei, c_pi));
     const int64_t off = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
     c_q = (const __bf16*)QP.q + off;
     c_g = (const __bf16*)QP.dout + off;
     c_l = QP.lsed + ((int64_t)b * p.hq + h) * c_nqb * (2 * kBN);
   };
-  auto issue_next = [&](int st) {
+  auto issue_next = [&](int st) -> BlkMask {
     const int64_t roff = (int64_t)c_qb * kBN * p.q_ss;
     const __bf16* qbase = c_q + roff;
     const __bf16* gbase = c_g + roff;
@@ -640,20 +713,29 @@ bwd_dkv_kernel(const BwdParams p) {
       }
     }
     if (lane < 8) lds_dma16(c_l + c_qb * (2 * kBN), (uint32_t)(wave * 128 + lane * 16), lds_addr(&ld_s[st][wave * 32]));
+    BlkMask bm{1, 0};
+    if constexpr (SEG1) {  // every row of a whole block passes (-2^30)
+      bm.whole = c_qb >= c_qfull;
+      bm.lim = bm.whole ? -(1 << 30) : c_tfirst - c_qb * kBN;
+    }
     if (++c_qb == c_nqb) {
-      c_qb = 0;
       if (++c_hi == gsz) {
         c_hi = 0;
         ++c_pi;
       }
       if (c_pi < E.n) cur_load();
     }
+    return bm;
   };
-  auto issue_at = [&](int st, int g) {
-    if constexpr (MASKED) issue(st, g);
-    else issue_next(st);
+  auto issue_at = [&](int st, int g) -> BlkMask {
+    if constexpr (WALK) {
+      return issue_next(st);
+    } else {
+      issue(st, g);
+      return BlkMask{1, 0};
+    }
   };
-  if constexpr (!MASKED) cur_load();
+  if constexpr (WALK) cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (2 * LPW + 1)));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW + 1));
@@ -702,8 +784,8 @@ bwd_dkv_kernel(const BwdParams p) {
   // that are not fully allowed for the wave take a second copy of the body that
   // zeroes P where the key comes after the query; both copies are straight-line
   // code, so the VALU work interleaves with the MFMAs.
-  auto half_body = [&](auto masked, int g, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu, f32x16& sn,
-                       f32x16& dn) {
+  auto half_body = [&](auto masked, int g, const BlkMask& bm, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu,
+                       f32x16& sn, f32x16& dn) {
     // one wave per SIMD: ask the scheduler to interleave the LDS reads with the
     // MFMAs (measured: 14% faster than the default schedule for this kernel)
     __builtin_amdgcn_iglp_opt(0);
@@ -711,13 +793,21 @@ bwd_dkv_kernel(const BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(sc[e] * c2);
     if constexpr (decltype(masked)::value) {
-      int pi, hi, qb;
-      decode(g, pi, hi, qb);
-      const BwdQPart QP = qpart_at(partner_at(ei, pi));
+      if constexpr (SEG1) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {  // position at a clamped index, then a select
-        const int t = min(QP.sq - 1, qb * kBN + 32 * u + 16 * (e >> 3) + 8 * hl + (e & 7));
-        pe[e] = (my_kpos <= pos_at_dev(QP.qp, t)) ? pe[e] : 0.f;
+        for (int e = 0; e < 16; ++e) {  // row of the block at or after this key's first allowed row
+          const int rr = 32 * u + 16 * (e >> 3) + 8 * hl + (e & 7);
+          pe[e] = rr >= bm.lim ? pe[e] : 0.f;
+        }
+      } else {
+        int pi, hi, qb;
+        decode(g, pi, hi, qb);
+        const BwdQPart QP = qpart_at(partner_at(ei, pi));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {  // position at a clamped index, then a select
+          const int t = min(QP.sq - 1, qb * kBN + 32 * u + 16 * (e >> 3) + 8 * hl + (e & 7));
+          pe[e] = (my_kpos <= pos_at_dev(QP.qp, t)) ? pe[e] : 0.f;
+        }
       }
     }
     bf16x8 pf[2], dsf[2];
@@ -742,22 +832,29 @@ bwd_dkv_kernel(const BwdParams p) {
       }
     }
   };
-  auto half_step = [&](int g, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu, f32x16& sn, f32x16& dn) {
-    if constexpr (MASKED) {
+  auto half_step = [&](int g, const BlkMask& bm, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu, f32x16& sn,
+                       f32x16& dn) {
+    if constexpr (SEG1) {
+      // one straight-line body: the row test costs two VALU ops per element, less
+      // than a second copy of the body costs in registers
+      half_body(std::true_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
+      return;
+    } else if constexpr (MASKED) {
       if (block_class(g, w_kmin, w_kmax, false) != 2) {
-        half_body(std::true_type{}, g, st, u, sc, dc, nst, nu, sn, dn);
+        half_body(std::true_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
         return;
       }
     }
-    half_body(std::false_type{}, g, st, u, sc, dc, nst, nu, sn, dn);
+    half_body(std::false_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
   };
 
   int bj0 = next_block(0);
   int bj1 = bj0 < total ? next_block(bj0 + 1) : total;
   int bj2 = bj1 < total ? next_block(bj1 + 1) : total;
-  if (bj0 < total) issue_at(0, bj0);
-  if (bj1 < total) issue_at(1, bj1);
-  if (bj2 < total) issue_at(2, bj2);
+  BlkMask m0{1, 0}, m1{1, 0}, m2{1, 0};  // masks of positions bj0..bj2
+  if (bj0 < total) m0 = issue_at(0, bj0);
+  if (bj1 < total) m1 = issue_at(1, bj1);
+  if (bj2 < total) m2 = issue_at(2, bj2);
   f32x16 sA, dA, sB, dB;
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // also retires the fragment loads
   if (bj0 < total) {
@@ -766,15 +863,18 @@ bwd_dkv_kernel(const BwdParams p) {
   }
 #define MA_DKV_BLOCK(ST)                                                 \
   {                                                                      \
-    half_step(bj0, (ST), 0, sA, dA, (ST), 1, sB, dB);                    \
+    half_step(bj0, m0, (ST), 0, sA, dA, (ST), 1, sB, dB);                \
     const int bj3 = bj2 < total ? next_block(bj2 + 1) : total;           \
     wait_positions(bj2 < total ? 1 : 0);                                 \
     __syncthreads();                                                     \
-    if (bj3 < total) issue_at(((ST) + 3) & 3, bj3);                      \
-    half_step(bj0, (ST), 1, sB, dB, ((ST) + 1) & 3, 0, sA, dA);          \
+    const BlkMask m3 = bj3 < total ? issue_at(((ST) + 3) & 3, bj3) : BlkMask{1, 0}; \
+    half_step(bj0, m0, (ST), 1, sB, dB, ((ST) + 1) & 3, 0, sA, dA);      \
     bj0 = bj1;                                                           \
     bj1 = bj2;                                                           \
     bj2 = bj3;                                                           \
+    m0 = m1;                                                             \
+    m1 = m2;                                                             \
+    m2 = m3;                                                             \
     if (bj0 >= total) break;                                             \
   }
   while (bj0 < total) {
@@ -826,11 +926,13 @@ int launch_bwd_dq(const BwdParams& p, int head_dim, int total_wgs, void* stream)
   hipStream_t s = (hipStream_t)stream;
   dim3 g(total_wgs), blk(512);
   if (head_dim == 128) {
-    if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), g, blk, 0, s, p);
+    if (p.mask == 1) hipLaunchKernelGGL((bwd_dq_kernel<128, 1>), g, blk, 0, s, p);
+    else if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<128, 2>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, 0>), g, blk, 0, s, p);
   } else {
-    if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_kernel<64, false>), g, blk, 0, s, p);
+    if (p.mask == 1) hipLaunchKernelGGL((bwd_dq_kernel<64, 1>), g, blk, 0, s, p);
+    else if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<64, 2>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<64, 0>), g, blk, 0, s, p);
   }
   return (int)hipGetLastError();
 }
@@ -840,11 +942,13 @@ int launch_bwd_dkv(const BwdParams& p, int head_dim, int total_wgs, void* stream
   hipStream_t s = (hipStream_t)stream;
   dim3 g(total_wgs), blk(256);
   if (head_dim == 128) {
-    if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<128, true>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dkv_kernel<128, false>), g, blk, 0, s, p);
+    if (p.mask == 1) hipLaunchKernelGGL((bwd_dkv_kernel<128, 1>), g, blk, 0, s, p);
+    else if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<128, 2>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkv_kernel<128, 0>), g, blk, 0, s, p);
   } else {
-    if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<64, true>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dkv_kernel<64, false>), g, blk, 0, s, p);
+    if (p.mask == 1) hipLaunchKernelGGL((bwd_dkv_kernel<64, 1>), g, blk, 0, s, p);
+    else if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<64, 2>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkv_kernel<64, 0>), g, blk, 0, s, p);
   }
   return (int)hipGetLastError();
 }

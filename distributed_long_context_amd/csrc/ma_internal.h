@@ -122,7 +122,7 @@ struct BwdEntry {        // one group: its own partition and the partner partiti
 struct BwdParams {
   int32_t nentries;
   int32_t batch, hq, hkv, gmax;
-  int32_t mask;
+  int32_t mask;  // 0 none; 1 causal, every partner's positions one segment; 2 causal, any positions
   float scale, scale_log2;
   int64_t q_sb, q_ss, q_sh;    // q, o, dout
   int64_t k_sb, k_ss, k_sh;    // k, v

@@ -211,3 +211,47 @@ def test_bwd_q_tile_meets_many_kv(nkv, mode):
         check_grad("dK", dk, dk_r)
         check_grad("dV", dv, dv_r)
     check_grad("dQ (sum of shares)", dq, dq_ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_striped_partition_grid(d):
+    # striped layout with N = 4 ([Mesh] section 3.7): Q partitions r = 0, 2 and KV partitions 1, 3,
+    # every pair PARTIAL, all four in one call (dq shared per Q partition, dk/dv per KV partition)
+    sq, sk, hq, hkv, N = 200, 150, 8, 2, 4
+    log(f"[bwd striped grid] d={d}")
+    wid = 1500 + d
+    scale = np.float32(1.0 / math.sqrt(d))
+    Q = {r: gen(wid, synthetic.T_Q, r, (1, sq, hq, d)) for r in (0, 2)}
+    G = {r: gen(wid, synthetic.T_DO, r, (1, sq, hq, d)) for r in (0, 2)}
+    K = {c: gen(wid, synthetic.T_K, c, (1, sk, hkv, d)) for c in (1, 3)}
+    V = {c: gen(wid, synthetic.T_V, c, (1, sk, hkv, d)) for c in (1, 3)}
+    qpos = {r: np.arange(sq) * N + r for r in (0, 2)}
+    kpos = {c: np.arange(sk) * N + c for c in (1, 3)}
+    kall = np.concatenate([K[c][1] for c in (1, 3)], axis=1)
+    vall = np.concatenate([V[c][1] for c in (1, 3)], axis=1)
+    kpall = np.concatenate([kpos[c] for c in (1, 3)])
+    stored, dq = {}, {}
+    for r in (0, 2):
+        O, L = attn_tile(Q[r][1], kall, vall, scale, None, True, qpos[r], kpall)
+        stored[r] = stored_o_lse(O, L)
+        dq[r] = torch.full((1, sq, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    dk = {c: torch.full((1, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV) for c in (1, 3)}
+    dv = {c: torch.full((1, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV) for c in (1, 3)}
+    tiles = [BwdTile(Q[r][0], K[c][0], V[c][0], stored[r][0], G[r][0], stored[r][2], dq[r], dk[c], dv[c],
+                     ma.mesh_attn_pos_striped(N, r), ma.mesh_attn_pos_striped(N, c)) for r in (0, 2) for c in (1, 3)]
+    assert all(ma.mesh_attn_classify(t.q_pos, sq, t.k_pos, sk, ma.MA_MASK_STRIPED_ZIGZAG) == ma.MA_TILE_PARTIAL
+               for t in tiles)
+    ma.mesh_attn_tile_bwd(tiles, float(scale), ma.MA_MASK_STRIPED_ZIGZAG)
+    torch.cuda.synchronize()
+    dk_ref = {c: 0 for c in (1, 3)}
+    dv_ref = {c: 0 for c in (1, 3)}
+    for r in (0, 2):
+        dq_r, dk_r, dv_r = attn_tile_bwd(Q[r][1], kall, vall, stored[r][1], G[r][1], stored[r][3], scale, None,
+                                         True, qpos[r], kpall)
+        check_grad(f"dQ{r}", dq[r], dq_r)
+        for i, c in enumerate((1, 3)):
+            dk_ref[c] = dk_ref[c] + dk_r[:, i * sk:(i + 1) * sk]
+            dv_ref[c] = dv_ref[c] + dv_r[:, i * sk:(i + 1) * sk]
+    for c in (1, 3):
+        check_grad(f"dK{c}", dk[c], dk_ref[c])
+        check_grad(f"dV{c}", dv[c], dv_ref[c])
