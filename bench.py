@@ -47,9 +47,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle sample")
     ap.add_argument("--parts", default="fwd,merge,bwd", help="kernels in the step (all by default)")
-    ap.add_argument("--workloads", default="zigzag,mesh,bwd4",
+    ap.add_argument("--workloads", default="zigzag,mesh,striped,bwd4",
                     help="the other workloads timed after the step (comma list; 'none' for none): "
                          "zigzag = causal zigzag share of S=131072, mesh = Mesh 8x8 tile of S=1048576, "
+                         "striped = the same Mesh tile under the causal mask with striped positions, "
                          "bwd4 = backward of 4 Q partitions x one KV partition of 8192")
     ap.add_argument("--workload-reps", type=int, default=2, help="timed repetitions per workload entry")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -358,6 +359,38 @@ def measure_workloads(names, reps):
         w["reduce_add_8_dq"] = _gb(9 * parts[0].numel() * 4, _timed(lambda: ma.mesh_attn_reduce_add(parts, red), reps))
         res["mesh-8x8-1m-g9"] = w
         del Q, kg, vg, K, V, inc, dO, O, L, dq, dk, dv, btiles, ws, parts, red
+        torch.cuda.empty_cache()
+    if "striped" in names:
+        # Mesh 8 x 8 share at S = 1,048,576 under the causal mask with the striped layout of [Mesh]
+        # section 3.7: partition p holds tokens p + 64 t, so every (Q, KV) pair is PARTIAL
+        n, a, b, g, P = 64, 8, 8, 9, 16384
+        qparts, kparts = ma.mesh_attn_map_mesh_tile(n, a, b, g, True)
+        Q = {i: randn((1, P, HQ, D)) for i in qparts}
+        kg = randn((1, b * P, HKV, D))
+        vg = randn((1, b * P, HKV, D))
+        K = {j: kg[:, t * P:(t + 1) * P] for t, j in enumerate(kparts)}
+        V = {j: vg[:, t * P:(t + 1) * P] for t, j in enumerate(kparts)}
+        qpos = {i: ma.mesh_attn_pos_striped(n, i) for i in qparts}
+        kpos = {j: ma.mesh_attn_pos_striped(n, j) for j in kparts}
+        mode = ma.MA_MASK_STRIPED_ZIGZAG
+        pairs = sum(ma.mesh_attn_count_allowed(qpos[i], P, kpos[j], P, mode) for i in qparts for j in kparts)
+        tiles = [Tile(Q[i], K[j], V[j], *out(P), qpos[i], kpos[j]) for i in qparts for j in kparts]
+        w = {"tiles": len(tiles), "allowed_pairs_per_head": pairs}
+        w["fwd_tiles"] = _tf(4.0 * D * HQ * pairs, _timed(lambda: ma.mesh_attn_tile_fwd(tiles, scale, mode), reps))
+        del tiles
+        torch.cuda.empty_cache()
+        dO = {i: randn((1, P, HQ, D)) for i in qparts}
+        O = {i: randn((1, P, HQ, D), mul=0.01) for i in qparts}
+        L = {i: randn((1, HQ, P), torch.float32, 0.3, math.log(b * P / 2) + 0.5) for i in qparts}
+        dq = {i: torch.empty((1, P, HQ, D), dtype=torch.float32, device=dev) for i in qparts}
+        dk = {j: torch.empty((1, P, HKV, D), dtype=torch.float32, device=dev) for j in kparts}
+        dv = {j: torch.empty_like(dk[j]) for j in kparts}
+        btiles = [BwdTile(Q[i], K[j], V[j], O[i], dO[i], L[i], dq[i], dk[j], dv[j], qpos[i], kpos[j])
+                  for i in qparts for j in kparts]
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        w["bwd_tiles"] = _tf(10.0 * D * HQ * pairs, _timed(lambda: ma.mesh_attn_tile_bwd(btiles, scale, mode, workspace=ws), 1))
+        res["mesh-8x8-1m-g9-striped-causal"] = w
+        del Q, kg, vg, K, V, dO, O, L, dq, dk, dv, btiles, ws
         torch.cuda.empty_cache()
     if "bwd4" in names:
         S, nq = 8192, 4

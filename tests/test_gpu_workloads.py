@@ -303,3 +303,80 @@ def test_zigzag_causal_128k_rank5_backward():
         check(f"dV chunk {j}", host_f64(dv[j])[:, keys], dv_r)
     for j in range(nkv):
         assert torch.isfinite(dk[j]).all() and torch.isfinite(dv[j]).all()
+
+
+def test_mesh_8x8_striped_causal_share():
+    # The Mesh 8 x 8 share of GPU 9 (n = 64, KV rotation) under the causal mask with the striped
+    # layout of [Mesh] section 3.7 (partition p holds tokens p + 64 t), at 2048 tokens per partition:
+    # every pair is PARTIAL.  Forward: 64 tiles in one call, 8-way merges, sampled rows against the
+    # oracle over all 8 KV partitions.  Backward: 64 pairs in one call with seeded stored O and LSE;
+    # sampled dQ rows and sampled dK/dV keys.
+    wid, n, a, b, g, P = 7, 64, 8, 8, 9, 2048
+    log("[workload mesh-8x8 striped causal, P=2048]")
+    mode = ma.MA_MASK_STRIPED_ZIGZAG
+    qparts, kparts = ma.mesh_attn_map_mesh_tile(n, a, b, g, True)
+    Q = {i: gen(wid, synthetic.T_Q, i, (1, P, HQ, D)) for i in qparts}
+    K = {j: gen(wid, synthetic.T_K, j, (1, P, HKV, D)) for j in kparts}
+    V = {j: gen(wid, synthetic.T_V, j, (1, P, HKV, D)) for j in kparts}
+    qpos = {i: ma.mesh_attn_pos_striped(n, i) for i in qparts}
+    kpos = {j: ma.mesh_attn_pos_striped(n, j) for j in kparts}
+    tiles = {(i, j): Tile(Q[i][0], K[j][0], V[j][0], *empty_out(P), qpos[i], kpos[j]) for i in qparts for j in kparts}
+    assert all(ma.mesh_attn_classify(qpos[i], P, kpos[j], P, mode) == ma.MA_TILE_PARTIAL for i, j in tiles)
+    ma.mesh_attn_tile_fwd(list(tiles.values()), float(SCALE), mode)
+    merged = {}
+    for i in qparts:
+        o, lse = empty_out(P)
+        ma.mesh_attn_merge([tiles[(i, j)].o for j in kparts], [tiles[(i, j)].lse for j in kparts], o, lse)
+        merged[i] = (o, lse)
+    torch.cuda.synchronize()
+    kall = np.concatenate([K[j][1] for j in kparts], axis=1)
+    vall = np.concatenate([V[j][1] for j in kparts], axis=1)
+    kp_all = np.concatenate([positions(kpos[j], P) for j in kparts])
+    for i in (qparts[0], qparts[5]):
+        rows = sample_rows(P, wid + i, extra=8)
+        Oref, Lref = attn_tile(Q[i][1], kall, vall, SCALE, None, True, positions(qpos[i], P), kp_all, rows=rows)
+        check_close(f"merged O Q{i}", host_f64(merged[i][0])[:, rows], Oref, BF16_O_TOL)
+        check_close(f"merged LSE Q{i}", host_f64(merged[i][1])[:, :, rows], Lref, BF16_LSE_TOL)
+    del tiles, merged
+    # backward
+    host, dev_in = {}, {}
+    for i in qparts:
+        do, dov = gen(wid, synthetic.T_DO, i, (1, P, HQ, D))
+        ob = synthetic.f32_to_bf16_bits(synthetic.normal_f32(wid, synthetic.T_O_IN, i, (1, P, HQ, D)) * np.float32(0.02))
+        ov = synthetic.bf16_bits_to_f32(ob).astype(np.float64)
+        lv = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (1, HQ, P)) * np.float32(0.3)
+              + np.float32(math.log(b * P / 2) + 0.5)).astype(np.float32)
+        dq = torch.empty((1, P, HQ, D), dtype=torch.float32, device=DEV)
+        dev_in[i] = (do, dev_bf16(ob), torch.from_numpy(lv).to(DEV), dq)
+        host[i] = dict(do=dov, o=ov, lse=lv.astype(np.float64), q_pos=positions(qpos[i], P))
+    dk = {j: torch.empty((1, P, HKV, D), dtype=torch.float32, device=DEV) for j in kparts}
+    dv = {j: torch.empty_like(dk[j]) for j in kparts}
+    btiles = [BwdTile(Q[i][0], K[j][0], V[j][0], dev_in[i][1], dev_in[i][0], dev_in[i][2], dev_in[i][3], dk[j], dv[j],
+                      qpos[i], kpos[j]) for i in qparts for j in kparts]
+    ma.mesh_attn_tile_bwd(btiles, float(SCALE), mode)
+    torch.cuda.synchronize()
+
+    def check(name, got, ref):
+        scale = max(float(np.max(np.abs(ref))), 1e-3)
+        err = float(np.max(np.abs(got - ref)))
+        log(f"  {name}: max_abs_err={err:.3e} max|ref|={scale:.3e} rel={err/scale:.2e}")
+        assert np.isfinite(got).all() and err <= 2e-2 * scale
+
+    for i in (qparts[0], qparts[7]):
+        rows = sample_rows(P, wid + 10 * i, extra=6)
+        h = host[i]
+        dq_r, _, _ = attn_tile_bwd(Q[i][1][:, rows], kall, vall, h["o"][:, rows], h["do"][:, rows],
+                                   h["lse"][:, :, rows], SCALE, None, True, h["q_pos"][rows], kp_all)
+        check(f"dQ Q{i}", host_f64(dev_in[i][3])[:, rows], dq_r)
+    for j in (kparts[0], kparts[6]):
+        keys = sample_rows(P, wid + 100 + j, extra=4)
+        kp = positions(kpos[j], P)[keys]
+        dk_r = dv_r = 0
+        for i in qparts:
+            h = host[i]
+            _, a_, b_ = attn_tile_bwd(Q[i][1], K[j][1][:, keys], V[j][1][:, keys], h["o"], h["do"], h["lse"], SCALE,
+                                      None, True, h["q_pos"], kp)
+            dk_r = dk_r + a_
+            dv_r = dv_r + b_
+        check(f"dK KV{j}", host_f64(dk[j])[:, keys], dk_r)
+        check(f"dV KV{j}", host_f64(dv[j])[:, keys], dv_r)
