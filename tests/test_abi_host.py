@@ -109,3 +109,27 @@ def test_null_args():
     L = _abi.lib()
     assert L.mesh_attn_tile_fwd(None, None) == _abi.MA_ERR_INVALID
     assert L.mesh_attn_merge(None, None) == _abi.MA_ERR_INVALID
+
+
+def test_reduce_add_rejects_bad_arguments_without_launching():
+    L = _abi.lib()
+    ptrs = (C.c_void_p * 2)(4096, 4096)
+    a = _abi.ma_reduce_args()
+    a.k, a.n, a.out = 2, 16, 4096
+    a.in_ = C.cast(ptrs, C.POINTER(C.c_void_p))
+    for k in (0, _abi.MA_MAX_MERGE + 1):
+        a.k = k
+        assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_ERR_INVALID
+    a.k = 2
+    a.n = -1
+    assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_ERR_INVALID
+    a.n = 16
+    a.out = 4100  # not 16-byte aligned
+    assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_ERR_INVALID
+    a.out = 4096
+    ptrs[1] = 4104
+    assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_ERR_INVALID
+    ptrs[1] = None
+    assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_ERR_INVALID
+    a.n = 0  # no-op before any pointer is looked at
+    assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_OK
