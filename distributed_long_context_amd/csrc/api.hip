@@ -135,7 +135,6 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   p.hq = a->hq;
   p.hkv = a->hkv;
   p.mask = a->mask_mode != MA_MASK_NONE;
-  p.accumulate = a->accumulate;
   p.scale = a->scale;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   p.q_sb = a->q_stride[0]; p.q_ss = a->q_stride[1]; p.q_sh = a->q_stride[2];
@@ -157,13 +156,17 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   }
 
   const bool bf16 = a->dtype == MA_BF16;
-  // Tiles go to one of three launches by how much masking they need: FULL tiles
-  // (and every tile without a mask) run the unmasked kernel, PARTIAL tiles whose
-  // key positions are one segment the single-segment variant, the rest the
-  // general one.  A tile naming the output of one already queued waits for it.
-  FwdParams bp[3];
-  int bn[3] = {0, 0, 0}, bwg[3] = {0, 0, 0};
-  for (int m = 0; m < 3; ++m) {
+  const int64_t esize = bf16 ? 2 : 4;
+  // Tiles go to one of two launches by how much masking they need: FULL tiles (and
+  // every tile without a mask) run the unmasked kernel, PARTIAL ones the masked
+  // kernel, whose key positions must be one segment: a tile whose key positions
+  // have several segments is run as one piece per segment (the keys of a segment
+  // are contiguous rows), the first piece with any allowed pair writing the
+  // output and the later ones folding into it.  A tile naming the output of one
+  // already queued waits for it.
+  FwdParams bp[2];
+  int bn[2] = {0, 0}, bwg[2] = {0, 0};
+  for (int m = 0; m < 2; ++m) {
     bp[m] = p;
     bp[m].mask = m;
   }
@@ -176,38 +179,28 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     return check_hip(e, "tile_fwd launch");
   };
   auto flush_all = [&]() -> int {
-    for (int m = 0; m < 3; ++m) {
+    for (int m = 0; m < 2; ++m) {
       int r = flush(m);
       if (r) return r;
     }
     return MA_OK;
   };
-  for (int i = 0; i < a->ntiles; ++i) {
-    const ma_tile& t = a->tiles[i];
+  // queue one (sub-)tile; cls is its class, acc its accumulate flag
+  auto enqueue = [&](const ma_tile& t, int cls, int acc) -> int {
     bool dup = false;
-    for (int m = 0; m < 3 && !dup; ++m)
-      for (int j = 0; j < bn[m]; ++j)
-        if (bp[m].tiles[j].o == t.o || bp[m].tiles[j].lse == t.lse) dup = true;
+    for (int k = 0; k < 2; ++k)
+      for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == t.o || bp[k].tiles[j].lse == t.lse;
     if (dup) {
-      rc = flush_all();
-      if (rc) return rc;
+      int r = flush_all();
+      if (r) return r;
     }
-    const int cls = a->mask_mode == MA_MASK_NONE ? MA_TILE_FULL
-                                                 : mesh_attn_classify(&t.q_pos, t.sq, &t.k_pos, t.sk, a->mask_mode);
-    if (cls == MA_TILE_EMPTY) {
-      if (a->accumulate) continue;  // nothing to fold in
-      int e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss,
-                                p.o_sh, p.l_sb, p.l_sh, stream);
-      rc = check_hip(e, "fill launch");
-      if (rc) return rc;
-      continue;
-    }
-    const int m = cls == MA_TILE_FULL ? 0 : (t.k_pos.nseg == 1 ? 1 : 2);
+    const int m = cls == MA_TILE_FULL ? 0 : 1;
     FwdTile& ft = bp[m].tiles[bn[m]];
     std::memset(&ft, 0, sizeof(ft));
     ft.q = t.q; ft.k = t.k; ft.v = t.v; ft.o = t.o; ft.lse = t.lse;
     ft.sq = (int32_t)t.sq;
     ft.sk = (int32_t)t.sk;
+    ft.accumulate = acc;
     if (m != 0) {
       to_kpos(t.q_pos, ft.qp);
       to_kpos(t.k_pos, ft.kp);
@@ -229,8 +222,40 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     ft.wg_begin = bwg[m];
     bwg[m] += (int)wgs;
     ++bn[m];
-    if (bn[m] == kFwdTilesPerLaunch) {
-      rc = flush(m);
+    if (bn[m] == kFwdTilesPerLaunch) return flush(m);
+    return MA_OK;
+  };
+  for (int i = 0; i < a->ntiles; ++i) {
+    const ma_tile& t = a->tiles[i];
+    const int nseg = a->mask_mode == MA_MASK_NONE ? 1 : t.k_pos.nseg;
+    int acc = a->accumulate;  // the first piece with work writes unless the call accumulates
+    for (int sgi = 0; sgi < nseg; ++sgi) {
+      ma_tile u = t;
+      if (nseg > 1) {
+        const int64_t lb = t.k_pos.seg[sgi].local_begin;
+        const int64_t le = sgi + 1 < nseg ? t.k_pos.seg[sgi + 1].local_begin : t.sk;
+        u.k = (const char*)t.k + lb * a->k_stride[1] * esize;
+        u.v = (const char*)t.v + lb * a->v_stride[1] * esize;
+        u.sk = le - lb;
+        std::memset(&u.k_pos, 0, sizeof(u.k_pos));
+        u.k_pos.nseg = 1;
+        u.k_pos.seg[0].local_begin = 0;
+        u.k_pos.seg[0].global_begin = t.k_pos.seg[sgi].global_begin;
+        u.k_pos.seg[0].stride = t.k_pos.seg[sgi].stride;
+      }
+      const int cls = a->mask_mode == MA_MASK_NONE ? MA_TILE_FULL
+                                                   : mesh_attn_classify(&u.q_pos, u.sq, &u.k_pos, u.sk, a->mask_mode);
+      if (cls == MA_TILE_EMPTY) continue;
+      rc = enqueue(u, cls, acc);
+      if (rc) return rc;
+      acc = 1;
+    }
+    if (acc == 0) {  // no piece had an allowed pair: the tile's result is (0, -inf)
+      rc = flush_all();  // a queued tile may name the same output
+      if (rc) return rc;
+      int e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss,
+                                p.o_sh, p.l_sb, p.l_sh, stream);
+      rc = check_hip(e, "fill launch");
       if (rc) return rc;
     }
   }
@@ -298,6 +323,60 @@ struct BwdGroups {
   std::vector<std::vector<int>> qg, kvg;        // tiles of each group
 };
 
+// Under a mask, a tile whose Q or K positions have several segments runs as one
+// piece per (Q segment, K segment): the rows of a segment are contiguous, so a
+// piece is the same buffers at a row offset with a one-segment position map.  The
+// pieces of a tile's Q segment share its dq rows (summed like any Q group) and
+// those of a K segment its dk/dv rows.  Returns a or the expanded copy in e.
+const ma_tile_bwd_args* expand_bwd_segments(const ma_tile_bwd_args* a, std::vector<ma_bwd_tile>& ex,
+                                            ma_tile_bwd_args& e) {
+  if (a->mask_mode == MA_MASK_NONE) return a;
+  bool any = false;
+  for (int i = 0; i < a->ntiles; ++i) any = any || a->tiles[i].q_pos.nseg > 1 || a->tiles[i].k_pos.nseg > 1;
+  if (!any) return a;
+  auto seg_end = [](const ma_pos& ps, int s, int64_t len) {
+    return s + 1 < ps.nseg ? ps.seg[s + 1].local_begin : len;
+  };
+  auto one_seg = [](const ma_pos& ps, int s) {
+    ma_pos o;
+    std::memset(&o, 0, sizeof(o));
+    o.nseg = 1;
+    o.seg[0].global_begin = ps.seg[s].global_begin;
+    o.seg[0].stride = ps.seg[s].stride;
+    return o;
+  };
+  for (int i = 0; i < a->ntiles; ++i) {
+    const ma_bwd_tile& t = a->tiles[i];
+    for (int qs = 0; qs < t.q_pos.nseg; ++qs)
+      for (int ks = 0; ks < t.k_pos.nseg; ++ks) {
+        ma_bwd_tile u = t;
+        const int64_t qb = t.q_pos.seg[qs].local_begin, kb = t.k_pos.seg[ks].local_begin;
+        if (t.q_pos.nseg > 1) {
+          u.q = (const char*)t.q + qb * a->q_stride[1] * 2;
+          u.o = (const char*)t.o + qb * a->q_stride[1] * 2;
+          u.dout = (const char*)t.dout + qb * a->q_stride[1] * 2;
+          u.lse = t.lse + qb;
+          u.dq = t.dq + qb * a->dq_stride[1];
+          u.sq = seg_end(t.q_pos, qs, t.sq) - qb;
+          u.q_pos = one_seg(t.q_pos, qs);
+        }
+        if (t.k_pos.nseg > 1) {
+          u.k = (const char*)t.k + kb * a->k_stride[1] * 2;
+          u.v = (const char*)t.v + kb * a->k_stride[1] * 2;
+          u.dk = t.dk + kb * a->dk_stride[1];
+          u.dv = t.dv + kb * a->dk_stride[1];
+          u.sk = seg_end(t.k_pos, ks, t.sk) - kb;
+          u.k_pos = one_seg(t.k_pos, ks);
+        }
+        ex.push_back(u);
+      }
+  }
+  e = *a;
+  e.tiles = ex.data();
+  e.ntiles = (int32_t)ex.size();
+  return &e;
+}
+
 BwdGroups bwd_groups(const ma_tile_bwd_args* a) {
   BwdGroups g;
   g.q_of.assign(a->ntiles, -1);
@@ -326,10 +405,13 @@ size_t lsed_bytes(int batch, int hq, int64_t sq) {
 
 extern "C" {
 
-size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* a) {
-  if (!a || a->ntiles <= 0 || !a->tiles || a->batch < 1 || a->hq < 1) return 0;
-  for (int i = 0; i < a->ntiles; ++i)
-    if (a->tiles[i].sq < 1) return 0;
+size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* a0) {
+  if (!a0 || a0->ntiles <= 0 || !a0->tiles || a0->batch < 1 || a0->hq < 1) return 0;
+  for (int i = 0; i < a0->ntiles; ++i)
+    if (a0->tiles[i].sq < 1) return 0;
+  std::vector<ma_bwd_tile> ex;
+  ma_tile_bwd_args e;
+  const ma_tile_bwd_args* a = expand_bwd_segments(a0, ex, e);
   const BwdGroups g = bwd_groups(a);
   size_t bytes = 0;
   for (const auto& grp : g.qg) bytes += lsed_bytes(a->batch, a->hq, a->tiles[grp[0]].sq);
@@ -381,6 +463,10 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
   if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & 255u))
     return set_error(MA_ERR_INVALID, "workspace missing, too small or not 256-byte aligned");
 
+  // from here on the tiles are single-segment pieces
+  std::vector<ma_bwd_tile> ex;
+  ma_tile_bwd_args e;
+  a = expand_bwd_segments(a, ex, e);
   const BwdGroups grp = bwd_groups(a);
   BwdParams base;
   std::memset(&base, 0, sizeof(base));
@@ -445,7 +531,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
   for (int side = 0; side < 2; ++side) {
     const bool dq_side = side == 0;
     const auto& own = dq_side ? grp.qg : grp.kvg;
-    // kind 0: unmasked; 1: masked, every partner's positions one segment; 2: masked, any positions
+    // kind 0: unmasked; 1: masked
     struct Piece { int group; std::vector<int> partners; int accumulate; int kind; };
     std::vector<Piece> pieces;
     for (int gi = 0; gi < (int)own.size(); ++gi) {
@@ -463,15 +549,7 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
           pc.group = gi;
           pc.partners.assign(lst.begin() + s0, lst.begin() + std::min(lst.size(), s0 + kBwdPerLaunch));
           pc.accumulate = first ? (a->accumulate ? 1 : 0) : 1;
-          pc.kind = 0;
-          if (kind == 1) {
-            pc.kind = 1;
-            for (int pg : pc.partners) {
-              // the partners' positions: KV partitions on the dQ side, Q partitions on the dK/dV side
-              const ma_bwd_tile& pt = a->tiles[dq_side ? grp.kvg[pg][0] : grp.qg[pg][0]];
-              if ((dq_side ? pt.k_pos.nseg : pt.q_pos.nseg) != 1) pc.kind = 2;
-            }
-          }
+          pc.kind = kind;  // pieces have one-segment positions (expand_bwd_segments)
           first = false;
           pieces.push_back(pc);
         }

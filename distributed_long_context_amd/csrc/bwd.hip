@@ -122,39 +122,16 @@ struct BlkMask {
   int lim;
 };
 
-// ------------------------------------------------------ walks over partners --
-// Blocks of an entry's partners, flattened: position g -> (partner index, block).
-struct PartnerWalk {
-  int n;
-  int pre[kBwdPerLaunch];  // pre[i]: blocks of partners 0..i-1 (uniform)
-  // branch-free: the last partner whose first block is <= g; positions past the
-  // end map to the last partner with a block index past its end
-  __device__ __forceinline__ void decode(int g, int& pi, int& blk) const {
-    int p = 0, base = 0;
-#pragma unroll
-    for (int i = 1; i < kBwdPerLaunch; ++i) {
-      const bool ge = (i < n) & (g >= pre[i]);
-      p = ge ? i : p;
-      base = ge ? pre[i] : base;
-    }
-    pi = __builtin_amdgcn_readfirstlane(p);
-    blk = __builtin_amdgcn_readfirstlane(g - base);
-  }
-};
-
 // ---------------------------------------------------------------- dQ kernel --
-// MODE 0: no position mask.  MODE 1: the key positions of every KV partition are
-// one segment (they grow with the key index), so a lane's mask is the index of
-// its last allowed key and the blocks with any allowed pair for the workgroup are
-// a prefix of each partition.  MODE 2: any position maps.
-template <int D, int MODE>
+// MASKED: causal on positions; the key positions of every KV partition are one
+// segment (they grow with the key index), so a lane's mask is the index of its
+// last allowed key and the blocks with any allowed pair for the workgroup are a
+// prefix of each partition.  Without it only keys past a partition's end are masked.
+template <int D, bool MASKED>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(const BwdParams p) {
   using C = Cfg<D>;
-  constexpr bool MASKED = MODE != 0;
-  constexpr bool SEG1 = MODE == 1;
-  constexpr bool WALK = MODE != 2;  // blocks visited in order with a cursor
   constexpr int kWaves = 8, kQW = 32;
   constexpr int LPW = kBN * C::CH / 64 / kWaves;  // direct-to-LDS loads per wave per tensor
   // K stages, then V stages
@@ -236,41 +213,13 @@ bwd_dq_kernel(const BwdParams p) {
     return pq < gb ? -1 : min(KV.sk - 1, (pq - gb) / st);
   };
   auto part_blocks = [&](const BwdKVPart& KV) {
-    if constexpr (SEG1) return (last_key(KV, wg_pmax) + kBN) / kBN;
+    if constexpr (MASKED) return (last_key(KV, wg_pmax) + kBN) / kBN;
     else return (KV.sk + kBN - 1) / kBN;
   };
-  PartnerWalk walk;
-  walk.n = E.n;
-  int total = 0;
+  int total = 0;  // blocks of the walk
 #pragma unroll
-  for (int i = 0; i < kBwdPerLaunch; ++i) {
-    walk.pre[i] = total;
-    total += i < E.n ? part_blocks(kvpart_at(partner_at(ei, i))) : 0;
-  }
-  auto block_class = [&](int g, int pmin, int pmax) -> int {  // 0 empty, 1 partial, 2 full
-    int pi, kb;
-    walk.decode(g, pi, kb);
-    const BwdKVPart KV = kvpart_at(partner_at(ei, pi));
-    const bool tail = kb * kBN + kBN > KV.sk;
-    if constexpr (!MASKED) {
-      return tail ? 1 : 2;
-    } else {
-      int kmin, kmax;
-      pos_minmax_dev(KV.kp, KV.sk, kb * kBN, min(KV.sk, kb * kBN + kBN), kmin, kmax);
-      if (kmin > pmax) return 0;
-      if (kmax <= pmin && !tail) return 2;
-      return 1;
-    }
-  };
-  auto next_block = [&](int from) -> int {
-    if constexpr (WALK) {
-      return from < total ? from : total;
-    } else {
-      for (int g = from; g < total; ++g)
-        if (block_class(g, wg_pmin, wg_pmax) != 0) return __builtin_amdgcn_readfirstlane(g);
-      return total;
-    }
-  };
+  for (int i = 0; i < kBwdPerLaunch; ++i) total += i < E.n ? part_blocks(kvpart_at(partner_at(ei, i))) : 0;
+  auto next_block = [&](int from) -> int { return from < total ? from : total; };
 
   // ---- direct-to-LDS loads of one K block and one V block ----
   auto load_row = [&](int i) { return ((wave * LPW + i) * 64 + lane) / C::CH; };
@@ -279,33 +228,11 @@ bwd_dq_kernel(const BwdParams p) {
   uint32_t go[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) go[i] = (uint32_t)(load_row(i) * k_ss + load_col(i)) * 2u;
-  auto issue = [&](int st, int g) {
-    int pi, kb;
-    walk.decode(g, pi, kb);
-    const BwdKVPart KV = kvpart_at(partner_at(ei, pi));
-    const int64_t off = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh + (int64_t)kb * kBN * p.k_ss;
-    const __bf16* kbase = (const __bf16*)KV.k + off;
-    const __bf16* vbase = (const __bf16*)KV.v + off;
-    const int valid = KV.sk - kb * kBN;
-    if (valid >= kBN) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        lds_dma16(kbase, go[i], lds_addr(&kv_s[0][st][(wave * LPW + i) * 512]));
-        lds_dma16(vbase, go[i], lds_addr(&kv_s[1][st][(wave * LPW + i) * 512]));
-      }
-    } else {  // ragged last block: repeat the last row (finite; masked)
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const uint32_t o2 = (uint32_t)(min(load_row(i), valid - 1) * k_ss + load_col(i)) * 2u;
-        lds_dma16(kbase, o2, lds_addr(&kv_s[0][st][(wave * LPW + i) * 512]));
-        lds_dma16(vbase, o2, lds_addr(&kv_s[1][st][(wave * LPW + i) * 512]));
-      }
-    }
-  };
-  // On the walk (no position masks, or one key segment per partition) the blocks
-  // are visited in order: a cursor (partner, block) and the current partner's
-  // bases and mask data replace the per-block decode; issue_at returns the mask of
-  // the block it loads.
+  // The blocks are visited in order: a cursor (partner, block) and the current
+  // partner's bases and mask data, refreshed only when the partner changes, stand
+  // in for a per-block decode (a kernel-argument load in the loop would also make
+  // the wave wait for all of its LDS reads); issue_at returns the mask of the
+  // block it loads.
   int c_pi = 0, c_kb = 0, c_nkb = 0, c_sk = 0, c_kfull = 0, c_klast = 0;
   const __bf16* c_k = nullptr;
   const __bf16* c_v = nullptr;
@@ -317,7 +244,7 @@ bwd_dq_kernel(const BwdParams p) {
       const int64_t off = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
       c_k = (const __bf16*)KV.k + off;
       c_v = (const __bf16*)KV.v + off;
-      if constexpr (SEG1) {
+      if constexpr (MASKED) {
         c_klast = last_key(KV, qpos);
         c_kfull = active ? (last_key(KV, w_pmin) + 1) / kBN : 0;
       }
@@ -345,7 +272,7 @@ bwd_dq_kernel(const BwdParams p) {
       }
     }
     BlkMask bm;
-    if constexpr (SEG1) {
+    if constexpr (MASKED) {
       bm.whole = c_kb < c_kfull;
       bm.lim = c_klast - c_kb * kBN;
     } else {
@@ -359,15 +286,8 @@ bwd_dq_kernel(const BwdParams p) {
     }
     return bm;
   };
-  auto issue_at = [&](int st, int g) -> BlkMask {
-    if constexpr (WALK) {
-      return issue_next(st);
-    } else {
-      issue(st, g);
-      return BlkMask{1, kBN - 1};
-    }
-  };
-  if constexpr (WALK) cur_load();
+  auto issue_at = [&](int st, int g) -> BlkMask { return issue_next(st); };
+  cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
@@ -401,27 +321,11 @@ bwd_dq_kernel(const BwdParams p) {
   // allowed key index within the block (keys past a partition's end included;
   // -1 past the end of the walk: every key masked).
   auto mask_half = [&](int g, const BlkMask& bm, int kb2, f32x16& s) {
-    if constexpr (WALK) {
-      if (__builtin_expect(bm.whole, 1)) return;
+    if (__builtin_expect(bm.whole, 1)) return;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int kk = kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-        s[e] = kk <= bm.lim ? s[e] : -INFINITY;
-      }
-      return;
-    }
-    const int cls = active ? block_class(g, w_pmin, w_pmax) : 1;
-    if (cls == 2) return;
-    int pi, kb;
-    walk.decode(g < total ? g : total - 1, pi, kb);
-    if (g >= total) kb += 1 << 20;  // past the end: every key masked
-    const BwdKVPart KV = kvpart_at(partner_at(ei, pi));
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {  // branch-free: position at a clamped index, then a select
-      const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-      bool ok = key < KV.sk;
-      if constexpr (MASKED) ok = ok & (pos_at_dev(KV.kp, min(key, KV.sk - 1)) <= qpos);
-      s[e] = ok ? s[e] : -INFINITY;
+    for (int e = 0; e < 16; ++e) {
+      const int kk = kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
+      s[e] = kk <= bm.lim ? s[e] : -INFINITY;
     }
   };
   // one 32-key step: P, dS of the current half; S^T, dP^T of the next half under
@@ -510,18 +414,15 @@ bwd_dq_kernel(const BwdParams p) {
 }
 
 // --------------------------------------------------------------- dK/dV kernel --
-// MODE 0: no position mask.  MODE 1: the query positions of every Q partition
-// are one segment (they grow with the row index), so a lane's mask is the index
-// of the first row allowed to see its key and the blocks with any allowed pair
-// for the workgroup are a suffix of each (partition, head).  MODE 2: any maps.
-template <int D, int MODE>
+// MASKED: causal on positions; the query positions of every Q partition are one
+// segment (they grow with the row index), so a lane's mask is the index of the
+// first row allowed to see its key and the blocks with any allowed pair for the
+// workgroup are a suffix of each (partition, head).
+template <int D, bool MASKED>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_dkv_kernel(const BwdParams p) {
   using C = Cfg<D>;
-  constexpr bool MASKED = MODE != 0;
-  constexpr bool SEG1 = MODE == 1;
-  constexpr bool WALK = MODE != 2;
   constexpr int kWaves = 4, kKW = 32;
   constexpr int LPW = kBN * C::CH / 64 / kWaves;
   // Q stages, then dO stages; LSE2/D blocks
@@ -583,50 +484,18 @@ bwd_dkv_kernel(const BwdParams p) {
   };
   // 64-row blocks of a partition, and the first one with any allowed pair for the workgroup
   auto part_qb0 = [&](const BwdQPart& QP) {
-    if constexpr (SEG1) return first_row(QP, wg_kmin) / kBN;
+    if constexpr (MASKED) return first_row(QP, wg_kmin) / kBN;
     else return 0;
   };
-  PartnerWalk walk;  // blocks per partner = heads x 64-row blocks
-  walk.n = E.n;
-  int total = 0;
+  int total = 0;  // blocks of the walk
 #pragma unroll
   for (int i = 0; i < kBwdPerLaunch; ++i) {
-    walk.pre[i] = total;
     if (i < E.n) {
       const BwdQPart QP = qpart_at(partner_at(ei, i));
       total += gsz * ((QP.sq + kBN - 1) / kBN - part_qb0(QP));
     }
   }
-  auto decode = [&](int g, int& pi, int& hi, int& qb) {
-    int blk;
-    walk.decode(g, pi, blk);
-    const int nqb = (qpart_at(partner_at(ei, pi)).sq + kBN - 1) / kBN;
-    hi = __builtin_amdgcn_readfirstlane(blk / nqb);
-    qb = __builtin_amdgcn_readfirstlane(blk % nqb);
-  };
-  auto block_class = [&](int g, int kmin, int kmax, bool ktail) -> int {  // 0 empty, 1 partial, 2 full
-    if constexpr (!MASKED) {
-      return ktail ? 1 : 2;
-    } else {
-      int pi, hi, qb;
-      decode(g, pi, hi, qb);
-      const BwdQPart QP = qpart_at(partner_at(ei, pi));
-      int qmin, qmax;
-      pos_minmax_dev(QP.qp, QP.sq, qb * kBN, min(QP.sq, qb * kBN + kBN), qmin, qmax);
-      if (kmin > qmax) return 0;
-      if (kmax <= qmin && !ktail) return 2;
-      return 1;
-    }
-  };
-  auto next_block = [&](int from) -> int {
-    if constexpr (WALK) {
-      return from < total ? from : total;
-    } else {
-      for (int g = from; g < total; ++g)
-        if (block_class(g, wg_kmin, wg_kmax, false) != 0) return __builtin_amdgcn_readfirstlane(g);
-      return total;
-    }
-  };
+  auto next_block = [&](int from) -> int { return from < total ? from : total; };
 
   // ---- direct-to-LDS loads of one Q block, one dO block and the LSE2/D block ----
   auto load_row = [&](int i) { return ((wave * LPW + i) * 64 + lane) / C::CH; };
@@ -635,39 +504,11 @@ bwd_dkv_kernel(const BwdParams p) {
   uint32_t go[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) go[i] = (uint32_t)(load_row(i) * q_ss + load_col(i)) * 2u;
-  auto issue = [&](int st, int g) {
-    int pi, hi, qb;
-    decode(g, pi, hi, qb);
-    const BwdQPart QP = qpart_at(partner_at(ei, pi));
-    const int h = head_of(g0 + hi);
-    const int64_t off = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)qb * kBN * p.q_ss;
-    const __bf16* qbase = (const __bf16*)QP.q + off;
-    const __bf16* gbase = (const __bf16*)QP.dout + off;
-    const int valid = QP.sq - qb * kBN;
-    if (valid >= kBN) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        lds_dma16(qbase, go[i], lds_addr(&qd_s[0][st][(wave * LPW + i) * 512]));
-        lds_dma16(gbase, go[i], lds_addr(&qd_s[1][st][(wave * LPW + i) * 512]));
-      }
-    } else {  // ragged last block: repeat the last row (finite; its LSE2 is +inf so P = 0)
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const uint32_t o2 = (uint32_t)(min(load_row(i), valid - 1) * q_ss + load_col(i)) * 2u;
-        lds_dma16(qbase, o2, lds_addr(&qd_s[0][st][(wave * LPW + i) * 512]));
-        lds_dma16(gbase, o2, lds_addr(&qd_s[1][st][(wave * LPW + i) * 512]));
-      }
-    }
-    // the 512-byte LSE2/D block: each wave brings 128 bytes with its first 8 lanes
-    const int nqb64 = (QP.sq + kBN - 1) / kBN;
-    const float* lblk = QP.lsed + (((int64_t)b * p.hq + h) * nqb64 + qb) * (2 * kBN);
-    if (lane < 8) lds_dma16(lblk, (uint32_t)(wave * 128 + lane * 16), lds_addr(&ld_s[st][wave * 32]));
-  };
-  // On the walk (no position masks, or one query segment per partition) the
-  // blocks are visited in order, so a cursor (partner, head, 64-row block) and the
-  // bases and mask data of the current (partner, head), refreshed only when those
-  // change, replace the per-block decode: no division or parameter load per block
-  // (a scalar load would also make the wave wait for all of its LDS reads).
+  // The blocks are visited in order, so a cursor (partner, head, 64-row block)
+  // and the bases and mask data of the current (partner, head), refreshed only
+  // when those change, stand in for a per-block decode: no division or parameter
+  // load per block (a scalar load would also make the wave wait for all of its
+  // LDS reads).
   int c_pi = 0, c_hi = 0, c_qb = 0, c_qb0 = 0, c_nqb = 0, c_sq = 0, c_qfull = 0, c_tfirst = 0;
   const __bf16* c_q = nullptr;
   const __bf16* c_g = nullptr;
@@ -678,7 +519,7 @@ bwd_dkv_kernel(const BwdParams p) {
       c_sq = QP.sq;
       c_nqb = (QP.sq + kBN - 1) / kBN;
       c_qb0 = part_qb0(QP);
-      if constexpr (SEG1) {
+      if constexpr (MASKED) {
         c_tfirst = key_ok ? first_row(QP, my_kpos) : 0;
         c_qfull = (first_row(QP, w_kmax) + kBN - 1) / kBN;
       }
@@ -714,7 +555,7 @@ bwd_dkv_kernel(const BwdParams p) {
     }
     if (lane < 8) lds_dma16(c_l + c_qb * (2 * kBN), (uint32_t)(wave * 128 + lane * 16), lds_addr(&ld_s[st][wave * 32]));
     BlkMask bm{1, 0};
-    if constexpr (SEG1) {  // every row of a whole block passes (-2^30)
+    if constexpr (MASKED) {  // every row of a whole block passes (-2^30)
       bm.whole = c_qb >= c_qfull;
       bm.lim = bm.whole ? -(1 << 30) : c_tfirst - c_qb * kBN;
     }
@@ -727,15 +568,8 @@ bwd_dkv_kernel(const BwdParams p) {
     }
     return bm;
   };
-  auto issue_at = [&](int st, int g) -> BlkMask {
-    if constexpr (WALK) {
-      return issue_next(st);
-    } else {
-      issue(st, g);
-      return BlkMask{1, 0};
-    }
-  };
-  if constexpr (WALK) cur_load();
+  auto issue_at = [&](int st, int g) -> BlkMask { return issue_next(st); };
+  cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (2 * LPW + 1)));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW + 1));
@@ -793,21 +627,10 @@ bwd_dkv_kernel(const BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(sc[e] * c2);
     if constexpr (decltype(masked)::value) {
-      if constexpr (SEG1) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {  // row of the block at or after this key's first allowed row
-          const int rr = 32 * u + 16 * (e >> 3) + 8 * hl + (e & 7);
-          pe[e] = rr >= bm.lim ? pe[e] : 0.f;
-        }
-      } else {
-        int pi, hi, qb;
-        decode(g, pi, hi, qb);
-        const BwdQPart QP = qpart_at(partner_at(ei, pi));
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {  // position at a clamped index, then a select
-          const int t = min(QP.sq - 1, qb * kBN + 32 * u + 16 * (e >> 3) + 8 * hl + (e & 7));
-          pe[e] = (my_kpos <= pos_at_dev(QP.qp, t)) ? pe[e] : 0.f;
-        }
+      for (int e = 0; e < 16; ++e) {  // row of the block at or after this key's first allowed row
+        const int rr = 32 * u + 16 * (e >> 3) + 8 * hl + (e & 7);
+        pe[e] = rr >= bm.lim ? pe[e] : 0.f;
       }
     }
     bf16x8 pf[2], dsf[2];
@@ -834,18 +657,10 @@ bwd_dkv_kernel(const BwdParams p) {
   };
   auto half_step = [&](int g, const BlkMask& bm, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu, f32x16& sn,
                        f32x16& dn) {
-    if constexpr (SEG1) {
-      // one straight-line body: the row test costs two VALU ops per element, less
-      // than a second copy of the body costs in registers
-      half_body(std::true_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
-      return;
-    } else if constexpr (MASKED) {
-      if (block_class(g, w_kmin, w_kmax, false) != 2) {
-        half_body(std::true_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
-        return;
-      }
-    }
-    half_body(std::false_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
+    // masked: one straight-line body for every block (the row test costs two VALU
+    // ops per element, less than a second copy of the body costs in registers)
+    if constexpr (MASKED) half_body(std::true_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
+    else half_body(std::false_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
   };
 
   int bj0 = next_block(0);
@@ -926,13 +741,11 @@ int launch_bwd_dq(const BwdParams& p, int head_dim, int total_wgs, void* stream)
   hipStream_t s = (hipStream_t)stream;
   dim3 g(total_wgs), blk(512);
   if (head_dim == 128) {
-    if (p.mask == 1) hipLaunchKernelGGL((bwd_dq_kernel<128, 1>), g, blk, 0, s, p);
-    else if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<128, 2>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_kernel<128, 0>), g, blk, 0, s, p);
+    if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), g, blk, 0, s, p);
   } else {
-    if (p.mask == 1) hipLaunchKernelGGL((bwd_dq_kernel<64, 1>), g, blk, 0, s, p);
-    else if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<64, 2>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_kernel<64, 0>), g, blk, 0, s, p);
+    if (p.mask) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<64, false>), g, blk, 0, s, p);
   }
   return (int)hipGetLastError();
 }
@@ -942,13 +755,11 @@ int launch_bwd_dkv(const BwdParams& p, int head_dim, int total_wgs, void* stream
   hipStream_t s = (hipStream_t)stream;
   dim3 g(total_wgs), blk(256);
   if (head_dim == 128) {
-    if (p.mask == 1) hipLaunchKernelGGL((bwd_dkv_kernel<128, 1>), g, blk, 0, s, p);
-    else if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<128, 2>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dkv_kernel<128, 0>), g, blk, 0, s, p);
+    if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<128, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkv_kernel<128, false>), g, blk, 0, s, p);
   } else {
-    if (p.mask == 1) hipLaunchKernelGGL((bwd_dkv_kernel<64, 1>), g, blk, 0, s, p);
-    else if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<64, 2>), g, blk, 0, s, p);
-    else hipLaunchKernelGGL((bwd_dkv_kernel<64, 0>), g, blk, 0, s, p);
+    if (p.mask) hipLaunchKernelGGL((bwd_dkv_kernel<64, true>), g, blk, 0, s, p);
+    else hipLaunchKernelGGL((bwd_dkv_kernel<64, false>), g, blk, 0, s, p);
   }
   return (int)hipGetLastError();
 }

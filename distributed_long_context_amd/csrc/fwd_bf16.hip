@@ -34,13 +34,14 @@
 //    (factor 256), which keeps the result exact while skipping most rescales.
 //  * Masks are resolved per 64-key block ([Mesh] section 3.7 pair classes):
 //    blocks with no allowed pair for the workgroup are never loaded, blocks with
-//    every pair allowed run unmasked, the rest (and the ragged last block)
-//    compare global positions element by element.  Tiles that are FULL as a
-//    whole run the kernel without masks.  When the key positions are one
-//    segment (contiguous or striped) they grow with the key index, so a lane
-//    keeps only the index of its last allowed key, a wave the count of leading
-//    blocks it sees whole and the workgroup the count of blocks with any allowed
-//    pair; no position data stays live in the loop.
+//    every pair allowed run unmasked, the rest (and a ragged last block) are
+//    masked element by element.  Tiles that are FULL as a whole run the kernel
+//    without masks; the masked kernel takes key positions of one segment
+//    (contiguous or striped; the host runs a tile of several key segments as one
+//    piece per segment), which grow with the key index, so a lane keeps only the
+//    index of its last allowed key, a wave the count of leading blocks it sees
+//    whole and the workgroup the count of blocks with any allowed pair; no
+//    position data stays live in the loop.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <type_traits>
@@ -67,16 +68,14 @@ struct FwdCfg {
   static constexpr int LPW = kBN * CH / 64 / kWaves;  // direct-to-LDS loads per wave per tensor
 };
 
-// MODE 0: no position mask.  MODE 1: the key positions are one segment
-// (global = kgb + t * kst, nondecreasing), so every mask decision reduces to the
-// last allowed key index of a query position.  MODE 2: any position maps.
-template <int D, int MODE>
+// MASKED: causal on positions, the key positions one segment (global = kgb +
+// t * kst, growing with t), so every mask decision reduces to the last allowed
+// key index of a query position.  Without it only a ragged last block is masked.
+template <int D, bool MASKED>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(const FwdParams p) {
   using C = FwdCfg<D>;
-  constexpr bool MASKED = MODE != 0;
-  constexpr bool SEG1 = MODE == 1;
   // K stages in the first half, V stages in the second: kv_s[0][st] is K, kv_s[1][st] is V
   __shared__ __attribute__((aligned(1024))) __bf16 kv_s[2][kStages][C::BLK];
 
@@ -147,41 +146,20 @@ fwd_bf16_kernel(const FwdParams p) {
     if constexpr (MASKED) qpos = ok ? pos_at_dev(T.qp, row) : INT32_MIN;
   }
 
-  // ---- block classes: 0 empty, 1 partial (element mask), 2 full ----
-  const int nkb_all = (T.sk + kBN - 1) / kBN;
-  // one key segment: this lane's last allowed key (-1: none), the number of
-  // leading blocks every row of the wave may see whole, and the number of
-  // blocks with any allowed pair for the workgroup (the rest follow them)
-  int klast = T.sk - 1, kfull_w = 0, nkb_wg = nkb_all;
-  if constexpr (SEG1) {
+  // ---- which blocks, and which keys of a block, a lane may see ----
+  // klast: this lane's last allowed key (-1: none); kfull_w: the leading blocks
+  // every row of the wave sees whole; nkb: the blocks with any allowed pair for
+  // the workgroup (the blocks after them have none).  Without a mask every key
+  // of the partition is allowed and only a ragged last block is partial.
+  int klast = T.sk - 1, kfull_w = T.sk / kBN, nkb = (T.sk + kBN - 1) / kBN;
+  if constexpr (MASKED) {
     const int kgb = T.kp.gb[0], kst = T.kp.st[0];
     auto last_key = [&](int pq) { return pq < kgb ? -1 : min(T.sk - 1, (pq - kgb) / kst); };
     klast = last_key(qpos);
     kfull_w = active ? (last_key(w_pmin) + 1) / kBN : 0;
-    nkb_wg = (last_key(wg_pmax) + kBN) / kBN;
+    nkb = (last_key(wg_pmax) + kBN) / kBN;
   }
-  const int nkb = nkb_wg;
-  auto block_class = [&](int kb, int pmin, int pmax) -> int {
-    const bool tail = kb * kBN + kBN > T.sk;
-    if constexpr (!MASKED) {
-      return tail ? 1 : 2;
-    } else {
-      int kmin, kmax;
-      pos_minmax_dev(T.kp, T.sk, kb * kBN, min(T.sk, kb * kBN + kBN), kmin, kmax);
-      if (kmin > pmax) return 0;
-      if (kmax <= pmin && !tail) return 2;
-      return 1;
-    }
-  };
-  auto next_block = [&](int from) -> int {
-    if constexpr (!MASKED || SEG1) {
-      return from < nkb ? from : nkb;
-    } else {
-      for (int kb = from; kb < nkb; ++kb)
-        if (block_class(kb, wg_pmin, wg_pmax) != 0) return kb;
-      return nkb;
-    }
-  };
+  auto next_block = [&](int from) -> int { return from < nkb ? from : nkb; };
 
   // ---- direct-to-LDS loads: wave instruction i fills LDS chunks [(wave*LPW+i)*64, +64) ----
   auto load_row = [&](int i) { return ((wave * C::LPW + i) * 64 + lane) / C::CH; };
@@ -246,28 +224,16 @@ fwd_bf16_kernel(const FwdParams p) {
   // element mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8
   auto mask_half = [&](int kb, int kb2, f32x16& s) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {  // branch-free: position at a clamped index, then a select
+    for (int e = 0; e < 16; ++e) {  // branch-free select
       const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-      bool ok;
-      if constexpr (SEG1) {
-        ok = key <= klast;
-      } else {
-        ok = key < T.sk;
-        if constexpr (MASKED) ok = ok & (pos_at_dev(T.kp, min(key, T.sk - 1)) <= qpos);
-      }
-      s[e] = ok ? s[e] : -INFINITY;
+      s[e] = key <= klast ? s[e] : -INFINITY;
     }
   };
 
-  // mask (when the block is not fully allowed for this wave) and row max of a half, in log2 units
+  // mask (when the block is not whole for this wave) and row max of a half, in log2 units
   float mb2 = -INFINITY;
   auto half_max = [&](int kb, int kb2, f32x16& s) {
-    if constexpr (SEG1) {
-      if (kb >= kfull_w) mask_half(kb, kb2, s);
-    } else {
-      const int cls = active ? block_class(kb, w_pmin, w_pmax) : 1;
-      if (cls != 2) mask_half(kb, kb2, s);  // partial, or empty for this wave only
-    }
+    if (kb >= kfull_w) mask_half(kb, kb2, s);
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
@@ -402,7 +368,7 @@ fwd_bf16_kernel(const FwdParams p) {
   float wn = has ? 1.0f / ltot : 0.0f;  // weight of this tile's unnormalised sums
   float wo = 0.0f;                      // weight of the output already held (accumulate)
   __bf16* orow = Og + (int64_t)row * p.o_ss;
-  if (p.accumulate) {
+  if (T.accumulate) {
     // fold into (O_old, lse_old): L = ln(e^lse_old + e^lse), O = e^(lse_old-L) O_old + e^(lse-L) O
     const float lo = Lg[row];
     const float mx = fmaxf(lo, lse);
@@ -424,7 +390,7 @@ fwd_bf16_kernel(const FwdParams p) {
       float v4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * wn;
-      if (p.accumulate) {
+      if (T.accumulate) {
         const bf16x4 old = *(const bf16x4*)dst;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v4[i] = __builtin_fmaf(wo, (float)old[i], v4[i]);
@@ -441,13 +407,11 @@ int launch_fwd_bf16(const FwdParams& p, int head_dim, int total_wgs, void* strea
   dim3 grid(total_wgs), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
   if (head_dim == 128) {
-    if (p.mask == 1) hipLaunchKernelGGL((fwd_bf16_kernel<128, 1>), grid, block, 0, s, p);
-    else if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<128, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 0>), grid, block, 0, s, p);
+    if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, s, p);
   } else {
-    if (p.mask == 1) hipLaunchKernelGGL((fwd_bf16_kernel<64, 1>), grid, block, 0, s, p);
-    else if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<64, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, 0>), grid, block, 0, s, p);
+    if (p.mask) hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, s, p);
   }
   return (int)hipGetLastError();
 }

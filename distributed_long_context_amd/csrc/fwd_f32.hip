@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(kRows) fwd_f32_kernel(const FwdParams p) {
   float wo = 0.f;                   // weight of the output already held (accumulate)
   float* Og = (float*)T.o + (int64_t)b * p.o_sb + (int64_t)head * p.o_sh + (int64_t)row * p.o_ss;
   float* Lp = T.lse + (int64_t)b * p.l_sb + (int64_t)head * p.l_sh + row;
-  if (p.accumulate) {
+  if (T.accumulate) {
     // fold into (O_old, lse_old): L = ln(e^lse_old + e^lse), O = e^(lse_old-L) O_old + e^(lse-L) O
     const float lo = *Lp;
     const float mx = fmaxf(lo, lse);
@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(kRows) fwd_f32_kernel(const FwdParams p) {
 #pragma unroll
   for (int c = 0; c < D; c += 4) {
     float4 r = make_float4(o[c] * wn, o[c + 1] * wn, o[c + 2] * wn, o[c + 3] * wn);
-    if (p.accumulate) {
+    if (T.accumulate) {
       const float4 old = *(const float4*)(Og + c);
       r.x = __builtin_fmaf(wo, old.x, r.x);
       r.y = __builtin_fmaf(wo, old.y, r.y);

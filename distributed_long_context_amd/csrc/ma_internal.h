@@ -35,15 +35,15 @@ struct FwdTile {
   int32_t sq, sk;
   int32_t wg_begin;  // first workgroup of this tile in the launch
   int32_t chunks;    // workgroup chunks per (batch, kv head)
+  int32_t accumulate;  // fold into the (O, LSE) held by the output buffers
   KPos qp, kp;
 };
 
 struct FwdParams {
   int32_t ntiles;
   int32_t batch, hq, hkv;
-  int32_t mask;           // 0 none; 1 causal, one key segment; 2 causal, any positions
+  int32_t mask;           // 0 none; 1 causal, one key segment per tile
   int32_t gmax;           // largest number of query heads sharing one KV head
-  int32_t accumulate;     // fold into the (O, LSE) held by the output buffers
   float scale;            // softmax scale
   float scale_log2;       // scale * log2(e)
   int64_t q_sb, q_ss, q_sh;
@@ -122,7 +122,7 @@ struct BwdEntry {        // one group: its own partition and the partner partiti
 struct BwdParams {
   int32_t nentries;
   int32_t batch, hq, hkv, gmax;
-  int32_t mask;  // 0 none; 1 causal, every partner's positions one segment; 2 causal, any positions
+  int32_t mask;  // 0 none; 1 causal, positions of one segment on both sides
   float scale, scale_log2;
   int64_t q_sb, q_ss, q_sh;    // q, o, dout
   int64_t k_sb, k_ss, k_sh;    // k, v
