@@ -133,3 +133,31 @@ def test_reduce_add_rejects_bad_arguments_without_launching():
     assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_ERR_INVALID
     a.n = 0  # no-op before any pointer is looked at
     assert L.mesh_attn_reduce_add(C.byref(a), None) == _abi.MA_OK
+
+
+def test_bwd_workspace_counts_one_segment_pieces():
+    # Under a mask a two-segment Q partition runs as one piece per segment, each with its own
+    # blocked LSE/D slice of ceil(rows / 64) blocks x 2 x 64 floats per (batch, head).
+    L = _abi.lib()
+    B, hq, sq = 2, 4, 130
+    t = (_abi.ma_bwd_tile * 1)()
+    t[0].sq, t[0].sk = sq, 96
+    t[0].q_pos.nseg = 2
+    t[0].q_pos.seg[0].local_begin, t[0].q_pos.seg[0].global_begin, t[0].q_pos.seg[0].stride = 0, 0, 1
+    t[0].q_pos.seg[1].local_begin, t[0].q_pos.seg[1].global_begin, t[0].q_pos.seg[1].stride = 65, 1000, 1
+    t[0].k_pos.nseg = 1
+    t[0].k_pos.seg[0].stride = 1
+    t[0].dq, t[0].dk, t[0].dv = 4096, 8192, 12288
+    a = _abi.ma_tile_bwd_args()
+    a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.scale, a.ntiles = _abi.MA_BF16, B, hq, 2, 128, 0.1, 1
+    a.tiles = C.cast(t, C.POINTER(_abi.ma_bwd_tile))
+    a.q_stride[:] = (sq * hq * 128, hq * 128, 128)
+    a.dq_stride[:] = (sq * hq * 128, hq * 128, 128)
+
+    def blocked(rows):
+        return (B * hq * ((rows + 63) // 64) * 2 * 64 * 4 + 255) // 256 * 256
+
+    a.mask_mode = _abi.MA_MASK_NONE  # positions unused: one piece
+    assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) == blocked(130)
+    a.mask_mode = _abi.MA_MASK_STRIPED_ZIGZAG  # two pieces of 65 rows
+    assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) == 2 * blocked(65)
