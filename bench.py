@@ -47,10 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle sample")
     ap.add_argument("--parts", default="fwd,merge,bwd", help="kernels in the step (all by default)")
-    ap.add_argument("--workloads", default="zigzag,mesh,striped,bwd4",
+    ap.add_argument("--workloads", default="zigzag,mesh,striped,small,bwd4",
                     help="the other workloads timed after the step (comma list; 'none' for none): "
                          "zigzag = causal zigzag share of S=131072, mesh = Mesh 8x8 tile of S=1048576, "
                          "striped = the same Mesh tile under the causal mask with striped positions, "
+                         "small = a 13440-token share cut into tiles of 13440 down to 210 tokens, "
                          "bwd4 = backward of 4 Q partitions x one KV partition of 8192")
     ap.add_argument("--workload-reps", type=int, default=2, help="timed repetitions per workload entry")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -391,6 +392,33 @@ def measure_workloads(names, reps):
         w["bwd_tiles"] = _tf(10.0 * D * HQ * pairs, _timed(lambda: ma.mesh_attn_tile_bwd(btiles, scale, mode, workspace=ws), 1))
         res["mesh-8x8-1m-g9-striped-causal"] = w
         del Q, kg, vg, K, V, dO, O, L, dq, dk, dv, btiles, ws
+        torch.cuda.empty_cache()
+    if "small" in names:
+        # Small-tile efficiency: one Q x KV share of 13440 x 13440 tokens (GQA 32/8, d = 128,
+        # non-causal) cut into (13440 / P)^2 tiles of P x P tokens, all in one forward call, for
+        # the partition sizes of [CHARM+]'s scaling table (13440 down to 210 tokens)
+        S = 13440
+        q = randn((1, S, HQ, D))
+        k = randn((1, S, HKV, D))
+        v = randn((1, S, HKV, D))
+        o_all = torch.empty((S // 210) * S * HQ * D, dtype=torch.bfloat16, device=dev)
+        l_all = torch.empty((S // 210) * HQ * S, dtype=torch.float32, device=dev)
+        w = {}
+        for P in (13440, 3360, 840, 210):
+            n = S // P
+            tiles = []
+            for i in range(n):
+                for j in range(n):
+                    part = i * n + j
+                    o = o_all[part * P * HQ * D:(part + 1) * P * HQ * D].view(1, P, HQ, D)
+                    lse = l_all[part * HQ * P:(part + 1) * HQ * P].view(1, HQ, P)
+                    tiles.append(Tile(q[:, i * P:(i + 1) * P], k[:, j * P:(j + 1) * P], v[:, j * P:(j + 1) * P], o, lse))
+            flop = 4.0 * D * HQ * S * S
+            prep = ma.prepare_tile_fwd(tiles, scale, ma.MA_MASK_NONE)  # argument checks outside the timing
+            w[f"fwd_P{P}"] = _tf(flop, _timed(lambda: ma.launch_prepared_tile_fwd(prep), reps))
+            w[f"fwd_P{P}"]["tiles"] = n * n
+        res["small-tiles-13440"] = w
+        del q, k, v, o_all, l_all, tiles
         torch.cuda.empty_cache()
     if "bwd4" in names:
         S, nq = 8192, 4

@@ -109,9 +109,18 @@ def mesh_attn_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_
                        stream=None, accumulate: bool = False) -> None:
     """Partial (O, LSE) of every tile, enqueued on `stream` (default: current stream).
     With accumulate=True each tile's result is folded into the (O, LSE) its buffers hold."""
+    prepared = prepare_tile_fwd(tiles, scale, mask_mode, head_map, accumulate)
+    if prepared is not None:
+        launch_prepared_tile_fwd(prepared, stream)
+
+
+def prepare_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
+                     accumulate: bool = False):
+    """The checked argument block of mesh_attn_tile_fwd, to be launched (possibly many times) by
+    launch_prepared_tile_fwd; it holds the tensors' addresses, so keep the tensors alive."""
     tiles = list(tiles)
     if not tiles:
-        return
+        return None
     t0 = tiles[0]
     B, _, Hq, d = t0.q.shape
     Hkv = t0.k.shape[2]
@@ -150,7 +159,12 @@ def mesh_attn_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_
     a.v_stride[:] = _bshd_strides(t0.v, "v")
     a.o_stride[:] = _bshd_strides(t0.o, "o")
     a.lse_stride[:] = (t0.lse.stride(0), t0.lse.stride(1))
-    _abi.check(lib().mesh_attn_tile_fwd(C.byref(a), _stream_ptr(stream)), "mesh_attn_tile_fwd")
+    return (a, arr, hm_keep)
+
+
+def launch_prepared_tile_fwd(prepared, stream=None) -> None:
+    """Enqueue a forward prepared by prepare_tile_fwd (the C call only)."""
+    _abi.check(lib().mesh_attn_tile_fwd(C.byref(prepared[0]), _stream_ptr(stream)), "mesh_attn_tile_fwd")
 
 
 # ------------------------------------------------------------------ merge --

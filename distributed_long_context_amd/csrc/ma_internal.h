@@ -24,7 +24,7 @@ struct KPos {
 };
 
 // ---- tile forward ----
-constexpr int kFwdTilesPerLaunch = 8;
+constexpr int kFwdTilesPerLaunch = 16;  // the parameter block stays under the 4 KB kernel-argument limit
 
 struct FwdTile {
   const void* q;
@@ -57,6 +57,7 @@ struct FwdParams {
 };
 
 // launchers (return hipError_t as int)
+static_assert(sizeof(FwdParams) <= 4096, "forward parameters exceed the kernel-argument limit");
 int launch_fwd_bf16(const FwdParams& p, int head_dim, int total_wgs, void* stream);
 int launch_fwd_f32(const FwdParams& p, int head_dim, int total_wgs, void* stream);
 int launch_fill_empty(void* o, float* lse, int dtype, int batch, int sq, int hq, int head_dim,
@@ -134,6 +135,7 @@ struct BwdParams {
   BwdKVPart kvparts[kBwdPerLaunch];
   BwdEntry entries[kBwdPerLaunch];
 };
+static_assert(sizeof(BwdParams) <= 4096, "backward parameters exceed the kernel-argument limit");
 
 // LSE*log2(e) (+inf for rows without an allowed key) and D = rowsum(dO*O) of a Q
 // partition, in the blocked layout the main kernels stage into LDS.
