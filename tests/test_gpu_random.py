@@ -1,0 +1,113 @@
+"""Seeded random sweep of the forward and backward against the fp64 oracle (through the C ABI).
+
+Each case draws its shape, batch, GQA map, head dim, mask mode and position map (contiguous,
+striped, or two to four segments) from a fixed seed, so the sweep is the same on every run;
+the tolerances are the ones of the other parity tests.
+"""
+import math
+import random
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import distributed_long_context_amd as ma  # noqa: E402
+from distributed_long_context_amd import BwdTile, Pos, Tile  # noqa: E402
+from oracle import attn_tile, attn_tile_bwd, merge  # noqa: E402
+from gpu_helpers import BF16_LSE_TOL, BF16_O_TOL, DEV, check_close, gen, host_f64, log, positions  # noqa: E402
+from test_gpu_bwd import check_grad, stored_o_lse  # noqa: E402
+
+import synthetic  # noqa: E402
+
+
+def _segments(rng, n, base):
+    """One to four segments over n local tokens with random global starts and strides."""
+    cuts = sorted(rng.sample(range(1, n), min(n - 1, rng.randint(0, 3)))) if n > 1 else []
+    lbs = [0] + cuts
+    segs = []
+    g = base
+    for lb in lbs:
+        st = rng.choice([1, 1, 2, 3])
+        segs.append((lb, g, st))
+        g += rng.randint(0, 400)
+    return Pos(segs)
+
+
+def _case(seed):
+    rng = random.Random(seed)
+    hq, hkv = rng.choice([(4, 4), (8, 2), (8, 1), (6, 3), (4, 2)])
+    d = rng.choice([64, 128])
+    B = rng.choice([1, 1, 2])
+    sq, sk = rng.randint(1, 260), rng.randint(1, 330)
+    kind = rng.choice(["none", "causal", "striped", "segments"])
+    if kind == "none":
+        return dict(hq=hq, hkv=hkv, d=d, B=B, sq=sq, sk=sk, mode=ma.MA_MASK_NONE, qp=None, kp=None)
+    if kind == "causal":
+        qb, kb = rng.randint(0, 400), rng.randint(0, 400)
+        return dict(hq=hq, hkv=hkv, d=d, B=B, sq=sq, sk=sk, mode=ma.MA_MASK_CAUSAL, qp=Pos([(0, qb, 1)]),
+                    kp=Pos([(0, kb, 1)]))
+    if kind == "striped":
+        N = rng.choice([2, 4, 8])
+        return dict(hq=hq, hkv=hkv, d=d, B=B, sq=sq, sk=sk, mode=ma.MA_MASK_STRIPED_ZIGZAG,
+                    qp=ma.mesh_attn_pos_striped(N, rng.randrange(N)), kp=ma.mesh_attn_pos_striped(N, rng.randrange(N)))
+    return dict(hq=hq, hkv=hkv, d=d, B=B, sq=sq, sk=sk, mode=ma.MA_MASK_STRIPED_ZIGZAG,
+                qp=_segments(rng, sq, rng.randint(0, 300)), kp=_segments(rng, sk, 0))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_forward(seed):
+    c = _case(1000 + seed)
+    log(f"[random fwd {seed}] {c}")
+    B, sq, sk, hq, hkv, d = c["B"], c["sq"], c["sk"], c["hq"], c["hkv"], c["d"]
+    wid = 2000 + seed
+    q, qv = gen(wid, synthetic.T_Q, 0, (B, sq, hq, d))
+    k, kv = gen(wid, synthetic.T_K, 0, (B, sk, hkv, d))
+    v, vv = gen(wid, synthetic.T_V, 0, (B, sk, hkv, d))
+    scale = np.float32(1.0 / math.sqrt(d))
+    causal = c["mode"] != ma.MA_MASK_NONE
+    qpos = positions(c["qp"], sq) if causal else None
+    kpos = positions(c["kp"], sk) if causal else None
+    Oref, Lref = attn_tile(qv, kv, vv, scale, None, causal, qpos, kpos)
+    o = torch.full((B, sq, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, hq, sq), float("nan"), dtype=torch.float32, device=DEV)
+    accumulate = seed % 3 == 0
+    if accumulate:  # fold into a seeded incoming partial
+        oi, oiv = gen(wid, synthetic.T_O_IN, 0, (B, sq, hq, d))
+        li = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, 0, (B, hq, sq)) + 4).astype(np.float32)
+        o.copy_(oi)
+        lse.copy_(torch.from_numpy(li))
+        Oref, Lref = merge([(oiv, li.astype(np.float64)), (Oref, Lref)])
+    ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, c["qp"], c["kp"])], float(scale), c["mode"], accumulate=accumulate)
+    torch.cuda.synchronize()
+    check_close("O", host_f64(o), Oref, BF16_O_TOL, normalised_also=False)
+    check_close("LSE", host_f64(lse), Lref, BF16_LSE_TOL)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_backward(seed):
+    c = _case(3000 + seed)
+    log(f"[random bwd {seed}] {c}")
+    B, sq, sk, hq, hkv, d = c["B"], c["sq"], c["sk"], c["hq"], c["hkv"], c["d"]
+    wid = 4000 + seed
+    q, qv = gen(wid, synthetic.T_Q, 0, (B, sq, hq, d))
+    k, kv = gen(wid, synthetic.T_K, 0, (B, sk, hkv, d))
+    v, vv = gen(wid, synthetic.T_V, 0, (B, sk, hkv, d))
+    do, dov = gen(wid, synthetic.T_DO, 0, (B, sq, hq, d))
+    scale = np.float32(1.0 / math.sqrt(d))
+    causal = c["mode"] != ma.MA_MASK_NONE
+    qpos = positions(c["qp"], sq) if causal else None
+    kpos = positions(c["kp"], sk) if causal else None
+    O, L = attn_tile(qv, kv, vv, scale, None, causal, qpos, kpos)
+    o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+    dq = torch.full((B, sq, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.full((B, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full_like(dk, float("nan"))
+    ma.mesh_attn_tile_bwd([BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv, c["qp"], c["kp"])], float(scale), c["mode"])
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = attn_tile_bwd(qv, kv, vv, o_used, dov, l_used, scale, None, causal, qpos, kpos)
+    check_grad("dQ", dq, dq_r)
+    check_grad("dK", dk, dk_r)
+    check_grad("dV", dv, dv_r)
