@@ -47,8 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle sample")
     ap.add_argument("--parts", default="fwd,merge,bwd", help="kernels in the step (all by default)")
-    ap.add_argument("--workloads", default="zigzag,mesh,striped,small,bwd4",
+    ap.add_argument("--workloads", default="fp32,zigzag,mesh,striped,small,bwd4",
                     help="the other workloads timed after the step (comma list; 'none' for none): "
+                         "fp32 = 1 head, d=64, S=256 in 4 partitions (16 tiles + 4 merges), "
                          "zigzag = causal zigzag share of S=131072, mesh = Mesh 8x8 tile of S=1048576, "
                          "striped = the same Mesh tile under the causal mask with striped positions, "
                          "small = a 13440-token share cut into tiles of 13440 down to 210 tokens, "
@@ -420,6 +421,29 @@ def measure_workloads(names, reps):
         res["small-tiles-13440"] = w
         del q, k, v, o_all, l_all, tiles
         torch.cuda.empty_cache()
+    if "fp32" in names:
+        # the fp32 correctness configuration: 1 head, d = 64, S = 256 in 4 partitions of 64, all 16 tiles
+        # in one call, then a 4-way merge per Q partition (launch-bound; reported, not a roofline target)
+        S1, n1, d1 = 256, 4, 64
+        P1 = S1 // n1
+        q1 = torch.randn((1, S1, 1, d1), generator=gen, device=dev)
+        k1 = torch.randn((1, S1, 1, d1), generator=gen, device=dev)
+        v1 = torch.randn((1, S1, 1, d1), generator=gen, device=dev)
+        outs = [(torch.empty((1, P1, 1, d1), device=dev), torch.empty((1, 1, P1), device=dev)) for _ in range(n1 * n1)]
+        t16 = [Tile(q1[:, i * P1:(i + 1) * P1], k1[:, j * P1:(j + 1) * P1], v1[:, j * P1:(j + 1) * P1], *outs[i * n1 + j])
+               for i in range(n1) for j in range(n1)]
+        mo = [(torch.empty((1, P1, 1, d1), device=dev), torch.empty((1, 1, P1), device=dev)) for _ in range(n1)]
+        s1 = float(1.0 / math.sqrt(d1))
+
+        def c1():
+            ma.mesh_attn_tile_fwd(t16, s1, ma.MA_MASK_NONE)
+            for i in range(n1):
+                row = outs[i * n1:(i + 1) * n1]
+                ma.mesh_attn_merge([x[0] for x in row], [x[1] for x in row], mo[i][0], mo[i][1])
+
+        ms = _timed(c1, max(reps, 5))
+        res["fp32-s256-n4"] = {"fwd_and_merge": {"ms": round(ms, 4), "flop": 4.0 * d1 * S1 * S1,
+                                                 "note": "launch-bound correctness configuration"}}
     if "bwd4" in names:
         S, nq = 8192, 4
         k = randn((1, S, HKV, D))
