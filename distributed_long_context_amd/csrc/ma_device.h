@@ -63,15 +63,6 @@ __device__ __forceinline__ bf16x8 concat_bf16x4(bf16x4 lo, bf16x4 hi) {
   return r;
 }
 
-// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i
-// receives element j from the 8 bytes addressed by lane 4j + i/4, at position i%4.
-__device__ __forceinline__ bf16x4 ds_read_tr16(const __bf16* lds_ptr) {
-  typedef short i16x4 __attribute__((ext_vector_type(4)));
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) void*)lds_ptr));
-  return __builtin_bit_cast(bf16x4, r);
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
 // ---------------------------------------------------------------------------
@@ -173,6 +164,8 @@ __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
 __device__ __forceinline__ f32x4 lds_read_f32x4(uint32_t addr) {
   return *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)addr;
 }
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i
+// receives element j from the 8 bytes addressed by lane 4j + i/4, at position i%4.
 __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
   typedef short i16x4 __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
