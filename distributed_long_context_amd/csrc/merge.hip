@@ -11,17 +11,22 @@
 // Blocks Around the Ring" (m, s, acc rescaled when m grows), which is the same
 // value in exact arithmetic; only the rounding order differs.
 //
-// Layout on the chip (this file's own design): a workgroup owns 64 consecutive
-// rows t of one (b, h), so a wave's LSE reads of one partial fall in one cache
-// line; a thread owns one 16-byte column chunk of 64/RPP rows.  Partials are
-// taken in groups of G (2, 4 or 8, the smallest that covers k up to 8) whose
-// loads are all issued before any use: indices past k repeat the last partial
-// (a valid address) and get weight 0, so there are no branches between the
-// loads.  The partial outputs are read once and the merged output is not read
-// again by this kernel, so loads and stores are marked nontemporal (streaming):
-// with the MALL flushed before each merge that took the 2-way merge of 8192
-// rows x 32 heads from 3.1 to 5.4 TB/s and the 27-way merge of 4096 x 32 from
-// 3.8 to 4.7 TB/s on MI355X (the 8-way merges of 16384 x 32 stay near 5.0).
+// Layout on the chip (this file's own design): a workgroup of 256 threads owns a
+// small tile of rows, TH = 2 adjacent heads x 8 consecutive positions t (16 rows
+// at d = 128 in bf16; the tile grows to one full pass of the workgroup for
+// smaller rows), and a thread one 16-byte column chunk of a row.  Consecutive
+// workgroups take consecutive head pairs at the same positions, so the
+// workgroups in flight stream adjacent memory of every partial.  Partials are
+// taken in groups of G (2, 4 or 8, the smallest that covers k up to 8); the loads
+// of the next group are issued before the current one is folded, and within a
+// group all loads come before any use: indices past k repeat the last partial (a
+// valid address) with weight 0, so nothing branches between the loads.  The
+// partial outputs are read once and the merged output is not read again here, so
+// loads and stores are nontemporal (streaming).  Measured on MI355X with the
+// 256 MB MALL flushed before each merge, against 64-row workgroups of one head:
+// 2-way merge of 8192 x 32 heads 5.35 -> 5.7 TB/s, 27-way of 4096 x 32
+// 4.7 -> 5.3 TB/s, 8-way of 16384 x 32 4.9 -> 6.45 TB/s; small workgroups also
+// leave no half-empty last round of workgroups.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -33,42 +38,57 @@ namespace ma {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 64;  // rows t per workgroup
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D, bool BF16, int G>
+// rows of one workgroup: at least one full pass of the 256 threads, and 16
+template <int D, bool BF16>
+struct MergeTile {
+  static constexpr int ES = BF16 ? 2 : 4;      // element size
+  static constexpr int CPR = D * ES / 16;      // 16-byte chunks per row
+  static constexpr int RPP = kThreads / CPR;   // rows per pass
+  static constexpr int ROWS = RPP > 16 ? RPP : 16;
+  static constexpr int PASSES = ROWS / RPP;
+};
+
+template <int D, bool BF16, int G, int TH>
 __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeParams p) {
-  constexpr int ES = BF16 ? 2 : 4;            // element size
-  constexpr int CPR = D * ES / 16;            // 16-byte chunks per row
-  constexpr int RPP = kThreads / CPR;         // rows per pass
-  constexpr int PASSES = kRows / RPP;
-  constexpr int NE = BF16 ? 8 : 4;            // elements per chunk
-  const int nblk = (p.seqlen + kRows - 1) / kRows;
-  const int blk = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
-  const int h = bh % p.heads, b = bh / p.heads;
+  using T = MergeTile<D, BF16>;
+  constexpr int ES = T::ES, CPR = T::CPR, RPP = T::RPP;
+  constexpr int TT = T::ROWS / TH;             // positions per workgroup
+  constexpr int NE = BF16 ? 8 : 4;             // elements per chunk
+  const int nth = p.heads / TH;
+  const int ntb = (p.seqlen + TT - 1) / TT;
+  const int hg = blockIdx.x % nth;
+  const int tb = (blockIdx.x / nth) % ntb;
+  const int b = blockIdx.x / (nth * ntb);
   const int c = threadIdx.x % CPR, rs = threadIdx.x / CPR;
-  const int64_t lbase = (int64_t)b * p.l_sb + (int64_t)h * p.l_sh;
-  const int64_t obase = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + c * (16 / ES);
 #pragma unroll
-  for (int j = 0; j < PASSES; ++j) {
-    const int t = blk * kRows + rs + j * RPP;
-    if (t >= p.seqlen) break;
-    const int64_t off = obase + (int64_t)t * p.o_ss;  // elements
+  for (int j = 0; j < T::PASSES; ++j) {
+    const int r = rs + j * RPP;  // row of the tile: head r % TH, position r / TH
+    const int t = tb * TT + r / TH, h = hg * TH + r % TH;
+    if (t >= p.seqlen) break;    // t grows with j
+    const int64_t lbase = (int64_t)b * p.l_sb + (int64_t)h * p.l_sh;
+    const int64_t off = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)t * p.o_ss + c * (16 / ES);  // elements
     float acc[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[e] = 0.f;
     float m = -INFINITY, s = 0.f;  // running max and rescaled denominator
-    for (int i0 = 0; i0 < p.k; i0 += G) {
-      float l[G];
-      uint4 raw[G];
+    auto load_group = [&](int i0, float (&l)[G], u32x4 (&raw)[G]) {
 #pragma unroll
       for (int u = 0; u < G; ++u) {
         const int i = min(i0 + u, p.k - 1);
         l[u] = p.lse_in[i][lbase + t];
-        const u32x4 r = __builtin_nontemporal_load((const u32x4*)((const char*)p.o_in[i] + off * ES));
-        raw[u] = make_uint4(r.x, r.y, r.z, r.w);
+        raw[u] = __builtin_nontemporal_load((const u32x4*)((const char*)p.o_in[i] + off * ES));
       }
+    };
+    float l[G];
+    u32x4 raw[G];
+    load_group(0, l, raw);
+    for (int i0 = 0; i0 < p.k; i0 += G) {
+      float ln[G];
+      u32x4 rn[G];
+      const bool more = i0 + G < p.k;  // uniform
+      if (more) load_group(i0 + G, ln, rn);
 #pragma unroll
       for (int u = 0; u < G; ++u)
         if (i0 + u >= p.k) l[u] = -INFINITY;  // repeated partial: weight 0
@@ -98,13 +118,20 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeParams p) {
         }
       }
       m = mn;
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          l[u] = ln[u];
+          raw[u] = rn[u];
+        }
+      }
     }
     const bool has = m != -INFINITY;
     const float inv = has ? 1.0f / s : 0.f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[e] *= inv;
-    // every lane of this row has read all partials (same wave) before the row's
-    // first lane writes, so o_out == o_in[0] and lse_out == lse_in[0] are safe
+    // the CPR lanes of this row are in one wave and have read all partials before
+    // any of them writes, so o_out == o_in[0] and lse_out == lse_in[0] are safe
     if (BF16) {
       const bf16x8 pk = pack_bf16x8(acc);
       __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pk), (u32x4*)((__bf16*)p.o_out + off));
@@ -116,29 +143,31 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(const MergeParams p) {
   }
 }
 
+template <int D, bool BF16, int TH>
+int launch_th(const MergeParams& p, hipStream_t s) {
+  constexpr int TT = MergeTile<D, BF16>::ROWS / TH;
+  const int64_t blocks = (int64_t)p.batch * (p.heads / TH) * ((p.seqlen + TT - 1) / TT);
+  if (blocks <= 0) return 0;
+  if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
+  if (p.k <= 2) hipLaunchKernelGGL((merge_kernel<D, BF16, 2, TH>), grid, dim3(kThreads), 0, s, p);
+  else if (p.k <= 4) hipLaunchKernelGGL((merge_kernel<D, BF16, 4, TH>), grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((merge_kernel<D, BF16, 8, TH>), grid, dim3(kThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+// head pairs when the head count is even, single heads otherwise
 template <int D, bool BF16>
-void launch_g(const MergeParams& p, dim3 grid, hipStream_t s) {
-  if (p.k <= 2) hipLaunchKernelGGL((merge_kernel<D, BF16, 2>), grid, dim3(kThreads), 0, s, p);
-  else if (p.k <= 4) hipLaunchKernelGGL((merge_kernel<D, BF16, 4>), grid, dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((merge_kernel<D, BF16, 8>), grid, dim3(kThreads), 0, s, p);
+int launch_d(const MergeParams& p, hipStream_t s) {
+  return p.heads % 2 == 0 ? launch_th<D, BF16, 2>(p, s) : launch_th<D, BF16, 1>(p, s);
 }
 
 }  // namespace
 
 int launch_merge(const MergeParams& p, int dtype, int head_dim, void* stream) {
-  const int64_t blocks = (int64_t)p.batch * p.heads * ((p.seqlen + kRows - 1) / kRows);
-  if (blocks <= 0) return 0;
-  if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
-  dim3 grid((unsigned)blocks);
   hipStream_t s = (hipStream_t)stream;
-  if (head_dim == 128) {
-    if (dtype == MA_BF16) launch_g<128, true>(p, grid, s);
-    else launch_g<128, false>(p, grid, s);
-  } else {
-    if (dtype == MA_BF16) launch_g<64, true>(p, grid, s);
-    else launch_g<64, false>(p, grid, s);
-  }
-  return (int)hipGetLastError();
+  if (head_dim == 128) return dtype == MA_BF16 ? launch_d<128, true>(p, s) : launch_d<128, false>(p, s);
+  return dtype == MA_BF16 ? launch_d<64, true>(p, s) : launch_d<64, false>(p, s);
 }
 
 }  // namespace ma

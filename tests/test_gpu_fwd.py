@@ -182,12 +182,15 @@ def test_fp32_mha_s256_four_partitions():
         check_close(f"merged LSE[{i}]", host_f64(l_out), Lfull[:, :, i * P:(i + 1) * P], F32_TOL)
 
 
-@pytest.mark.parametrize("k,dtype,d", [(1, "bf16", 128), (2, "bf16", 64), (6, "bf16", 128), (27, "bf16", 128),
-                                       (64, "bf16", 128), (5, "f32", 64), (9, "f32", 128)])
-def test_merge_matches_oracle(k, dtype, d):
-    B, S, H = 2, 77, 3
-    log(f"[merge] k={k} dtype={dtype} d={d}")
-    wid = 700 + k
+@pytest.mark.parametrize("k,dtype,d,H", [(1, "bf16", 128, 3), (2, "bf16", 64, 3), (6, "bf16", 128, 3),
+                                         (27, "bf16", 128, 3), (64, "bf16", 128, 3), (5, "f32", 64, 3),
+                                         (9, "f32", 128, 3), (3, "bf16", 128, 4), (12, "bf16", 64, 6),
+                                         (2, "f32", 128, 2), (10, "f32", 64, 4)])
+def test_merge_matches_oracle(k, dtype, d, H):
+    """Odd head counts take one head per workgroup tile, even ones head pairs; 77 rows leave a ragged tile."""
+    B, S = 2, 77
+    log(f"[merge] k={k} dtype={dtype} d={d} H={H}")
+    wid = 700 + k + 100 * (H % 2 == 0)
     Os, Ls, Oh, Lh = [], [], [], []
     for r in range(k):
         o, ov = gen(wid, synthetic.T_O_IN, r, (B, S, H, d), dtype)
@@ -212,6 +215,28 @@ def test_merge_matches_oracle(k, dtype, d):
     check_close("LSE", host_f64(l_out), Lref, tol_l)
     if k > 3:
         assert torch.all(o_out[0, 7, 2].float() == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_head_major_strides(d):
+    """Partials and output as (B, H, S, d) storage seen through [B, S, H, d] views (row stride d,
+    head stride S*d): the kernel follows the strides it is given."""
+    B, S, H, k = 2, 45, 4, 5
+    log(f"[merge head-major strides] d={d}")
+    Os, Ls, Oh, Lh = [], [], [], []
+    for r in range(k):
+        o, ov = gen(900 + d, synthetic.T_O_IN, r, (B, S, H, d))
+        Os.append(o.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3))
+        Oh.append(ov)
+        lv = (synthetic.normal_f32(900 + d, synthetic.T_LSE_IN, r, (B, H, S)) * 2 + 4).astype(np.float32)
+        Ls.append(torch.from_numpy(lv).to(DEV)); Lh.append(lv.astype(np.float64))
+    o_out = torch.empty((B, H, S, d), dtype=torch.bfloat16, device=DEV).permute(0, 2, 1, 3)
+    l_out = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    ma.mesh_attn_merge(Os, Ls, o_out, l_out)
+    torch.cuda.synchronize()
+    Oref, Lref = merge(list(zip(Oh, Lh)))
+    check_close("O", host_f64(o_out), Oref, BF16_O_TOL, normalised_also=False)
+    check_close("LSE", host_f64(l_out), Lref, BF16_LSE_TOL)
 
 
 def test_merge_in_place():
