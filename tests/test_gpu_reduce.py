@@ -18,7 +18,8 @@ from test_gpu_bwd import check_grad, stored_o_lse  # noqa: E402
 import synthetic  # noqa: E402
 
 
-@pytest.mark.parametrize("k,n", [(1, 4096), (3, 5), (8, 1000003), (9, 77), (64, 4099)])
+@pytest.mark.parametrize("k,n", [(1, 4096), (2, 1 << 20), (3, 5), (4, 3), (8, 1000003), (9, 77), (17, 8195),
+                                 (64, 4099)])
 def test_reduce_add_matches_oracle(k, n):
     log(f"[reduce_add] k={k} n={n}")
     parts = [synthetic.normal_f32(1100 + k, synthetic.T_O_IN, r, (n,)) for r in range(k)]
