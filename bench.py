@@ -54,7 +54,7 @@ def parse():
                          "striped = the same Mesh tile under the causal mask with striped positions, "
                          "small = a 13440-token share cut into tiles of 13440 down to 210 tokens, "
                          "bwd4 = backward of 4 Q partitions x one KV partition of 8192")
-    ap.add_argument("--workload-reps", type=int, default=2, help="timed repetitions per workload entry")
+    ap.add_argument("--workload-reps", type=int, default=3, help="timed repetitions per workload entry (median)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB (outside the timed "
                          "region): the reference launch for scaling HBM byte counters")
@@ -185,20 +185,26 @@ def incoming_lse():
 
 
 def _timed(fn, reps, warmup=1):
-    """Mean milliseconds of fn() over `reps` runs after `warmup`, from events on the current stream."""
+    """Median milliseconds of fn() over `reps` runs after `warmup`, from events on the current stream.
+
+    The runs are enqueued back to back and the host synchronises once at the end, so a host-side
+    pause between recording an event and launching the work (seen as rare 30-40 ms outliers when
+    every run synchronised) is hidden behind the queued work; the median drops any that remain."""
     import torch
     for _ in range(warmup):
         fn()
     stream = torch.cuda.current_stream()
-    ts = []
+    evs = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
         e1.record(stream)
-        e1.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    return sum(ts) / len(ts)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    mid = len(ts) // 2
+    return ts[mid] if len(ts) % 2 else 0.5 * (ts[mid - 1] + ts[mid])
 
 
 def _tf(flop, ms):

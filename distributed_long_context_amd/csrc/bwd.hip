@@ -152,7 +152,8 @@ bwd_dq_kernel(const BwdParams p) {
   const int local = w - E.wg_begin;
   const int kvh = local % p.hkv;
   const int rest = local / p.hkv;
-  const int chunk = rest % E.chunks;
+  // causal tiles: later query rows see more keys, so the heaviest chunks go first
+  const int chunk = MASKED ? E.chunks - 1 - rest % E.chunks : rest % E.chunks;
   const int b = rest / E.chunks;
   if (b >= p.batch) return;
   const int g0 = kv_first_at(kvh);

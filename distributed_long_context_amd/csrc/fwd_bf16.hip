@@ -98,7 +98,8 @@ fwd_bf16_kernel(const FwdParams p) {
   const int local = w - T.wg_begin;
   const int kvh = local % p.hkv;
   const int rest = local / p.hkv;
-  const int chunk = rest % T.chunks;
+  // causal tiles: later query rows see more keys, so the heaviest chunks go first
+  const int chunk = MASKED ? T.chunks - 1 - rest % T.chunks : rest % T.chunks;
   const int b = rest / T.chunks;
   if (b >= p.batch) return;  // padding workgroup (uniform)
   const int g0 = p.kv_first[kvh];
