@@ -201,11 +201,12 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     ft.sq = (int32_t)t.sq;
     ft.sk = (int32_t)t.sk;
     ft.accumulate = acc;
-    if (m != 0) {
+    if (m != 0) {  // key positions are one segment here (split below)
       to_kpos(t.q_pos, ft.qp);
-      to_kpos(t.k_pos, ft.kp);
+      ft.kgb = (int32_t)t.k_pos.seg[0].global_begin;
+      ft.kst = (int32_t)t.k_pos.seg[0].stride;
     } else {
-      ft.qp.nseg = ft.kp.nseg = 1;
+      ft.qp.nseg = 1;
     }
     int64_t wgs;
     if (bf16) {

@@ -90,8 +90,11 @@ fwd_bf16_kernel(const FwdParams p) {
 
   // ---- which tile / batch / KV head / query block ----
   const int w = blockIdx.x;
+  // tile of this workgroup: the count of later tiles that start at or before it
+  // (independent scalar loads instead of a chain of dependent ones)
   int ti = 0;
-  while (ti + 1 < p.ntiles && w >= p.tiles[ti + 1].wg_begin) ++ti;
+#pragma unroll
+  for (int j = 1; j < kFwdTilesPerLaunch; ++j) ti += (j < p.ntiles && w >= p.tiles[j].wg_begin) ? 1 : 0;
   // by value, with a provably uniform index: the parameter block stays in the
   // kernel-argument segment (scalar loads) instead of being copied to scratch
   const FwdTile T = p.tiles[__builtin_amdgcn_readfirstlane(ti)];
@@ -157,7 +160,7 @@ fwd_bf16_kernel(const FwdParams p) {
   // of the partition is allowed and only a ragged last block is partial.
   int klast = T.sk - 1, kfull_w = T.sk / kBN, nkb = (T.sk + kBN - 1) / kBN;
   if constexpr (MASKED) {
-    const int kgb = T.kp.gb[0], kst = T.kp.st[0];
+    const int kgb = T.kgb, kst = T.kst;
     auto last_key = [&](int pq) { return pq < kgb ? -1 : min(T.sk - 1, (pq - kgb) / kst); };
     klast = last_key(qpos);
     kfull_w = active ? (last_key(w_pmin) + 1) / kBN : 0;

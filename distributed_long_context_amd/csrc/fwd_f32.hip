@@ -27,8 +27,9 @@ __global__ void __launch_bounds__(kRows) fwd_f32_kernel(const FwdParams p) {
 
   const int lane = threadIdx.x;
   const int w = blockIdx.x;
-  int ti = 0;
-  while (ti + 1 < p.ntiles && w >= p.tiles[ti + 1].wg_begin) ++ti;
+  int ti = 0;  // the count of later tiles that start at or before this workgroup
+#pragma unroll
+  for (int j = 1; j < kFwdTilesPerLaunch; ++j) ti += (j < p.ntiles && w >= p.tiles[j].wg_begin) ? 1 : 0;
   const FwdTile& T = p.tiles[ti];
   // workgroup -> (batch, query head, row block); T.chunks = row blocks
   int local = w - T.wg_begin;
@@ -66,10 +67,8 @@ __global__ void __launch_bounds__(kRows) fwd_f32_kernel(const FwdParams p) {
   const float* Kg = (const float*)T.k + (int64_t)b * p.k_sb + (int64_t)kv * p.k_sh;
   const float* Vg = (const float*)T.v + (int64_t)b * p.v_sb + (int64_t)kv * p.v_sh;
   for (int kb = 0; kb < T.sk; kb += kKB) {
-    const int u1 = min(T.sk, kb + kKB);
     if (p.mask) {
-      int kmin, kmax;
-      pos_minmax_dev(T.kp, T.sk, kb, u1, kmin, kmax);
+      const int kmin = T.kgb + kb * T.kst;  // key positions grow with the index (one segment)
       if (kmin > pmax) continue;  // no allowed pair in this block (uniform)
     }
     __syncthreads();
@@ -85,7 +84,7 @@ __global__ void __launch_bounds__(kRows) fwd_f32_kernel(const FwdParams p) {
     }
     if (lane < kKB) {
       const int key = kb + lane;
-      kpos_s[lane] = key >= T.sk ? INT32_MAX : (p.mask ? pos_at_dev(T.kp, key) : INT32_MIN);
+      kpos_s[lane] = key >= T.sk ? INT32_MAX : (p.mask ? T.kgb + key * T.kst : INT32_MIN);
     }
     __syncthreads();
     float s[kKB];

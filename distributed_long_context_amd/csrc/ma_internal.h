@@ -24,7 +24,7 @@ struct KPos {
 };
 
 // ---- tile forward ----
-constexpr int kFwdTilesPerLaunch = 16;  // the parameter block stays under the 4 KB kernel-argument limit
+constexpr int kFwdTilesPerLaunch = 30;  // the parameter block stays under the 4 KB kernel-argument limit
 
 struct FwdTile {
   const void* q;
@@ -33,10 +33,11 @@ struct FwdTile {
   void* o;
   float* lse;
   int32_t sq, sk;
-  int32_t wg_begin;  // first workgroup of this tile in the launch
-  int32_t chunks;    // workgroup chunks per (batch, kv head)
+  int32_t wg_begin;    // first workgroup of this tile in the launch
+  int32_t chunks;      // workgroup chunks per (batch, kv head)
   int32_t accumulate;  // fold into the (O, LSE) held by the output buffers
-  KPos qp, kp;
+  int32_t kgb, kst;    // key positions, one segment: global = kgb + kst * t (the host splits the others)
+  KPos qp;
 };
 
 struct FwdParams {

@@ -148,6 +148,40 @@ def test_many_tiles_one_call():
         check_close("LSE", host_f64(t.lse), Lref, BF16_LSE_TOL)
 
 
+@pytest.mark.parametrize("dtype,mode", [("bf16", "causal"), ("bf16", "striped"), ("bf16", "none"), ("f32", "striped")])
+def test_many_tiles_in_one_call(dtype, mode):
+    """64 tiles of one call (8 x 8 partitions of 40 tokens, GQA 4/2, d = 64) cross the batches of
+    tiles one launch holds, FULL and PARTIAL tiles interleaved (and EMPTY ones skipped), each
+    tile's (O, LSE) checked against the oracle."""
+    log(f"[many tiles] {dtype} {mode}")
+    n, P, hq, hkv, d = 8, 40, 4, 2, 64
+    mask = {"causal": ma.MA_MASK_CAUSAL, "striped": ma.MA_MASK_STRIPED_ZIGZAG, "none": ma.MA_MASK_NONE}[mode]
+    scale = np.float32(0.125)
+    qs = [gen(1500 + n, synthetic.T_Q, i, (1, P, hq, d), dtype) for i in range(n)]
+    ks = [gen(1500 + n, synthetic.T_K, j, (1, P, hkv, d), dtype) for j in range(n)]
+    vs = [gen(1500 + n, synthetic.T_V, j, (1, P, hkv, d), dtype) for j in range(n)]
+    pos = (lambda i: ma.mesh_attn_pos_striped(n, i)) if mode == "striped" else (lambda i: Pos([(0, i * P, 1)]))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tiles, refs = [], []
+    for i in range(n):
+        for j in range(n):
+            qp, kp = pos(i), pos(j)
+            if mode != "none" and ma.mesh_attn_classify(qp, P, kp, P, mask) == ma.MA_TILE_EMPTY:
+                continue
+            o = torch.full((1, P, hq, d), float("nan"), dtype=tdt, device=DEV)
+            lse = torch.full((1, hq, P), float("nan"), dtype=torch.float32, device=DEV)
+            tiles.append(Tile(qs[i][0], ks[j][0], vs[j][0], o, lse, qp, kp))
+            causal = mode != "none"
+            refs.append(attn_tile(qs[i][1], ks[j][1], vs[j][1], scale, None, causal,
+                                  positions(qp, P) if causal else None, positions(kp, P) if causal else None))
+    assert len(tiles) > 30
+    run_fwd(tiles, float(scale), mask)
+    tol_o, tol_l = (BF16_O_TOL, BF16_LSE_TOL) if dtype == "bf16" else (F32_TOL, F32_TOL)
+    for t, (Oref, Lref) in zip(tiles, refs):
+        check_close("O", host_f64(t.o), Oref, tol_o, normalised_also=False)
+        check_close("LSE", host_f64(t.lse), Lref, tol_l)
+
+
 def test_fp32_mha_s256_four_partitions():
     # fp32, 1 head, d=64, S=256 in 4 partitions of 64: all 16 tiles, then a 4-way merge per Q partition,
     # compared with unsplit attention (tolerance 1e-5 on O and LSE).
