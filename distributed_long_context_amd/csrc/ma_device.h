@@ -138,8 +138,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // states that, it is free when they already sit in scalar registers).  Written as
 // inline asm so that the compiler does not add vmcnt(0) waits in front of every
 // LDS read; the kernels order these loads themselves with s_waitcnt vmcnt and a
-// barrier.  M0 carries the LDS address and is restored, so the compiler's own
-// view of M0 stays valid.
+// barrier.  M0 carries the LDS address and is declared clobbered, so the compiler
+// sets it again wherever it relies on it (in these kernels nowhere: no save and
+// restore around each load).
 __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff_bytes, uint32_t lds_dst) {
   const uint64_t g = (uint64_t)(uintptr_t)gbase;
   // readfirstlane returns int: go through uint32_t so the low word is not sign-extended
@@ -147,16 +148,13 @@ __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff_bytes
   const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(g >> 32));
   const uint64_t gu = ((uint64_t)ghi << 32) | (uint64_t)glo;
   const uint32_t lu = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_dst);
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff_bytes), "s"(gu), "s"(lu)
-      : "memory");
+      : "memory", "m0");
 }
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
