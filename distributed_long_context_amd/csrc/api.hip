@@ -157,29 +157,31 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
 
   const bool bf16 = a->dtype == MA_BF16;
   const int64_t esize = bf16 ? 2 : 4;
-  // Tiles go to one of two launches by how much masking they need: FULL tiles (and
-  // every tile without a mask) run the unmasked kernel, PARTIAL ones the masked
-  // kernel, whose key positions must be one segment: a tile whose key positions
-  // have several segments is run as one piece per segment (the keys of a segment
-  // are contiguous rows), the first piece with any allowed pair writing the
-  // output and the later ones folding into it.  A tile naming the output of one
-  // already queued waits for it.
-  FwdParams bp[2];
-  int bn[2] = {0, 0}, bwg[2] = {0, 0};
-  for (int m = 0; m < 2; ++m) {
+  // Tiles go to one of four launches: by how much masking they need (bit 0) and, in
+  // bf16, by length (bit 1).  FULL tiles (and every tile without a mask) run the
+  // unmasked kernel, PARTIAL ones the masked kernel, whose key positions must be one
+  // segment: a tile whose key positions have several segments is run as one piece
+  // per segment (the keys of a segment are contiguous rows), the first piece with
+  // any allowed pair writing the output and the later ones folding into it.  Tiles
+  // of at most kFwdSmallBlocks key blocks run the four-wave kernel.  A tile naming
+  // the output of one already queued waits for it.
+  FwdParams bp[4];
+  int bn[4] = {0, 0, 0, 0}, bwg[4] = {0, 0, 0, 0};
+  for (int m = 0; m < 4; ++m) {
     bp[m] = p;
-    bp[m].mask = m;
+    bp[m].mask = m & 1;
   }
   auto flush = [&](int m) -> int {
     if (bn[m] == 0) return MA_OK;
     bp[m].ntiles = bn[m];
-    int e = bf16 ? launch_fwd_bf16(bp[m], a->head_dim, bwg[m], stream) : launch_fwd_f32(bp[m], a->head_dim, bwg[m], stream);
+    int e = bf16 ? launch_fwd_bf16(bp[m], a->head_dim, m & 2 ? 4 : 8, bwg[m], stream)
+                 : launch_fwd_f32(bp[m], a->head_dim, bwg[m], stream);
     bn[m] = 0;
     bwg[m] = 0;
     return check_hip(e, "tile_fwd launch");
   };
   auto flush_all = [&]() -> int {
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < 4; ++m) {
       int r = flush(m);
       if (r) return r;
     }
@@ -188,20 +190,21 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   // queue one (sub-)tile; cls is its class, acc its accumulate flag
   auto enqueue = [&](const ma_tile& t, int cls, int acc) -> int {
     bool dup = false;
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 4; ++k)
       for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == t.o || bp[k].tiles[j].lse == t.lse;
     if (dup) {
       int r = flush_all();
       if (r) return r;
     }
-    const int m = cls == MA_TILE_FULL ? 0 : 1;
+    const bool small = bf16 && (t.sk + 63) / 64 <= kFwdSmallBlocks;
+    const int m = (cls == MA_TILE_FULL ? 0 : 1) | (small ? 2 : 0);
     FwdTile& ft = bp[m].tiles[bn[m]];
     std::memset(&ft, 0, sizeof(ft));
     ft.q = t.q; ft.k = t.k; ft.v = t.v; ft.o = t.o; ft.lse = t.lse;
     ft.sq = (int32_t)t.sq;
     ft.sk = (int32_t)t.sk;
     ft.accumulate = acc;
-    if (m != 0) {  // key positions are one segment here (split below)
+    if (m & 1) {  // key positions are one segment here (split below)
       to_kpos(t.q_pos, ft.qp);
       ft.kgb = (int32_t)t.k_pos.seg[0].global_begin;
       ft.kst = (int32_t)t.k_pos.seg[0].stride;
@@ -210,9 +213,10 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     }
     int64_t wgs;
     if (bf16) {
-      // 8 waves of 32 query rows per workgroup; units are (32-row block, head of the group)
+      // 8 (or 4) waves of 32 query rows per workgroup; units are (32-row block, head of the group)
+      const int waves = small ? 4 : 8;
       const int64_t nqb = (t.sq + 31) / 32;
-      ft.chunks = (int32_t)((nqb * p.gmax + 7) / 8);
+      ft.chunks = (int32_t)((nqb * p.gmax + waves - 1) / waves);
       wgs = (int64_t)a->batch * a->hkv * ft.chunks;
       wgs = (wgs + 7) / 8 * 8;  // keep each tile's first workgroup on XCD 0
     } else {

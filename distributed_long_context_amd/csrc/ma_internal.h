@@ -59,7 +59,10 @@ struct FwdParams {
 
 // launchers (return hipError_t as int)
 static_assert(sizeof(FwdParams) <= 4096, "forward parameters exceed the kernel-argument limit");
-int launch_fwd_bf16(const FwdParams& p, int head_dim, int total_wgs, void* stream);
+// bf16 forward: waves = 8 (five-stage ring, one workgroup per CU) or 4 (two-stage ring,
+// two workgroups per CU; for tiles of at most kFwdSmallBlocks key blocks)
+constexpr int kFwdSmallBlocks = 16;
+int launch_fwd_bf16(const FwdParams& p, int head_dim, int waves, int total_wgs, void* stream);
 int launch_fwd_f32(const FwdParams& p, int head_dim, int total_wgs, void* stream);
 int launch_fill_empty(void* o, float* lse, int dtype, int batch, int sq, int hq, int head_dim,
                       int64_t o_sb, int64_t o_ss, int64_t o_sh, int64_t l_sb, int64_t l_sh, void* stream);

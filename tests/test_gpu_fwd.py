@@ -89,6 +89,29 @@ def test_fwd_bf16_small_shapes(sq, sk, hq, hkv, d, mname):
         assert np.all(Og[b, t, h] == 0.0)
 
 
+@pytest.mark.parametrize("sk", [960, 1024, 1025, 1090])
+@pytest.mark.parametrize("mname", ["none", "causal_offset", "striped"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_bf16_kernel_size_switch(sk, mname, d):
+    """Key counts on both sides of the switch between the four-wave kernel (at most 16 key
+    blocks: 960, 1024) and the eight-wave kernel (1025, 1090), each also with a ragged last
+    block, unmasked and masked, against the oracle."""
+    mode, qpf, kpf = MASKS[mname]
+    sq, hq, hkv = 200, 8, 2
+    wid = 1700 + sk + d
+    log(f"[fwd size switch] sk={sk} mask={mname} d={d} seed={wid}")
+    (q, k, v, o, lse), (qv, kv, vv) = make_case(wid, sq, sk, hq, hkv, d)
+    qp = qpf(sq, sk) if qpf else None
+    kp = kpf(sq, sk) if kpf else None
+    scale = 1.0 / math.sqrt(d)
+    run_fwd([Tile(q, k, v, o, lse, qp, kp)], scale, mode)
+    causal = mode != ma.MA_MASK_NONE
+    Oref, Lref = attn_tile(qv, kv, vv, np.float32(scale), None, causal,
+                           positions(qp, sq) if causal else None, positions(kp, sk) if causal else None)
+    check_close("O", host_f64(o), Oref, BF16_O_TOL)
+    check_close("LSE", host_f64(lse), Lref, BF16_LSE_TOL)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fwd_bf16_head_map_and_batch(d):
     sq, sk, hq, hkv, B = 130, 200, 6, 3, 2
