@@ -41,7 +41,9 @@ def _case(seed):
     hq, hkv = rng.choice([(4, 4), (8, 2), (8, 1), (6, 3), (4, 2)])
     d = rng.choice([64, 128])
     B = rng.choice([1, 1, 2])
-    sq, sk = rng.randint(1, 260), rng.randint(1, 330)
+    # key counts on both sides of the forward's switch between its four-wave (at most 1024 keys)
+    # and eight-wave instances
+    sq, sk = rng.randint(1, 260), (rng.randint(1, 330) if rng.random() < 0.7 else rng.randint(1025, 1400))
     kind = rng.choice(["none", "causal", "striped", "segments"])
     if kind == "none":
         return dict(hq=hq, hkv=hkv, d=d, B=B, sq=sq, sk=sk, mode=ma.MA_MASK_NONE, qp=None, kp=None)
