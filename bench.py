@@ -55,6 +55,9 @@ def parse():
                          "small = a 13440-token share cut into tiles of 13440 down to 210 tokens, "
                          "bwd4 = backward of 4 Q partitions x one KV partition of 8192")
     ap.add_argument("--workload-reps", type=int, default=3, help="timed repetitions per workload entry (median)")
+    ap.add_argument("--power-sample", type=float, default=0.0,
+                    help="after the timed steps, run the forward and then the backward back to back for this many "
+                         "seconds each while sampling socket power and shader clocks with amd-smi (0: off)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB (outside the timed "
                          "region): the reference launch for scaling HBM byte counters")
@@ -90,6 +93,67 @@ def cpu_baseline(rows, scale):
             "sample": f"{rows} of {SQ} query rows x {HQ} heads against all {SK} keys: forward, 2-way merge, "
                       f"backward in float64 NumPy ({dt:.1f} s; cpu {platform.processor() or platform.machine()}, "
                       f"{len(os.sched_getaffinity(0))} host cores visible)"}
+
+
+def _smi_sample():
+    """(socket power W, [shader clock MHz of each XCD]) from one amd-smi call, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True,
+                           timeout=10)
+        d = json.loads(r.stdout)
+        g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+        w = g["power"]["socket_power"]["value"]
+        clk = [v["clk"]["value"] for n, v in g["clock"].items()
+               if n.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        return (float(w), [float(c) for c in clk]) if isinstance(w, (int, float)) and clk else None
+    except Exception:
+        return None
+
+
+def power_clock(runs, seconds):
+    """Socket power and shader clock while each entry of `runs` (name, fn) is enqueued back to back
+    for `seconds`; amd-smi refreshes about once a second, so the first second of a phase is dropped."""
+    import threading
+    import statistics
+    import torch
+    samples, label, stop = [], ["idle"], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t = time.time()
+            x = _smi_sample()
+            if x:
+                samples.append((t, label[0], x[0], statistics.mean(x[1])))
+            time.sleep(0.25)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(1.5)
+    res, starts = {}, {}
+    for name, fn in runs:
+        label[0] = name
+        starts[name] = time.time()
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                fn()
+            n += 20
+            torch.cuda.synchronize()
+        res[name] = {"ms_per_call": round((time.perf_counter() - t0) * 1e3 / n, 4), "calls": n}
+        label[0] = "idle"
+        time.sleep(1.5)
+    stop.set()
+    th.join()
+    for name in list(res) + ["idle"]:
+        sel = [(w, c) for t, lab, w, c in samples if lab == name and (name == "idle" or t >= starts[name] + 1.0)]
+        entry = res.setdefault(name, {})
+        if sel:
+            entry.update({"socket_w_median": statistics.median(w for w, _ in sel),
+                          "gfx_mhz_median": round(statistics.median(c for _, c in sel)),
+                          "gfx_mhz_range": [round(min(c for _, c in sel)), round(max(c for _, c in sel))],
+                          "samples": len(sel)})
+    return res
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tile_bwd_gqa_tile_8k.md")
@@ -568,6 +632,16 @@ def main():
         merge_cold_ms = sum(ts[1:]) / len(ts[1:])
         del scratch
 
+    power = None
+    if args.power_sample > 0:
+        runs = []
+        if "fwd" in parts:
+            runs.append(("tile_fwd", lambda: ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, q_pos, k_pos)], scale,
+                                                                  ma.MA_MASK_NONE)))
+        if "bwd" in parts:
+            runs.append(("tile_bwd", lambda: ma.mesh_attn_tile_bwd(bwd_tiles, scale, ma.MA_MASK_NONE, workspace=ws)))
+        power = power_clock(runs, args.power_sample)
+
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -624,6 +698,16 @@ def main():
                    "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "mask": "none", "steps_parts": sorted(parts)},
         "roofline": rl, "parts": res_parts,
     }
+    if power is not None:
+        # the dense bf16 peak scales with the shader clock: the rate each part reaches against the
+        # peak at the clock the chip held while it ran
+        for name in ("tile_fwd", "tile_bwd"):
+            pw = power.get(name, {})
+            if "gfx_mhz_median" in pw and name in res_parts:
+                pk = PEAK_BF16_TFLOPS * pw["gfx_mhz_median"] / 2400.0
+                pw["bf16_peak_at_held_clock_tflops"] = round(pk, 1)
+                pw["frac_of_peak_at_held_clock"] = round(res_parts[name]["TFLOP/s"] / pk, 4)
+        out["power_clock"] = power
     names = set(args.workloads.split(",")) - {"none", ""}
     if names:
         del q, k, v, dO, o_in, lse_in, o, lse, o_m, lse_m, dq, dk, dv, bwd_tiles, ws
