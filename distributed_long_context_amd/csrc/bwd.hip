@@ -333,6 +333,9 @@ bwd_dq_kernel(const BwdParams p) {
   // the exponentials; dQ^T += K^T dS^T; mask of the next half
   auto half_step = [&](int st, int kb2, f32x16& sc, f32x16& dc, int ng, const BlkMask& nv, int nst, int nkb2,
                        f32x16& sn, f32x16& dn) {
+    // ask the scheduler to interleave the LDS reads with the MFMAs (measured: the dQ
+    // kernel 1.46 -> 1.42 ms at the 8k tile)
+    __builtin_amdgcn_iglp_opt(0);
     bf16x8 dsf[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
