@@ -276,6 +276,8 @@ fwd_bf16_kernel(const FwdParams p) {
   };
 
   auto half_step = [&](auto may_mask, int st, int kb2, f32x16& sc, int nkb_, int nst, int nkb2, f32x16& sn) {
+    // scheduler hint: LDS reads interleaved with the MFMAs (measured 0.5-1% faster at the 8k tile)
+    __builtin_amdgcn_iglp_opt(0);
     const float mref = (m2 == -INFINITY) ? 0.0f : m2;
     bf16x8 pf[2];
 #pragma unroll
