@@ -55,9 +55,10 @@ def parse():
                          "small = a 13440-token share cut into tiles of 13440 down to 210 tokens, "
                          "bwd4 = backward of 4 Q partitions x one KV partition of 8192")
     ap.add_argument("--workload-reps", type=int, default=3, help="timed repetitions per workload entry (median)")
-    ap.add_argument("--power-sample", type=float, default=0.0,
-                    help="after the timed steps, run the forward and then the backward back to back for this many "
-                         "seconds each while sampling socket power and shader clocks with amd-smi (0: off)")
+    ap.add_argument("--power-sample", type=float, default=5.0,
+                    help="after the timed steps (outside the timed region), run the forward and then the backward "
+                         "back to back for this many seconds each while sampling socket power and shader clocks "
+                         "with amd-smi (0: off)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB (outside the timed "
                          "region): the reference launch for scaling HBM byte counters")
