@@ -541,8 +541,8 @@ def main():
         return
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share on one GPU; --gpus above 1 is not supported "
-              "(this build runs on a single MI355X).", file=sys.stderr)
+        print("bench.py measures one GPU's share on one MI355X; --gpus above 1 is not supported "
+              "(the path runs on a single GPU, with no collectives).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
