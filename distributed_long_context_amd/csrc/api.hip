@@ -160,11 +160,12 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   // Tiles go to one of four launches: by how much masking they need (bit 0) and, in
   // bf16, by length (bit 1).  FULL tiles (and every tile without a mask) run the
   // unmasked kernel, PARTIAL ones the masked kernel, whose key positions must be one
-  // segment: a tile whose key positions have several segments is run as one piece
-  // per segment (the keys of a segment are contiguous rows), the first piece with
-  // any allowed pair writing the output and the later ones folding into it.  Tiles
-  // of at most kFwdSmallBlocks key blocks run the four-wave kernel.  A tile naming
-  // the output of one already queued waits for it.
+  // segment: a tile whose key positions have several segments is cut into one piece
+  // per segment (the keys of a segment are contiguous rows) and its pieces with any
+  // allowed pair go to the masked kernel as a chain of consecutive entries, which one
+  // workgroup runs in turn with the softmax state in registers, so the output is
+  // written (and rounded) once.  Tiles of at most kFwdSmallBlocks key blocks run the
+  // four-wave kernel.  A tile naming the output of one already queued waits for it.
   FwdParams bp[4];
   int bn[4] = {0, 0, 0, 0}, bwg[4] = {0, 0, 0, 0};
   for (int m = 0; m < 4; ++m) {
@@ -187,17 +188,25 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     }
     return MA_OK;
   };
-  // queue one (sub-)tile; cls is its class, acc its accumulate flag
-  auto enqueue = [&](const ma_tile& t, int cls, int acc) -> int {
+  // queue one tile (or the pieces of one, as a chain): cls is the class of the tile (any
+  // chain runs masked), acc its accumulate flag, pieces the key segments after the first
+  auto enqueue_chain = [&](const ma_tile* pcs, int npcs, int cls, int acc) -> int {
     bool dup = false;
     for (int k = 0; k < 4; ++k)
-      for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == t.o || bp[k].tiles[j].lse == t.lse;
+      for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == pcs[0].o || bp[k].tiles[j].lse == pcs[0].lse;
     if (dup) {
       int r = flush_all();
       if (r) return r;
     }
-    const bool small = bf16 && (t.sk + 63) / 64 <= kFwdSmallBlocks;
-    const int m = (cls == MA_TILE_FULL ? 0 : 1) | (small ? 2 : 0);
+    int64_t blocks = 0;
+    for (int i = 0; i < npcs; ++i) blocks += (pcs[i].sk + 63) / 64;
+    const bool small = bf16 && blocks <= kFwdSmallBlocks;
+    const int m = (cls == MA_TILE_FULL && npcs == 1 ? 0 : 1) | (small ? 2 : 0);
+    if (bn[m] + npcs > kFwdTilesPerLaunch) {  // a chain stays in one launch
+      int r = flush(m);
+      if (r) return r;
+    }
+    const ma_tile& t = pcs[0];
     FwdTile& ft = bp[m].tiles[bn[m]];
     std::memset(&ft, 0, sizeof(ft));
     ft.q = t.q; ft.k = t.k; ft.v = t.v; ft.o = t.o; ft.lse = t.lse;
@@ -227,13 +236,29 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     ft.wg_begin = bwg[m];
     bwg[m] += (int)wgs;
     ++bn[m];
+    // the chained key segments: no workgroups of their own (their first workgroup is where
+    // the next tile's begin, so the kernel's tile lookup skips them)
+    for (int i = 1; i < npcs; ++i) {
+      FwdTile& ct = bp[m].tiles[bn[m]];
+      ct = ft;
+      ct.k = pcs[i].k;
+      ct.v = pcs[i].v;
+      ct.sk = (int32_t)pcs[i].sk;
+      ct.kgb = (int32_t)pcs[i].k_pos.seg[0].global_begin;
+      ct.kst = (int32_t)pcs[i].k_pos.seg[0].stride;
+      ct.accumulate = kFwdChained;
+      ct.wg_begin = bwg[m];
+      ++bn[m];
+    }
     if (bn[m] == kFwdTilesPerLaunch) return flush(m);
     return MA_OK;
   };
   for (int i = 0; i < a->ntiles; ++i) {
     const ma_tile& t = a->tiles[i];
     const int nseg = a->mask_mode == MA_MASK_NONE ? 1 : t.k_pos.nseg;
-    int acc = a->accumulate;  // the first piece with work writes unless the call accumulates
+    ma_tile pcs[MA_MAX_SEGMENTS];
+    int pcls[MA_MAX_SEGMENTS];
+    int npcs = 0, cls_all = MA_TILE_FULL;
     for (int sgi = 0; sgi < nseg; ++sgi) {
       ma_tile u = t;
       if (nseg > 1) {
@@ -251,11 +276,21 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       const int cls = a->mask_mode == MA_MASK_NONE ? MA_TILE_FULL
                                                    : mesh_attn_classify(&u.q_pos, u.sq, &u.k_pos, u.sk, a->mask_mode);
       if (cls == MA_TILE_EMPTY) continue;
-      rc = enqueue(u, cls, acc);
-      if (rc) return rc;
-      acc = 1;
+      if (cls != MA_TILE_FULL) cls_all = cls;
+      pcls[npcs] = cls;
+      pcs[npcs++] = u;
     }
-    if (acc == 0) {  // no piece had an allowed pair: the tile's result is (0, -inf)
+    if (npcs > 0 && bf16) {
+      rc = enqueue_chain(pcs, npcs, cls_all, a->accumulate);
+      if (rc) return rc;
+    } else if (npcs > 0) {
+      // fp32: one tile per piece, the later pieces folding into the first (fp32 outputs
+      // lose nothing by being stored between pieces)
+      for (int i = 0; i < npcs; ++i) {
+        rc = enqueue_chain(&pcs[i], 1, pcls[i], i == 0 ? a->accumulate : 1);
+        if (rc) return rc;
+      }
+    } else if (a->accumulate == 0) {  // no piece had an allowed pair: the tile's result is (0, -inf)
       rc = flush_all();  // a queued tile may name the same output
       if (rc) return rc;
       int e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss,

@@ -137,8 +137,11 @@ fwd_bf16_kernel(const FwdParams p) {
     pos_minmax_dev(T.qp, T.sq, q0, min(T.sq, q0 + kQW), w_pmin, w_pmax);
   }
 
-  const __bf16* __restrict__ Kg = (const __bf16*)T.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
-  const __bf16* __restrict__ Vg = (const __bf16*)T.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+  // key side of the current tile; a chain of tiles (one per key segment of a partition, the
+  // masked instance only) changes it between pipelines while the softmax state carries over
+  const __bf16* Kg = nullptr;
+  const __bf16* Vg = nullptr;
+  int sk = 0;
   const int k_ss = (int)p.k_ss, v_ss = (int)p.v_ss;  // below 2^24 (checked by the caller)
 
   // ---- query fragments (B operand of S^T = K Q^T) and query position ----
@@ -161,14 +164,23 @@ fwd_bf16_kernel(const FwdParams p) {
   // every row of the wave sees whole; nkb: the blocks with any allowed pair for
   // the workgroup (the blocks after them have none).  Without a mask every key
   // of the partition is allowed and only a ragged last block is partial.
-  int klast = T.sk - 1, kfull_w = T.sk / kBN, nkb = (T.sk + kBN - 1) / kBN;
-  if constexpr (MASKED) {
-    const int kgb = T.kgb, kst = T.kst;
-    auto last_key = [&](int pq) { return pq < kgb ? -1 : min(T.sk - 1, (pq - kgb) / kst); };
-    klast = last_key(qpos);
-    kfull_w = active ? (last_key(w_pmin) + 1) / kBN : 0;
-    nkb = (last_key(wg_pmax) + kBN) / kBN;
-  }
+  int klast = 0, kfull_w = 0, nkb = 0;
+  auto set_keys = [&](const FwdTile& X) {
+    Kg = (const __bf16*)X.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+    Vg = (const __bf16*)X.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+    sk = X.sk;
+    klast = sk - 1;
+    kfull_w = sk / kBN;
+    nkb = (sk + kBN - 1) / kBN;
+    if constexpr (MASKED) {
+      const int kgb = X.kgb, kst = X.kst;
+      auto last_key = [&](int pq) { return pq < kgb ? -1 : min(sk - 1, (pq - kgb) / kst); };
+      klast = last_key(qpos);
+      kfull_w = active ? (last_key(w_pmin) + 1) / kBN : 0;
+      nkb = (last_key(wg_pmax) + kBN) / kBN;
+    }
+  };
+  set_keys(T);
   auto next_block = [&](int from) -> int { return from < nkb ? from : nkb; };
 
   // ---- direct-to-LDS loads: wave instruction i fills LDS chunks [(wave*LPW+i)*64, +64) ----
@@ -183,7 +195,7 @@ fwd_bf16_kernel(const FwdParams p) {
   auto issue = [&](int st, int kb) {
     const __bf16* kbase = Kg + (int64_t)kb * kBN * p.k_ss;
     const __bf16* vbase = Vg + (int64_t)kb * kBN * p.v_ss;
-    const int valid = T.sk - kb * kBN;  // rows of this block inside the partition
+    const int valid = sk - kb * kBN;  // rows of this block inside the partition
     if (valid >= kBN) {
 #pragma unroll
       for (int i = 0; i < C::LPW; ++i) {
@@ -382,9 +394,20 @@ fwd_bf16_kernel(const FwdParams p) {
     }
   };
   if constexpr (MASKED) {
-    pipeline(std::true_type{});
+    // the tile and the key segments chained to it: the entries after the tile flagged as
+    // continuations (same query rows and output, one key segment each) run in turn
+    int tj = __builtin_amdgcn_readfirstlane(ti);
+    for (;;) {
+      pipeline(std::true_type{});
+      if (tj + 1 >= p.ntiles) break;
+      const FwdTile N = p.tiles[__builtin_amdgcn_readfirstlane(tj + 1)];
+      if (!(N.accumulate & kFwdChained)) break;
+      ++tj;
+      __syncthreads();  // every wave is done with the ring before it is refilled
+      set_keys(N);
+    }
   } else {
-    if (T.sk % kBN != 0) pipeline(std::true_type{});  // ragged last block needs the key mask
+    if (sk % kBN != 0) pipeline(std::true_type{});  // ragged last block needs the key mask
     else pipeline(std::false_type{});
   }
 
@@ -401,7 +424,7 @@ fwd_bf16_kernel(const FwdParams p) {
   float wn = has ? 1.0f / ltot : 0.0f;  // weight of this tile's unnormalised sums
   float wo = 0.0f;                      // weight of the output already held (accumulate)
   __bf16* orow = Og + (int64_t)row * p.o_ss;
-  if (T.accumulate) {
+  if (T.accumulate & 1) {
     // fold into (O_old, lse_old): L = ln(e^lse_old + e^lse), O = e^(lse_old-L) O_old + e^(lse-L) O
     const float lo = Lg[row];
     const float mx = fmaxf(lo, lse);
@@ -423,7 +446,7 @@ fwd_bf16_kernel(const FwdParams p) {
       float v4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * wn;
-      if (T.accumulate) {
+      if (T.accumulate & 1) {
         const bf16x4 old = *(const bf16x4*)dst;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v4[i] = __builtin_fmaf(wo, (float)old[i], v4[i]);

@@ -24,7 +24,8 @@ struct KPos {
 };
 
 // ---- tile forward ----
-constexpr int kFwdTilesPerLaunch = 30;  // the parameter block stays under the 4 KB kernel-argument limit
+constexpr int kFwdTilesPerLaunch = 30;
+constexpr int32_t kFwdChained = 2;  // FwdTile::accumulate flag of a chained key segment  // the parameter block stays under the 4 KB kernel-argument limit
 
 struct FwdTile {
   const void* q;
@@ -35,8 +36,9 @@ struct FwdTile {
   int32_t sq, sk;
   int32_t wg_begin;    // first workgroup of this tile in the launch
   int32_t chunks;      // workgroup chunks per (batch, kv head)
-  int32_t accumulate;  // fold into the (O, LSE) held by the output buffers
-  int32_t kgb, kst;    // key positions, one segment: global = kgb + kst * t (the host splits the others)
+  int32_t accumulate;  // bit 0: fold into the (O, LSE) held by the output buffers; kFwdChained:
+                       // continues the previous entry (same rows and output, next key segment)
+  int32_t kgb, kst;    // key positions, one segment: global = kgb + kst * t (the host chains the others)
   KPos qp;
 };
 

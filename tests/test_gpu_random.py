@@ -59,7 +59,9 @@ def _case(seed):
                 qp=_segments(rng, sq, rng.randint(0, 300)), kp=_segments(rng, sk, 0))
 
 
-@pytest.mark.parametrize("seed", range(24))
+# 72: four key segments folded into an incoming partial with |O| near 3.5; when the segments of a
+# tile were separate folds, each rounding O to bf16, its error reached 0.021 (bar 0.02)
+@pytest.mark.parametrize("seed", list(range(24)) + [72])
 def test_random_forward(seed):
     c = _case(1000 + seed)
     log(f"[random fwd {seed}] {c}")
