@@ -455,7 +455,9 @@ bwd_dkv_kernel(const BwdParams p) {
   const int gsz = kv_first_at(kvh + 1) - g0;
   const int key0 = kblk * (kWaves * kKW);
   const int wg_keys = min(kWaves * kKW, KV.sk - key0);
-  if (gsz <= 0 || wg_keys <= 0) return;
+  // a KV head that no query head reads (an explicit head map may leave one) still gets its
+  // dK and dV written: its walk has no blocks, so the epilogue stores zeros (or adds nothing)
+  if (wg_keys <= 0) return;
   const int my_key = key0 + wave * kKW + l32;
   const bool key_ok = my_key < KV.sk;
   const bool wg_tail = wg_keys < kWaves * kKW;

@@ -112,6 +112,19 @@ def test_bwd_head_map_batch():
              head_map=[1, 2, 0, 0, 2, 1], B=2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_unused_kv_head(causal):
+    """An explicit head map that leaves KV head 1 unread: its dK and dV are zero (the buffers start
+    as NaN and are overwritten), the other heads match the oracle."""
+    log(f"[bwd unused kv head] causal={causal}")
+    hm = [0, 2, 3, 3, 2, 3, 2]
+    if causal:
+        tiles = run_case(1250, 53, 81, 7, 4, 64, ma.MA_MASK_CAUSAL, Pos([(0, 40, 1)]), Pos([(0, 0, 1)]), head_map=hm)
+    else:
+        tiles = run_case(1251, 53, 81, 7, 4, 128, head_map=hm)
+    assert torch.all(tiles[0].dk[:, :, 1] == 0) and torch.all(tiles[0].dv[:, :, 1] == 0)
+
+
 def test_bwd_many_q_tiles_share_kv():
     # dK/dV summed over several Q partitions (more than one launch packs)
     log("[bwd 11 q tiles]")
