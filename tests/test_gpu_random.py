@@ -115,3 +115,107 @@ def test_random_backward(seed):
     check_grad("dQ", dq, dq_r)
     check_grad("dK", dk, dk_r)
     check_grad("dV", dv, dv_r)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_head_map(seed):
+    """Irregular explicit GQA maps (groups of unequal size, KV heads no query head reads):
+    forward and backward of one drawn tile."""
+    rng = random.Random(7000 + seed)
+    c = _case(90000 + seed)
+    hkv = rng.randint(1, 6)
+    hq = rng.randint(hkv, 12)
+    hm = [rng.randrange(hkv) for _ in range(hq)]
+    log(f"[random head map {seed}] hq={hq} hkv={hkv} map={hm} {c}")
+    B, sq, sk, d = c["B"], c["sq"], c["sk"], c["d"]
+    wid = 6000 + seed
+    q, qv = gen(wid, synthetic.T_Q, 0, (B, sq, hq, d))
+    k, kv = gen(wid, synthetic.T_K, 0, (B, sk, hkv, d))
+    v, vv = gen(wid, synthetic.T_V, 0, (B, sk, hkv, d))
+    scale = np.float32(1.0 / math.sqrt(d))
+    causal = c["mode"] != ma.MA_MASK_NONE
+    qpos = positions(c["qp"], sq) if causal else None
+    kpos = positions(c["kp"], sk) if causal else None
+    O, L = attn_tile(qv, kv, vv, scale, hm, causal, qpos, kpos)
+    o = torch.full((B, sq, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, hq, sq), float("nan"), dtype=torch.float32, device=DEV)
+    ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, c["qp"], c["kp"])], float(scale), c["mode"], hm)
+    torch.cuda.synchronize()
+    check_close("O", host_f64(o), O, BF16_O_TOL, normalised_also=False)
+    check_close("LSE", host_f64(lse), L, BF16_LSE_TOL)
+    o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+    do, dov = gen(wid, synthetic.T_DO, 0, (B, sq, hq, d))
+    dq = torch.full((B, sq, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.full((B, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+    dv = torch.full_like(dk, float("nan"))
+    ma.mesh_attn_tile_bwd([BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv, c["qp"], c["kp"])], float(scale),
+                          c["mode"], hm)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = attn_tile_bwd(qv, kv, vv, o_used, dov, l_used, scale, hm, causal, qpos, kpos)
+    check_grad("dQ", dq, dq_r)
+    check_grad("dK", dk, dk_r)
+    check_grad("dV", dv, dv_r)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_multi_tile_calls(seed):
+    """One accumulate forward call over a random set of (Q partition, KV partition) pairs in random
+    order, each folding into its Q partition's output, then one backward call over the same pairs
+    (dQ summed per Q partition, dK/dV per KV partition)."""
+    rng = random.Random(8000 + seed)
+    hkv = rng.choice([1, 2, 4])
+    hq = hkv * rng.choice([1, 2, 4])
+    d = rng.choice([64, 128])
+    mode = rng.choice(["none", "causal", "striped"])
+    mask = {"none": ma.MA_MASK_NONE, "causal": ma.MA_MASK_CAUSAL, "striped": ma.MA_MASK_STRIPED_ZIGZAG}[mode]
+    nq, nk = rng.randint(1, 5), rng.randint(1, 12)
+    P = rng.choice([16, 33, 64, 100, 129])
+    log(f"[random multi-tile {seed}] hq={hq} hkv={hkv} d={d} {mode} nq={nq} nk={nk} P={P}")
+    wid = 7100 + seed
+    scale = np.float32(1.0 / math.sqrt(d))
+    causal = mode != "none"
+    n = max(nq, nk)
+    pos = (lambda i: None) if not causal else (
+        (lambda i: ma.mesh_attn_pos_striped(n, i)) if mode == "striped" else (lambda i: Pos([(0, i * P, 1)])))
+    qs = [gen(wid, synthetic.T_Q, i, (1, P, hq, d)) for i in range(nq)]
+    ks = [gen(wid, synthetic.T_K, j, (1, P, hkv, d)) for j in range(nk)]
+    vs = [gen(wid, synthetic.T_V, j, (1, P, hkv, d)) for j in range(nk)]
+    dos = [gen(wid, synthetic.T_DO, i, (1, P, hq, d)) for i in range(nq)]
+    pairs = [(i, j) for i in range(nq) for j in range(nk) if rng.random() < 0.7] or [(0, 0)]
+    rng.shuffle(pairs)
+    qp, kp = [pos(i) for i in range(nq)], [pos(j) for j in range(nk)]
+    outs = [(torch.zeros((1, P, hq, d), dtype=torch.bfloat16, device=DEV),
+             torch.full((1, hq, P), float("-inf"), dtype=torch.float32, device=DEV)) for _ in range(nq)]
+    ma.mesh_attn_tile_fwd([Tile(qs[i][0], ks[j][0], vs[j][0], outs[i][0], outs[i][1], qp[i], kp[j]) for i, j in pairs],
+                          float(scale), mask, accumulate=True)
+    torch.cuda.synchronize()
+    refs = {}
+    for i, j in pairs:
+        refs.setdefault(i, []).append(attn_tile(qs[i][1], ks[j][1], vs[j][1], scale, None, causal,
+                                                positions(qp[i], P) if causal else None,
+                                                positions(kp[j], P) if causal else None))
+    stored = {}
+    for i in refs:
+        Oref, Lref = merge(refs[i])
+        check_close("O", host_f64(outs[i][0]), Oref, BF16_O_TOL, normalised_also=False)
+        check_close("LSE", host_f64(outs[i][1]), Lref, BF16_LSE_TOL)
+        stored[i] = stored_o_lse(Oref, Lref)
+    dqs = [torch.full((1, P, hq, d), float("nan"), dtype=torch.float32, device=DEV) for _ in range(nq)]
+    dks = [torch.full((1, P, hkv, d), float("nan"), dtype=torch.float32, device=DEV) for _ in range(nk)]
+    dvs = [torch.full((1, P, hkv, d), float("nan"), dtype=torch.float32, device=DEV) for _ in range(nk)]
+    ma.mesh_attn_tile_bwd([BwdTile(qs[i][0], ks[j][0], vs[j][0], stored[i][0], dos[i][0], stored[i][2], dqs[i], dks[j],
+                                   dvs[j], qp[i], kp[j]) for i, j in pairs], float(scale), mask)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = {}, {}, {}
+    for i, j in pairs:
+        a, b, c = attn_tile_bwd(qs[i][1], ks[j][1], vs[j][1], stored[i][1], dos[i][1], stored[i][3], scale, None,
+                                causal, positions(qp[i], P) if causal else None,
+                                positions(kp[j], P) if causal else None)
+        dq_r[i] = dq_r.get(i, 0) + a
+        dk_r[j] = dk_r.get(j, 0) + b
+        dv_r[j] = dv_r.get(j, 0) + c
+    for i in dq_r:
+        check_grad("dQ", dqs[i], dq_r[i])
+    for j in dk_r:
+        check_grad("dK", dks[j], dk_r[j])
+        check_grad("dV", dvs[j], dv_r[j])
