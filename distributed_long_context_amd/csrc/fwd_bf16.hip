@@ -40,8 +40,10 @@
 //    every pair allowed run unmasked, the rest (and a ragged last block) are
 //    masked element by element.  Tiles that are FULL as a whole run the kernel
 //    without masks; the masked kernel takes key positions of one segment
-//    (contiguous or striped; the host runs a tile of several key segments as one
-//    piece per segment), which grow with the key index, so a lane keeps only the
+//    (contiguous or striped; a tile of several key segments is cut by the host into
+//    one piece per segment, chained in the tile table, and a workgroup runs the
+//    pieces in turn with its softmax state in registers), which grow with the key
+//    index, so a lane keeps only the
 //    index of its last allowed key, a wave the count of leading blocks it sees
 //    whole and the workgroup the count of blocks with any allowed pair; no
 //    position data stays live in the loop.
