@@ -219,3 +219,44 @@ def test_random_multi_tile_calls(seed):
     for j in dk_r:
         check_grad("dK", dks[j], dk_r[j])
         check_grad("dV", dvs[j], dv_r[j])
+
+
+def _head_major(t):
+    """The same values stored [B, H, S, d], viewed as [B, S, H, d] (explicit strides in the ABI)."""
+    return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_head_major_layout(seed):
+    """Forward and backward of a drawn tile with every [B, S, H, d] tensor in head-major storage."""
+    c = _case(20000 + seed)
+    log(f"[random head-major {seed}] {c}")
+    B, sq, sk, hq, hkv, d = c["B"], c["sq"], c["sk"], c["hq"], c["hkv"], c["d"]
+    wid = 21000 + seed
+    q, qv = gen(wid, synthetic.T_Q, 0, (B, sq, hq, d))
+    k, kv = gen(wid, synthetic.T_K, 0, (B, sk, hkv, d))
+    v, vv = gen(wid, synthetic.T_V, 0, (B, sk, hkv, d))
+    q, k, v = _head_major(q), _head_major(k), _head_major(v)
+    scale = np.float32(1.0 / math.sqrt(d))
+    causal = c["mode"] != ma.MA_MASK_NONE
+    qpos = positions(c["qp"], sq) if causal else None
+    kpos = positions(c["kp"], sk) if causal else None
+    O, L = attn_tile(qv, kv, vv, scale, None, causal, qpos, kpos)
+    o = _head_major(torch.full((B, sq, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV))
+    lse = torch.full((B, hq, sq), float("nan"), dtype=torch.float32, device=DEV)
+    ma.mesh_attn_tile_fwd([Tile(q, k, v, o, lse, c["qp"], c["kp"])], float(scale), c["mode"])
+    torch.cuda.synchronize()
+    check_close("O", host_f64(o), O, BF16_O_TOL, normalised_also=False)
+    check_close("LSE", host_f64(lse), L, BF16_LSE_TOL)
+    o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+    do, dov = gen(wid, synthetic.T_DO, 0, (B, sq, hq, d))
+    o_dev, do = _head_major(o_dev), _head_major(do)
+    dq = _head_major(torch.full((B, sq, hq, d), float("nan"), dtype=torch.float32, device=DEV))
+    dk = _head_major(torch.full((B, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV))
+    dv = _head_major(torch.full((B, sk, hkv, d), float("nan"), dtype=torch.float32, device=DEV))
+    ma.mesh_attn_tile_bwd([BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv, c["qp"], c["kp"])], float(scale), c["mode"])
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = attn_tile_bwd(qv, kv, vv, o_used, dov, l_used, scale, None, causal, qpos, kpos)
+    check_grad("dQ", dq, dq_r)
+    check_grad("dK", dk, dk_r)
+    check_grad("dV", dv, dv_r)
