@@ -121,7 +121,10 @@ typedef struct {
  *   O = exp(lse_old - L) O_old + exp(lse_tile - L) O_tile;
  * with (0, -inf) when both are -inf.  The buffers must hold a valid pair (for
  * example the first tile's output, or O = 0 and LSE = -inf); EMPTY tiles leave
- * them unchanged.  The arithmetic is fp32 and O is rounded once, at the store.
+ * them unchanged.  The arithmetic is fp32 and O is rounded once, at the store;
+ * this holds too for a tile whose key positions have several segments (in bf16
+ * its segments are computed in turn by one workgroup, the softmax state carried
+ * in fp32 between them).
  * In either mode, tiles of one call that name the same o are applied in list
  * order (each waits for the one before), so a ring of KV partitions can be
  * handed over as one call.
