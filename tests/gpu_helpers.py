@@ -68,3 +68,32 @@ def check_close(name, got, ref, tol, normalised_also=True):
     if normalised_also and scale > 0:
         assert err / scale <= max(tol, 2e-2), f"{name}: normalised error {err/scale} too large"
     return err
+
+
+def oracle_forward_by_head(q, k, v, scale, threads=16):
+    """The oracle forward (non-causal, default GQA map) of every query row, one query head per task.
+
+    Each task calls oracle.attn_tile on one query head and its KV head (a [B, S, 1, d] slice of
+    each), so the arithmetic is the oracle's own; the tasks only run side by side (NumPy releases
+    the GIL inside its kernels).  Returns (O [B, Sq, Hq, d], LSE [B, Hq, Sq]) in float64."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attn_tile
+
+    B, Sq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    O = np.zeros((B, Sq, Hq, d))
+    L = np.zeros((B, Hq, Sq))
+
+    def one(h):
+        kv = h // g
+        Oh, Lh = attn_tile(q[:, :, h:h + 1], k[:, :, kv:kv + 1], v[:, :, kv:kv + 1], scale)
+        O[:, :, h:h + 1] = Oh
+        L[:, h:h + 1] = Lh
+
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(Hq)))
+    return O, L

@@ -18,7 +18,8 @@ import distributed_long_context_amd as ma  # noqa: E402
 from distributed_long_context_amd import BwdTile, Pos, Tile  # noqa: E402
 from oracle import attn_tile, attn_tile_bwd, merge, layout  # noqa: E402
 from gpu_helpers import (BF16_LSE_TOL, BF16_O_TOL, DEV, check_close, dev_bf16, gen, host_f64, log,  # noqa: E402
-                         positions)
+                         oracle_forward_by_head, positions)
+from test_gpu_bwd import stored_o_lse  # noqa: E402
 
 import synthetic  # noqa: E402
 
@@ -193,8 +194,9 @@ def test_mesh_8x8_1m_forward_and_merge():
 
 def test_gqa_bwd_4x8k():
     # Backward at the 8k GQA shape: 4 Q partitions of 8192 against one KV partition of 8192, non-causal;
-    # dK/dV summed over the 4 partitions.  O and LSE are seeded stored inputs with the magnitudes of a
-    # real forward (O ~ 0.02 N(0,1), LSE ~ ln 8192 + 0.5 + 0.3 N(0,1)); both sides read the same values.
+    # dK/dV summed over the 4 partitions.  O and LSE are the oracle's forward of each Q partition against
+    # the KV partition (every row, every head), stored as bf16 O and fp32 LSE; both sides read those
+    # stored values, so the gradients are those of a consistent forward.
     wid, S, nq = 5, 8192, 4
     log("[workload gqa-bwd-4x8k]")
     k, kv = gen(wid, synthetic.T_K, 0, (1, S, HKV, D))
@@ -202,16 +204,15 @@ def test_gqa_bwd_4x8k():
     dk = torch.empty((1, S, HKV, D), dtype=torch.float32, device=DEV)
     dv = torch.empty_like(dk)
     tiles, host = [], []
-    mu = np.float32(math.log(S) + 0.5)
     for i in range(nq):
         q, qv = gen(wid, synthetic.T_Q, i, (1, S, HQ, D))
         do, dov = gen(wid, synthetic.T_DO, i, (1, S, HQ, D))
-        ob = synthetic.f32_to_bf16_bits(synthetic.normal_f32(wid, synthetic.T_O_IN, i, (1, S, HQ, D)) * np.float32(0.02))
-        ov = synthetic.bf16_bits_to_f32(ob).astype(np.float64)
-        lv = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (1, HQ, S)) * np.float32(0.3) + mu).astype(np.float32)
+        O, L = oracle_forward_by_head(qv, kv, vv, SCALE)
+        o_dev, o_used, l_dev, l_used = stored_o_lse(O, L)
+        log(f"  oracle forward of Q partition {i} done")
         dq = torch.empty((1, S, HQ, D), dtype=torch.float32, device=DEV)
-        tiles.append(BwdTile(q, k, v, dev_bf16(ob), do, torch.from_numpy(lv).to(DEV), dq, dk, dv))
-        host.append(dict(q=qv, o=ov, do=dov, lse=lv.astype(np.float64)))
+        tiles.append(BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv))
+        host.append(dict(q=qv, o=o_used, do=dov, lse=l_used))
     ma.mesh_attn_tile_bwd(tiles, float(SCALE), ma.MA_MASK_NONE)
     torch.cuda.synchronize()
 
