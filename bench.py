@@ -346,7 +346,7 @@ def measure_workloads(names, reps):
         dv = [torch.empty_like(x) for x in dk]
         btiles = [BwdTile(Q[qchunks[i]], K[j], V[j], O[qchunks[i]], dO[qchunks[i]], L[qchunks[i]], dq[qchunks[i]],
                           dk[j], dv[j], qpos[i], kpos[j]) for i, j, _ in wl]
-        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale, ma.MA_MASK_CAUSAL)), dtype=torch.uint8, device=dev)
         w["bwd_tiles"] = _tf(10.0 * D * HQ * pairs,
                              _timed(lambda: ma.mesh_attn_tile_bwd(btiles, scale, ma.MA_MASK_CAUSAL, workspace=ws), reps))
         res["zigzag-causal-128k-r5"] = w
@@ -423,7 +423,7 @@ def measure_workloads(names, reps):
         dk = {j: torch.empty((1, P, HKV, D), dtype=torch.float32, device=dev) for j in kparts}
         dv = {j: torch.empty_like(dk[j]) for j in kparts}
         btiles = [BwdTile(Q[i], K[j], V[j], O[i], dO[i], L[i], dq[i], dk[j], dv[j]) for i in qparts for j in kparts]
-        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale, ma.MA_MASK_NONE)), dtype=torch.uint8, device=dev)
         w["bwd_tiles"] = _tf(10.0 * D * HQ * pairs,
                              _timed(lambda: ma.mesh_attn_tile_bwd(btiles, scale, ma.MA_MASK_NONE, workspace=ws), 1))
         # the addition of the gradient reduce-scatter: 8 partial dQ of one Q partition (fp32) summed
@@ -460,7 +460,7 @@ def measure_workloads(names, reps):
         dv = {j: torch.empty_like(dk[j]) for j in kparts}
         btiles = [BwdTile(Q[i], K[j], V[j], O[i], dO[i], L[i], dq[i], dk[j], dv[j], qpos[i], kpos[j])
                   for i in qparts for j in kparts]
-        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale, mode)), dtype=torch.uint8, device=dev)
         w["bwd_tiles"] = _tf(10.0 * D * HQ * pairs, _timed(lambda: ma.mesh_attn_tile_bwd(btiles, scale, mode, workspace=ws), 1))
         res["mesh-8x8-1m-g9-striped-causal"] = w
         del Q, kg, vg, K, V, dO, O, L, dq, dk, dv, btiles, ws
@@ -526,7 +526,7 @@ def measure_workloads(names, reps):
             btiles.append(BwdTile(randn((1, S, HQ, D)), k, v, randn((1, S, HQ, D), mul=0.02), randn((1, S, HQ, D)),
                                   randn((1, HQ, S), torch.float32, 0.3, math.log(S) + 0.5),
                                   torch.empty((1, S, HQ, D), dtype=torch.float32, device=dev), dk, dv))
-        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(btiles, scale, ma.MA_MASK_NONE)), dtype=torch.uint8, device=dev)
         res["gqa-bwd-4x8k"] = {"bwd_tiles": _tf(10.0 * D * HQ * nq * S * S, _timed(
             lambda: ma.mesh_attn_tile_bwd(btiles, scale, ma.MA_MASK_NONE, workspace=ws), reps))}
         del k, v, dk, dv, btiles, ws
@@ -575,7 +575,7 @@ def main():
     bwd_tiles = [BwdTile(q, k, v, o_m, dO, lse_m, dq, dk, dv, q_pos, k_pos)]
     ws = None
     if "bwd" in parts:
-        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(bwd_tiles, scale)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(bwd_tiles, scale, ma.MA_MASK_NONE)), dtype=torch.uint8, device=dev)
 
     pairs = ma.mesh_attn_count_allowed(q_pos, SQ, k_pos, SK, ma.MA_MASK_NONE)
     fwd_flop = 4.0 * D * HQ * pairs

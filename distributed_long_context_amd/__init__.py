@@ -280,8 +280,9 @@ def _bwd_args(tiles, scale, mask_mode, head_map, accumulate):
     return a, (arr, keep)
 
 
-def mesh_attn_tile_bwd_workspace_size(tiles: Sequence[BwdTile], scale: float = 1.0, mask_mode: int = MA_MASK_NONE,
-                                      head_map=None) -> int:
+def mesh_attn_tile_bwd_workspace_size(tiles: Sequence[BwdTile], scale: float, mask_mode: int, head_map=None) -> int:
+    """Workspace bytes of mesh_attn_tile_bwd for these tiles under this mask (a masked call cuts
+    multi-segment positions into pieces, each with its own slice)."""
     a, keep = _bwd_args(list(tiles), scale, mask_mode, head_map, False)
     return int(lib().mesh_attn_tile_bwd_workspace_size(C.byref(a)))
 

@@ -8,6 +8,7 @@
 #include <string>
 #include <vector>
 #include <algorithm>
+#include <utility>
 
 #include "mesh_attn.h"
 #include "ma_internal.h"
@@ -24,6 +25,13 @@ int set_error(int code, const char* msg) {
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// p advanced by `bytes`, as address arithmetic (well defined for any pointer value, so the
+// workspace query can expand the segments of tiles whose pointers are not set)
+template <class T>
+T* byte_offset(T* p, int64_t bytes) {
+  return (T*)((uintptr_t)p + (uintptr_t)bytes);
+}
 
 int check_hip(int e, const char* what) {
   if (e != 0) {
@@ -100,6 +108,38 @@ bool strides_ok(const int64_t* s, int n, int dtype) {
   return true;
 }
 
+
+// Outputs of two tiles that are the same buffer shifted along the sequence axis: the
+// base pointers differ by a non-zero whole number of rows (row_bytes apart) that is
+// smaller than the rows of the earlier view, so some rows are written by both tiles
+// in one launch.  Such a call is rejected; identical outputs are allowed (the tiles
+// are then applied in list order).  Other partial overlaps of output buffers are
+// undefined.
+template <class PtrOf, class RowsOf>
+int check_shifted_outputs(int n, PtrOf ptr_of, RowsOf rows_of, int64_t row_bytes, const char* what) {
+  if (row_bytes <= 0 || n < 2) return MA_OK;
+  std::vector<std::pair<uintptr_t, int64_t>> v;  // (address, rows), sorted by address
+  v.reserve(n);
+  for (int i = 0; i < n; ++i) v.emplace_back((uintptr_t)ptr_of(i), rows_of(i));
+  std::sort(v.begin(), v.end());
+  // each view is compared with the one before it and with the earlier view reaching furthest
+  size_t far = 0;
+  auto shifted = [&](size_t j, size_t i) {
+    const uintptr_t d = v[i].first - v[j].first;
+    return d != 0 && d % (uintptr_t)row_bytes == 0 && (int64_t)(d / (uintptr_t)row_bytes) < v[j].second;
+  };
+  auto end_of = [&](size_t j) { return v[j].first + (uintptr_t)(v[j].second * row_bytes); };
+  for (size_t i = 1; i < v.size(); ++i) {
+    if (shifted(i - 1, i) || shifted(far, i)) {
+      std::string m = std::string(what) + " buffers of two tiles overlap (the same buffer shifted by fewer rows than "
+                                          "it holds); give each tile its own rows or the same buffer";
+      return set_error(MA_ERR_INVALID, m.c_str());
+    }
+    if (end_of(i) > end_of(far)) far = i;
+  }
+  return MA_OK;
+}
+
 }  // namespace
 }  // namespace ma
 
@@ -157,6 +197,12 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
 
   const bool bf16 = a->dtype == MA_BF16;
   const int64_t esize = bf16 ? 2 : 4;
+  rc = check_shifted_outputs(a->ntiles, [&](int i) { return a->tiles[i].o; },
+                             [&](int i) { return a->tiles[i].sq; }, a->o_stride[1] * esize, "o");
+  if (rc) return rc;
+  rc = check_shifted_outputs(a->ntiles, [&](int i) { return (const void*)a->tiles[i].lse; },
+                             [&](int i) { return a->tiles[i].sq; }, 4, "lse");
+  if (rc) return rc;
   // Tiles go to one of four launches: by how much masking they need (bit 0) and, in
   // bf16, by length (bit 1).  FULL tiles (and every tile without a mask) run the
   // unmasked kernel, PARTIAL ones the masked kernel, whose key positions must be one
@@ -166,27 +212,31 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   // workgroup runs in turn with the softmax state in registers, so the output is
   // written (and rounded) once.  Tiles of at most kFwdSmallBlocks key blocks run the
   // four-wave kernel.  A tile naming the output of one already queued waits for it.
+  // The whole call is planned first and launched afterwards, so an argument error
+  // found on any tile leaves nothing enqueued.
+  struct Planned {
+    int m;    // launch class; -1: fill an EMPTY tile's output with (0, -inf)
+    int wgs;  // workgroups of the launch
+    int idx;  // class launches: index into batches; fills: the tile's index
+  };
+  std::vector<Planned> plan;
+  std::vector<FwdParams> batches;
   FwdParams bp[4];
   int bn[4] = {0, 0, 0, 0}, bwg[4] = {0, 0, 0, 0};
   for (int m = 0; m < 4; ++m) {
     bp[m] = p;
     bp[m].mask = m & 1;
   }
-  auto flush = [&](int m) -> int {
-    if (bn[m] == 0) return MA_OK;
+  auto flush = [&](int m) {
+    if (bn[m] == 0) return;
     bp[m].ntiles = bn[m];
-    int e = bf16 ? launch_fwd_bf16(bp[m], a->head_dim, m & 2 ? 4 : 8, bwg[m], stream)
-                 : launch_fwd_f32(bp[m], a->head_dim, bwg[m], stream);
+    plan.push_back(Planned{m, bwg[m], (int)batches.size()});
+    batches.push_back(bp[m]);
     bn[m] = 0;
     bwg[m] = 0;
-    return check_hip(e, "tile_fwd launch");
   };
-  auto flush_all = [&]() -> int {
-    for (int m = 0; m < 4; ++m) {
-      int r = flush(m);
-      if (r) return r;
-    }
-    return MA_OK;
+  auto flush_all = [&]() {
+    for (int m = 0; m < 4; ++m) flush(m);
   };
   // queue one tile (or the pieces of one, as a chain): cls is the class of the tile (any
   // chain runs masked), acc its accumulate flag, pieces the key segments after the first
@@ -194,25 +244,34 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     bool dup = false;
     for (int k = 0; k < 4; ++k)
       for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == pcs[0].o || bp[k].tiles[j].lse == pcs[0].lse;
-    if (dup) {
-      int r = flush_all();
-      if (r) return r;
-    }
+    if (dup) flush_all();
     int64_t blocks = 0;
     for (int i = 0; i < npcs; ++i) blocks += (pcs[i].sk + 63) / 64;
     const bool small = bf16 && blocks <= kFwdSmallBlocks;
     const int m = (cls == MA_TILE_FULL && npcs == 1 ? 0 : 1) | (small ? 2 : 0);
-    if (bn[m] + npcs > kFwdTilesPerLaunch) {  // a chain stays in one launch
-      int r = flush(m);
-      if (r) return r;
-    }
     const ma_tile& t = pcs[0];
+    int64_t wgs, chunks;
+    if (bf16) {
+      // 8 (or 4) waves of 32 query rows per workgroup; units are (32-row block, head of the group)
+      const int waves = small ? 4 : 8;
+      const int64_t nqb = (t.sq + 31) / 32;
+      chunks = (nqb * p.gmax + waves - 1) / waves;
+      wgs = (int64_t)a->batch * a->hkv * chunks;
+      wgs = (wgs + 7) / 8 * 8;  // keep each tile's first workgroup on XCD 0
+    } else {
+      chunks = (t.sq + 63) / 64;
+      wgs = (int64_t)a->batch * a->hq * chunks;
+    }
+    if (wgs >= INT32_MAX) return set_error(MA_ERR_INVALID, "tile too large for one launch");
+    // a chain stays in one launch, and a launch's workgroup count stays below 2^31
+    if (bn[m] + npcs > kFwdTilesPerLaunch || bwg[m] + wgs >= INT32_MAX) flush(m);
     FwdTile& ft = bp[m].tiles[bn[m]];
     std::memset(&ft, 0, sizeof(ft));
     ft.q = t.q; ft.k = t.k; ft.v = t.v; ft.o = t.o; ft.lse = t.lse;
     ft.sq = (int32_t)t.sq;
     ft.sk = (int32_t)t.sk;
     ft.accumulate = acc;
+    ft.chunks = (int32_t)chunks;
     if (m & 1) {  // key positions are one segment here (split below)
       to_kpos(t.q_pos, ft.qp);
       ft.kgb = (int32_t)t.k_pos.seg[0].global_begin;
@@ -220,19 +279,6 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     } else {
       ft.qp.nseg = 1;
     }
-    int64_t wgs;
-    if (bf16) {
-      // 8 (or 4) waves of 32 query rows per workgroup; units are (32-row block, head of the group)
-      const int waves = small ? 4 : 8;
-      const int64_t nqb = (t.sq + 31) / 32;
-      ft.chunks = (int32_t)((nqb * p.gmax + waves - 1) / waves);
-      wgs = (int64_t)a->batch * a->hkv * ft.chunks;
-      wgs = (wgs + 7) / 8 * 8;  // keep each tile's first workgroup on XCD 0
-    } else {
-      ft.chunks = (int32_t)((t.sq + 63) / 64);
-      wgs = (int64_t)a->batch * a->hq * ft.chunks;
-    }
-    if (wgs + bwg[m] >= INT32_MAX) return set_error(MA_ERR_INVALID, "tile too large for one launch");
     ft.wg_begin = bwg[m];
     bwg[m] += (int)wgs;
     ++bn[m];
@@ -250,7 +296,7 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       ct.wg_begin = bwg[m];
       ++bn[m];
     }
-    if (bn[m] == kFwdTilesPerLaunch) return flush(m);
+    if (bn[m] == kFwdTilesPerLaunch) flush(m);
     return MA_OK;
   };
   for (int i = 0; i < a->ntiles; ++i) {
@@ -264,8 +310,8 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       if (nseg > 1) {
         const int64_t lb = t.k_pos.seg[sgi].local_begin;
         const int64_t le = sgi + 1 < nseg ? t.k_pos.seg[sgi + 1].local_begin : t.sk;
-        u.k = (const char*)t.k + lb * a->k_stride[1] * esize;
-        u.v = (const char*)t.v + lb * a->v_stride[1] * esize;
+        u.k = byte_offset(t.k, lb * a->k_stride[1] * esize);
+        u.v = byte_offset(t.v, lb * a->v_stride[1] * esize);
         u.sk = le - lb;
         std::memset(&u.k_pos, 0, sizeof(u.k_pos));
         u.k_pos.nseg = 1;
@@ -291,15 +337,26 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
         if (rc) return rc;
       }
     } else if (a->accumulate == 0) {  // no piece had an allowed pair: the tile's result is (0, -inf)
-      rc = flush_all();  // a queued tile may name the same output
-      if (rc) return rc;
-      int e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss,
-                                p.o_sh, p.l_sb, p.l_sh, stream);
-      rc = check_hip(e, "fill launch");
-      if (rc) return rc;
+      flush_all();  // a queued tile may name the same output
+      plan.push_back(Planned{-1, 0, i});
     }
   }
-  return flush_all();
+  flush_all();
+  // launch the plan in order
+  for (const Planned& pl : plan) {
+    int e;
+    if (pl.m < 0) {
+      const ma_tile& t = a->tiles[pl.idx];
+      e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss, p.o_sh,
+                            p.l_sb, p.l_sh, stream);
+    } else {
+      e = bf16 ? launch_fwd_bf16(batches[pl.idx], a->head_dim, pl.m & 2 ? 4 : 8, pl.wgs, stream)
+               : launch_fwd_f32(batches[pl.idx], a->head_dim, pl.wgs, stream);
+    }
+    rc = check_hip(e, pl.m < 0 ? "fill launch" : "tile_fwd launch");
+    if (rc) return rc;
+  }
+  return MA_OK;
 }
 
 int mesh_attn_merge(const ma_merge_args* a, void* stream) {
@@ -392,19 +449,19 @@ const ma_tile_bwd_args* expand_bwd_segments(const ma_tile_bwd_args* a, std::vect
         ma_bwd_tile u = t;
         const int64_t qb = t.q_pos.seg[qs].local_begin, kb = t.k_pos.seg[ks].local_begin;
         if (t.q_pos.nseg > 1) {
-          u.q = (const char*)t.q + qb * a->q_stride[1] * 2;
-          u.o = (const char*)t.o + qb * a->q_stride[1] * 2;
-          u.dout = (const char*)t.dout + qb * a->q_stride[1] * 2;
-          u.lse = t.lse + qb;
-          u.dq = t.dq + qb * a->dq_stride[1];
+          u.q = byte_offset(t.q, qb * a->q_stride[1] * 2);
+          u.o = byte_offset(t.o, qb * a->q_stride[1] * 2);
+          u.dout = byte_offset(t.dout, qb * a->q_stride[1] * 2);
+          u.lse = byte_offset(t.lse, qb * 4);
+          u.dq = byte_offset(t.dq, qb * a->dq_stride[1] * 4);
           u.sq = seg_end(t.q_pos, qs, t.sq) - qb;
           u.q_pos = one_seg(t.q_pos, qs);
         }
         if (t.k_pos.nseg > 1) {
-          u.k = (const char*)t.k + kb * a->k_stride[1] * 2;
-          u.v = (const char*)t.v + kb * a->k_stride[1] * 2;
-          u.dk = t.dk + kb * a->dk_stride[1];
-          u.dv = t.dv + kb * a->dk_stride[1];
+          u.k = byte_offset(t.k, kb * a->k_stride[1] * 2);
+          u.v = byte_offset(t.v, kb * a->k_stride[1] * 2);
+          u.dk = byte_offset(t.dk, kb * a->dk_stride[1] * 4);
+          u.dv = byte_offset(t.dv, kb * a->dk_stride[1] * 4);
           u.sk = seg_end(t.k_pos, ks, t.sk) - kb;
           u.k_pos = one_seg(t.k_pos, ks);
         }
@@ -446,9 +503,16 @@ size_t lsed_bytes(int batch, int hq, int64_t sq) {
 extern "C" {
 
 size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* a0) {
-  if (!a0 || a0->ntiles <= 0 || !a0->tiles || a0->batch < 1 || a0->hq < 1) return 0;
-  for (int i = 0; i < a0->ntiles; ++i)
-    if (a0->tiles[i].sq < 1) return 0;
+  if (!a0 || a0->ntiles <= 0 || a0->ntiles > MA_MAX_TILES || !a0->tiles || a0->batch < 1 || a0->hq < 1 ||
+      a0->hq > MA_MAX_HEADS)
+    return 0;
+  for (int i = 0; i < a0->ntiles; ++i) {
+    const ma_bwd_tile& t = a0->tiles[i];
+    if (t.sq < 1 || t.sk < 1 || t.sq >= INT32_MAX || t.sk >= INT32_MAX) return 0;
+    // the segments are expanded below: they must be valid first
+    if (a0->mask_mode != MA_MASK_NONE && check_positions(a0->mask_mode, t.q_pos, t.sq, t.k_pos, t.sk) != MA_OK)
+      return 0;
+  }
   std::vector<ma_bwd_tile> ex;
   ma_tile_bwd_args e;
   const ma_tile_bwd_args* a = expand_bwd_segments(a0, ex, e);
@@ -458,7 +522,13 @@ size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* a0) {
   return bytes;
 }
 
-int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace ma {
+namespace {
+
+// Every argument check of the backward (nothing is enqueued before they all pass).
+int validate_bwd(const ma_tile_bwd_args* a) {
   if (!a) return set_error(MA_ERR_INVALID, "null args");
   if (a->dtype != MA_BF16) return set_error(a->dtype == MA_F32 ? MA_ERR_UNSUPPORTED : MA_ERR_INVALID,
                                             "tile_bwd supports bf16 inputs only");
@@ -499,10 +569,21 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
         return set_error(MA_ERR_INVALID, "tiles naming the same dq must name the same q, o, dout, lse, sq and q_pos");
     }
   }
-  const size_t need = mesh_attn_tile_bwd_workspace_size(a);
-  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & 255u))
-    return set_error(MA_ERR_INVALID, "workspace missing, too small or not 256-byte aligned");
+  rc = check_shifted_outputs(a->ntiles, [&](int i) { return (const void*)a->tiles[i].dq; },
+                             [&](int i) { return a->tiles[i].sq; }, a->dq_stride[1] * 4, "dq");
+  if (rc) return rc;
+  rc = check_shifted_outputs(a->ntiles, [&](int i) { return (const void*)a->tiles[i].dk; },
+                             [&](int i) { return a->tiles[i].sk; }, a->dk_stride[1] * 4, "dk");
+  if (rc) return rc;
+  rc = check_shifted_outputs(a->ntiles, [&](int i) { return (const void*)a->tiles[i].dv; },
+                             [&](int i) { return a->tiles[i].sk; }, a->dk_stride[1] * 4, "dv");
+  if (rc) return rc;
+  return MA_OK;
+}
 
+// The backward of validated arguments with a workspace of at least the required size.
+int run_bwd(const ma_tile_bwd_args* a, void* workspace, void* stream) {
+  int rc;
   // from here on the tiles are single-segment pieces
   std::vector<ma_bwd_tile> ex;
   ma_tile_bwd_args e;
@@ -658,6 +739,21 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
     }
   }
   return MA_OK;
+}
+
+}  // namespace
+}  // namespace ma
+
+extern "C" {
+
+int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_bwd(a);
+  if (rc) return rc;
+  if (a->ntiles == 0) return MA_OK;
+  const size_t need = mesh_attn_tile_bwd_workspace_size(a);
+  if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & 255u))
+    return set_error(MA_ERR_INVALID, "workspace missing, too small or not 256-byte aligned");
+  return run_bwd(a, workspace, stream);
 }
 
 }  // extern "C"

@@ -27,6 +27,10 @@
  *     and never synchronise the device.  Host arrays (tile lists, head maps,
  *     pointer lists) are read before the call returns.
  *   - The library allocates no device memory and keeps no state between calls.
+ *   - Every argument is checked before anything is enqueued, so a call that
+ *     returns MA_ERR_INVALID or MA_ERR_UNSUPPORTED has enqueued nothing.  A call
+ *     that returns MA_ERR_LAUNCH (the runtime refused a launch) may have
+ *     enqueued the launches before it.
  *   - Layouts: Q, O, dO are [B, S, Hq, d]; K, V are [B, S, Hkv, d]; LSE is
  *     [B, Hq, S] float32 (natural log).  Strides are in ELEMENTS; the d axis
  *     (and the S axis of LSE) must have stride 1.  bf16 tensors need 16-byte
@@ -127,7 +131,10 @@ typedef struct {
  * in fp32 between them).
  * In either mode, tiles of one call that name the same o are applied in list
  * order (each waits for the one before), so a ring of KV partitions can be
- * handed over as one call.
+ * handed over as one call.  Outputs of different tiles that are one buffer
+ * shifted along the sequence axis by fewer rows than the earlier view holds are
+ * rejected (MA_ERR_INVALID); other partial overlaps between different outputs,
+ * and outputs that alias inputs, are undefined.
  * --------------------------------------------------------------------------- */
 typedef struct {
   const void* q;  /* device, [B, sq, Hq, d], dtype */
@@ -223,10 +230,14 @@ int mesh_attn_reduce_add(const ma_reduce_args* args, void* stream);
  *
  * accumulate = 0: dq, dk, dv are overwritten; = 1: the results are added to
  * what the buffers hold.  All tiles naming the same dk (or dv) buffer must name
- * the same k and v buffers and sk.  dq buffers of different tiles must not
- * overlap unless they are identical (then contributions add).  bf16 only.
- * The workspace (device, >= mesh_attn_tile_bwd_workspace_size bytes, 256-byte
- * aligned) holds D and per-call scratch; its contents on entry do not matter.
+ * the same k and v buffers and sk.  dq (dk, dv) buffers of different tiles
+ * must not overlap unless they are identical (then contributions add): one
+ * buffer shifted along the sequence axis by fewer rows than the earlier view
+ * holds is rejected (MA_ERR_INVALID), other partial overlaps are undefined.
+ * bf16 only.  The workspace (device, >= mesh_attn_tile_bwd_workspace_size
+ * bytes, 256-byte aligned) holds D and per-call scratch; its contents on entry
+ * do not matter.  mesh_attn_tile_bwd_workspace_size returns 0 for arguments it
+ * cannot size (no tiles, sizes out of range, invalid positions under a mask).
  * --------------------------------------------------------------------------- */
 typedef struct {
   const void* q;     /* device bf16 [B, sq, Hq, d] */

@@ -10,6 +10,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # the host-only sanitizer build (tests/test_host_sanitizers.py) reruns the CPU tests of the ABI,
+    # the mapper and the planner against its own library, named here
+    alt = os.environ.get("MESH_ATTN_TEST_LIB")
+    if alt:
+        from distributed_long_context_amd import _abi
+        _abi.LIB_PATH = alt
 
 
 def pytest_collection_modifyitems(config, items):

@@ -161,3 +161,103 @@ def test_bwd_workspace_counts_one_segment_pieces():
     assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) == blocked(130)
     a.mask_mode = _abi.MA_MASK_STRIPED_ZIGZAG  # two pieces of 65 rows
     assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) == 2 * blocked(65)
+
+
+def _tile_arr(n, sq=64, sk=64, base=1 << 20, step=1 << 24):
+    t = (_abi.ma_tile * n)()
+    for i in range(n):
+        b = base + i * step
+        t[i].q, t[i].k, t[i].v, t[i].o, t[i].lse = b, b + 4096, b + 8192, b + 12288, b + 16384
+        t[i].sq, t[i].sk = sq, sk
+        t[i].q_pos.nseg = t[i].k_pos.nseg = 1
+        t[i].q_pos.seg[0].stride = t[i].k_pos.seg[0].stride = 1
+    return t
+
+
+def test_tile_fwd_rejects_shifted_outputs_without_launching():
+    # two tiles whose O is one buffer shifted by 10 rows (fewer than the 64 it holds): rejected
+    L = _abi.lib()
+    t = _tile_arr(2)
+    a = _fwd_args(ntiles=2, hq=4, hkv=2)
+    a.tiles = C.cast(t, C.POINTER(_abi.ma_tile))
+    row = 4 * 128  # o_stride[1] in elements (hq * d)
+    a.q_stride[:] = a.o_stride[:] = (64 * row, row, 128)
+    a.k_stride[:] = a.v_stride[:] = (64 * 256, 256, 128)
+    a.lse_stride[:] = (4 * 64, 64)
+    t[1].o = t[0].o + 10 * row * 2
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID
+    assert b"overlap" in L.mesh_attn_last_error()
+    # LSE shifted by 3 positions of 64
+    t[1].o = t[0].o + 64 * row * 2 * 4
+    t[1].lse = t[0].lse + 3 * 4
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID
+
+
+def test_tile_fwd_is_planned_before_launching():
+    # a valid tile, then one too large for a launch: the error comes from the plan, before the
+    # first tile is enqueued (an enqueue on this host, which has no GPU, would report a launch error)
+    L = _abi.lib()
+    t = _tile_arr(2)
+    a = _fwd_args(ntiles=2, hq=128, hkv=1, batch=2)
+    a.tiles = C.cast(t, C.POINTER(_abi.ma_tile))
+    row = 128 * 128
+    a.q_stride[:] = a.o_stride[:] = (0, row, 128)
+    a.k_stride[:] = a.v_stride[:] = (0, 128, 128)
+    a.lse_stride[:] = (0, 0)
+    t[1].sq = (1 << 31) - 2
+    assert L.mesh_attn_tile_fwd(C.byref(a), None) == _abi.MA_ERR_INVALID
+    assert b"too large" in L.mesh_attn_last_error()
+
+
+def _bwd_tiles(n, sq=64, sk=64, base=1 << 20, step=1 << 26):
+    t = (_abi.ma_bwd_tile * n)()
+    for i in range(n):
+        b = base + i * step
+        (t[i].q, t[i].k, t[i].v, t[i].o, t[i].dout, t[i].lse, t[i].dq, t[i].dk, t[i].dv) = \
+            [b + 65536 * j for j in range(9)]
+        t[i].sq, t[i].sk = sq, sk
+        t[i].q_pos.nseg = t[i].k_pos.nseg = 1
+        t[i].q_pos.seg[0].stride = t[i].k_pos.seg[0].stride = 1
+    return t
+
+
+def _bwd_args_c(t, n, hq=4, hkv=2, mask=_abi.MA_MASK_NONE):
+    a = _abi.ma_tile_bwd_args()
+    a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.scale, a.ntiles = _abi.MA_BF16, 1, hq, hkv, 128, 0.1, n
+    a.mask_mode = mask
+    a.tiles = C.cast(t, C.POINTER(_abi.ma_bwd_tile))
+    a.q_stride[:] = a.dq_stride[:] = (0, hq * 128, 128)
+    a.k_stride[:] = a.dk_stride[:] = (0, hkv * 128, 128)
+    a.lse_stride[:] = (0, 0)
+    return a
+
+
+def test_bwd_rejects_shifted_gradient_outputs():
+    L = _abi.lib()
+    t = _bwd_tiles(2)
+    a = _bwd_args_c(t, 2)
+    t[1].dq = t[0].dq + 5 * 4 * 128 * 4  # dq of tile 1 = dq of tile 0 shifted by 5 rows of 64
+    assert L.mesh_attn_tile_bwd(C.byref(a), C.c_void_p(1 << 30), 1 << 20, None) == _abi.MA_ERR_INVALID
+    assert b"overlap" in L.mesh_attn_last_error()
+
+
+def test_bwd_workspace_size_rejects_bad_segments():
+    # under a mask the segments are expanded: a position map with more than MA_MAX_SEGMENTS
+    # segments (or a bad stride) gives 0 instead of being read past its end
+    L = _abi.lib()
+    t = _bwd_tiles(1)
+    a = _bwd_args_c(t, 1, mask=_abi.MA_MASK_STRIPED_ZIGZAG)
+    assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) > 0
+    t[0].q_pos.nseg = _abi.MA_MAX_SEGMENTS + 1
+    assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) == 0
+    t[0].q_pos.nseg = 1
+    t[0].k_pos.seg[0].stride = 0
+    assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) == 0
+
+
+def test_python_workspace_helper_needs_the_mask_mode():
+    import inspect
+    import distributed_long_context_amd as ma
+    params = inspect.signature(ma.mesh_attn_tile_bwd_workspace_size).parameters
+    assert params["mask_mode"].default is inspect.Parameter.empty
+    assert params["scale"].default is inspect.Parameter.empty

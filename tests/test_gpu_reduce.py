@@ -71,7 +71,7 @@ def test_split_backward_then_add_reduce():
         for q, o_dev, do, l_dev in h:
             dq = torch.empty((1, sq, hq, d), dtype=torch.float32, device=DEV)
             tiles.append(BwdTile(q, k, v, o_dev, do, l_dev, dq, dk, dv))
-        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(tiles, float(scale))), dtype=torch.uint8,
+        ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(tiles, float(scale), ma.MA_MASK_NONE)), dtype=torch.uint8,
                          device=DEV)
         ma.mesh_attn_tile_bwd(tiles, float(scale), ma.MA_MASK_NONE, workspace=ws)
         dks.append(dk)

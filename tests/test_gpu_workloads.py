@@ -270,7 +270,7 @@ def test_zigzag_causal_128k_rank5_backward():
         host.append(dict(q=qv, o=ov, do=dov, lse=lv.astype(np.float64), q_pos=positions(qpos[i], C)))
     tiles = [BwdTile(dev_in[i][0], K[j][0], V[j][0], dev_in[i][1], dev_in[i][2], dev_in[i][3], dev_in[i][4],
                      dk[j], dv[j], qpos[i], kpos[j]) for i, j, _ in wl]
-    ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(tiles, float(SCALE))), dtype=torch.uint8,
+    ws = torch.empty(max(256, ma.mesh_attn_tile_bwd_workspace_size(tiles, float(SCALE), ma.MA_MASK_CAUSAL)), dtype=torch.uint8,
                      device=DEV)
     ma.mesh_attn_tile_bwd(tiles, float(SCALE), ma.MA_MASK_CAUSAL, workspace=ws)
     torch.cuda.synchronize()
