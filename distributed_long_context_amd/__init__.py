@@ -17,6 +17,7 @@ from ._abi import (MA_OK, MA_ERR_INVALID, MA_ERR_UNSUPPORTED, MA_ERR_LAUNCH, MA_
 
 __all__ = [
     "mesh_attn_tile_fwd", "mesh_attn_merge", "mesh_attn_reduce_add", "mesh_attn_tile_bwd", "mesh_attn_tile_bwd_workspace_size",
+    "mesh_attn_tile_bwd_noalloc",
     "mesh_attn_map_mesh_tile", "mesh_attn_map_groups", "mesh_attn_map_zigzag", "mesh_attn_pos_contiguous",
     "mesh_attn_pos_zigzag", "mesh_attn_pos_striped", "mesh_attn_pos_at", "mesh_attn_classify",
     "mesh_attn_count_allowed", "mesh_attn_build_worklist", "mesh_attn_goo_plan", "mesh_attn_version", "Pos", "Tile", "BwdTile",
@@ -306,6 +307,17 @@ def mesh_attn_tile_bwd(tiles: Sequence[BwdTile], scale: float, mask_mode: int = 
     _abi.check(lib().mesh_attn_tile_bwd(C.byref(a), C.c_void_p(workspace.data_ptr()),
                                         workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
                "mesh_attn_tile_bwd")
+
+
+def mesh_attn_tile_bwd_noalloc(tiles: Sequence[BwdTile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
+                               accumulate: bool = False, stream=None) -> None:
+    """mesh_attn_tile_bwd with the library's built-in scratch as the workspace: no device memory is
+    allocated (here or in the library).  Calls that overlap on one GPU race on that scratch."""
+    tiles = list(tiles)
+    if not tiles:
+        return
+    a, keep = _bwd_args(tiles, scale, mask_mode, head_map, accumulate)
+    _abi.check(lib().mesh_attn_tile_bwd_noalloc(C.byref(a), _stream_ptr(stream)), "mesh_attn_tile_bwd_noalloc")
 
 
 # ----------------------------------------------------------------- mapper --

@@ -15,6 +15,7 @@ MA_F32, MA_BF16 = 0, 1
 MA_MASK_NONE, MA_MASK_CAUSAL, MA_MASK_STRIPED_ZIGZAG = 0, 1, 2
 MA_TILE_EMPTY, MA_TILE_PARTIAL, MA_TILE_FULL = 0, 1, 2
 MA_MAX_SEGMENTS, MA_MAX_MERGE, MA_MAX_HEADS, MA_MAX_TILES = 4, 64, 128, 4096
+MA_BWD_NOALLOC_MAX_WORKSPACE = 32 << 20
 
 I32, I64, F32 = C.c_int32, C.c_int64, C.c_float
 VP = C.c_void_p
@@ -80,6 +81,7 @@ SIGNATURES = {
                                  I32, C.POINTER(ma_goo_step)]),
     "mesh_attn_tile_bwd_workspace_size": (C.c_size_t, [C.POINTER(ma_tile_bwd_args)]),
     "mesh_attn_tile_bwd": (I32, [C.POINTER(ma_tile_bwd_args), VP, C.c_size_t, VP]),
+    "mesh_attn_tile_bwd_noalloc": (I32, [C.POINTER(ma_tile_bwd_args), VP]),
     "mesh_attn_map_mesh_tile": (I32, [I32, I32, I32, I32, I32, C.POINTER(I32), C.POINTER(I32)]),
     "mesh_attn_map_groups": (I32, [I32, I32, I32, I32, C.POINTER(I32), C.POINTER(I32)]),
     "mesh_attn_map_zigzag": (I32, [I32, I32, C.POINTER(I32)]),

@@ -8,6 +8,7 @@
 #include <string>
 #include <vector>
 #include <algorithm>
+#include <mutex>
 #include <utility>
 
 #include "mesh_attn.h"
@@ -754,6 +755,69 @@ int mesh_attn_tile_bwd(const ma_tile_bwd_args* a, void* workspace, size_t worksp
   if (workspace_bytes < need || (need > 0 && !workspace) || ((uintptr_t)workspace & 255u))
     return set_error(MA_ERR_INVALID, "workspace missing, too small or not 256-byte aligned");
   return run_bwd(a, workspace, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The backward without any allocation.  Its only scratch buffer, the blocked LSE/D
+// workspace, lives in this device array (one copy per GPU, held until the process
+// ends).  In host code the name `scratch` is a host-side stand-in, never a device
+// address: its device address is looked up once per device with
+// hipGetSymbolAddress and only that pointer is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[MA_BWD_NOALLOC_MAX_WORKSPACE];
+
+namespace ma {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (the current device, which must be the
+// stream's); looked up on the first call on each device.
+int scratch_for_device(void* stream, void** out) {
+  int dev = -1;
+  int rc = check_hip((int)hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (stream) {
+    int sdev = -1;
+    rc = check_hip((int)hipStreamGetDevice((hipStream_t)stream, &sdev), "hipStreamGetDevice");
+    if (rc) return rc;
+    if (sdev != dev) return set_error(MA_ERR_INVALID, "the stream belongs to another device than the current one");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return set_error(MA_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    rc = check_hip((int)hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (rc) return rc;
+    if (!ptr || ((uintptr_t)ptr & 255u)) return set_error(MA_ERR_LAUNCH, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MA_OK;
+}
+
+}  // namespace
+}  // namespace ma
+
+extern "C" {
+
+int mesh_attn_tile_bwd_noalloc(const ma_tile_bwd_args* a, void* stream) {
+  int rc = validate_bwd(a);
+  if (rc) return rc;
+  if (a->ntiles == 0) return MA_OK;
+  const size_t need = mesh_attn_tile_bwd_workspace_size(a);
+  if (need > (size_t)MA_BWD_NOALLOC_MAX_WORKSPACE) {
+    std::string m = "this backward needs " + std::to_string(need) + " bytes of workspace; the built-in scratch holds " +
+                    std::to_string((size_t)MA_BWD_NOALLOC_MAX_WORKSPACE) + " (use mesh_attn_tile_bwd with a workspace)";
+    return set_error(MA_ERR_INVALID, m.c_str());
+  }
+  void* ws = nullptr;
+  rc = scratch_for_device(stream, &ws);
+  if (rc) return rc;
+  return run_bwd(a, ws, stream);
 }
 
 }  // extern "C"

@@ -26,7 +26,9 @@
  *     them alive until the stream reaches that point.  Calls are asynchronous
  *     and never synchronise the device.  Host arrays (tile lists, head maps,
  *     pointer lists) are read before the call returns.
- *   - The library allocates no device memory and keeps no state between calls.
+ *   - The library allocates no device memory and keeps no state between calls,
+ *     except for mesh_attn_tile_bwd_noalloc's scratch array (a static device
+ *     array, one per GPU) and the table of its device addresses.
  *   - Every argument is checked before anything is enqueued, so a call that
  *     returns MA_ERR_INVALID or MA_ERR_UNSUPPORTED has enqueued nothing.  A call
  *     that returns MA_ERR_LAUNCH (the runtime refused a launch) may have
@@ -277,6 +279,23 @@ typedef struct {
 
 size_t mesh_attn_tile_bwd_workspace_size(const ma_tile_bwd_args* args);
 int mesh_attn_tile_bwd(const ma_tile_bwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Tile backward that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, validation and results as
+ * mesh_attn_tile_bwd, but the workspace is a scratch array built into the
+ * library: MA_BWD_NOALLOC_MAX_WORKSPACE bytes on each GPU the library runs on,
+ * held until the process ends.  A call whose mesh_attn_tile_bwd_workspace_size
+ * exceeds that size returns MA_ERR_INVALID without enqueueing anything.  The
+ * stream must belong to the current device.  No hipMalloc/hipFree or allocating
+ * library call is made; the first call on a device looks up the array's device
+ * address.  All calls on one GPU share its array (nothing in it needs clearing:
+ * each call writes every byte it reads), so calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race.
+ * --------------------------------------------------------------------------- */
+#define MA_BWD_NOALLOC_MAX_WORKSPACE (32u << 20) /* bytes: 8 Q partitions of 16384 rows x 32 heads */
+int mesh_attn_tile_bwd_noalloc(const ma_tile_bwd_args* args, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Host-only mapper.  Pure functions: no device work, no allocation; output

@@ -239,6 +239,7 @@ def test_bwd_rejects_shifted_gradient_outputs():
     t[1].dq = t[0].dq + 5 * 4 * 128 * 4  # dq of tile 1 = dq of tile 0 shifted by 5 rows of 64
     assert L.mesh_attn_tile_bwd(C.byref(a), C.c_void_p(1 << 30), 1 << 20, None) == _abi.MA_ERR_INVALID
     assert b"overlap" in L.mesh_attn_last_error()
+    assert L.mesh_attn_tile_bwd_noalloc(C.byref(a), None) == _abi.MA_ERR_INVALID
 
 
 def test_bwd_workspace_size_rejects_bad_segments():
@@ -253,6 +254,19 @@ def test_bwd_workspace_size_rejects_bad_segments():
     t[0].q_pos.nseg = 1
     t[0].k_pos.seg[0].stride = 0
     assert L.mesh_attn_tile_bwd_workspace_size(C.byref(a)) == 0
+
+
+def test_bwd_noalloc_rejects_workspace_beyond_its_scratch():
+    # 128 heads x 16448 rows x 8 bytes of LSE/D blocks = 16.8 MiB per Q partition: two partitions
+    # need more than the 32 MiB built-in scratch, which is refused before anything runs
+    L = _abi.lib()
+    t = _bwd_tiles(2, sq=16448, sk=64, step=1 << 33)
+    a = _bwd_args_c(t, 2, hq=128, hkv=8)
+    need = L.mesh_attn_tile_bwd_workspace_size(C.byref(a))
+    assert need > _abi.MA_BWD_NOALLOC_MAX_WORKSPACE
+    assert L.mesh_attn_tile_bwd_noalloc(C.byref(a), None) == _abi.MA_ERR_INVALID
+    assert b"scratch" in L.mesh_attn_last_error()
+    assert L.mesh_attn_tile_bwd_noalloc(None, None) == _abi.MA_ERR_INVALID
 
 
 def test_python_workspace_helper_needs_the_mask_mode():
