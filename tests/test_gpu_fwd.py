@@ -375,3 +375,51 @@ def test_fwd_accumulate_into_incoming_partial():
     Oref, Lref = merge([(ov, lv.astype(np.float64)), (Ot, Lt)])
     check_close("O", host_f64(o), Oref, BF16_O_TOL, normalised_also=False)
     check_close("LSE", host_f64(lse), Lref, BF16_LSE_TOL)
+
+
+@pytest.mark.parametrize("d,acc", [(128, False), (64, False), (128, True)])
+def test_small_tiles_mixed_call(d, acc):
+    """30 small tiles in one call, the four-wave kernel's case: 22 tiles of [CHARM+]'s smallest
+    partition size (210 x 210, GQA 32/8) with tiles of one key block (48 keys), a single query row,
+    the 16-block limit (1000 keys) and ragged sizes, every tensor a prefix view of a longer buffer
+    (shared strides), more workgroups than two per CU; optionally folded into seeded incoming
+    partials.  Every row of every tile is checked against the oracle."""
+    hq, hkv = 32, 8
+    scale = np.float32(1.0 / math.sqrt(d))
+    shapes = [(210, 210)] * 22 + [(210, 48), (37, 48), (64, 64), (100, 130), (210, 1000), (1, 5), (33, 210),
+                                  (210, 65)]
+    log(f"[small tiles mixed call] d={d} acc={acc} tiles={len(shapes)}")
+    wid = 2600 + d + (1 if acc else 0)
+    smax = 1024  # every tensor is a prefix view of a buffer of this length, so all tiles share strides
+
+    def view(t, axis_len, kind):
+        shape = (1, smax, t.shape[2], t.shape[3]) if kind == "bshd" else (1, t.shape[1], smax)
+        buf = torch.full(shape, float("nan"), dtype=t.dtype, device=DEV)
+        v = buf[:, :axis_len] if kind == "bshd" else buf[:, :, :axis_len]
+        v.copy_(t)
+        return v
+
+    tiles, refs = [], []
+    for i, (sq, sk) in enumerate(shapes):
+        q, qv = gen(wid, synthetic.T_Q, i, (1, sq, hq, d))
+        k, kv = gen(wid, synthetic.T_K, i, (1, sk, hkv, d))
+        v, vv = gen(wid, synthetic.T_V, i, (1, sk, hkv, d))
+        O, L = attn_tile(qv, kv, vv, scale)
+        if acc:
+            ob, ov = gen(wid, synthetic.T_O_IN, i, (1, sq, hq, d))
+            li = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (1, hq, sq)) + np.float32(math.log(sk))).astype(
+                np.float32)
+            o, lse = ob, torch.from_numpy(li).to(DEV)
+            O, L = merge([(ov, li.astype(np.float64)), (O, L)])
+        else:
+            o = torch.full((1, sq, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((1, hq, sq), float("nan"), dtype=torch.float32, device=DEV)
+        tiles.append(Tile(view(q, sq, "bshd"), view(k, sk, "bshd"), view(v, sk, "bshd"), view(o, sq, "bshd"),
+                          view(lse, sq, "bhs")))
+        refs.append((O, L))
+    assert sum(((sq + 31) // 32 * (hq // hkv) + 3) // 4 * hkv for sq, _ in shapes) > 2 * 256
+    ma.mesh_attn_tile_fwd(tiles, float(scale), ma.MA_MASK_NONE, accumulate=acc)
+    torch.cuda.synchronize()
+    for t, (Oref, Lref) in zip(tiles, refs):
+        check_close("O", host_f64(t.o), Oref, BF16_O_TOL, normalised_also=False)
+        check_close("LSE", host_f64(t.lse), Lref, BF16_LSE_TOL)
