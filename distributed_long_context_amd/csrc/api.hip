@@ -204,8 +204,9 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   rc = check_shifted_outputs(a->ntiles, [&](int i) { return (const void*)a->tiles[i].lse; },
                              [&](int i) { return a->tiles[i].sq; }, 4, "lse");
   if (rc) return rc;
-  // Tiles go to one of four launches: by how much masking they need (bit 0) and, in
-  // bf16, by length (bit 1).  FULL tiles (and every tile without a mask) run the
+  // Tiles go to one of five launch classes: by how much masking they need (bit 0) and, in
+  // bf16, by length (bit 1), or (class 4) the resident-KV kernel, which takes the unmasked
+  // bf16 tiles of kFwdResMinKeys < sk <= kFwdResKeys keys.  FULL tiles (and every tile without a mask) run the
   // unmasked kernel, PARTIAL ones the masked kernel, whose key positions must be one
   // segment: a tile whose key positions have several segments is cut into one piece
   // per segment (the keys of a segment are contiguous rows) and its pieces with any
@@ -222,9 +223,9 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   };
   std::vector<Planned> plan;
   std::vector<FwdParams> batches;
-  FwdParams bp[4];
-  int bn[4] = {0, 0, 0, 0}, bwg[4] = {0, 0, 0, 0};
-  for (int m = 0; m < 4; ++m) {
+  FwdParams bp[5];
+  int bn[5] = {0, 0, 0, 0, 0}, bwg[5] = {0, 0, 0, 0, 0};
+  for (int m = 0; m < 5; ++m) {
     bp[m] = p;
     bp[m].mask = m & 1;
   }
@@ -237,26 +238,32 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     bwg[m] = 0;
   };
   auto flush_all = [&]() {
-    for (int m = 0; m < 4; ++m) flush(m);
+    for (int m = 0; m < 5; ++m) flush(m);
   };
   // queue one tile (or the pieces of one, as a chain): cls is the class of the tile (any
   // chain runs masked), acc its accumulate flag, pieces the key segments after the first
   auto enqueue_chain = [&](const ma_tile* pcs, int npcs, int cls, int acc) -> int {
     bool dup = false;
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < 5; ++k)
       for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == pcs[0].o || bp[k].tiles[j].lse == pcs[0].lse;
     if (dup) flush_all();
     int64_t blocks = 0;
     for (int i = 0; i < npcs; ++i) blocks += (pcs[i].sk + 63) / 64;
     const bool small = bf16 && blocks <= kFwdSmallBlocks;
-    const int m = (cls == MA_TILE_FULL && npcs == 1 ? 0 : 1) | (small ? 2 : 0);
+    const bool whole = cls == MA_TILE_FULL && npcs == 1;
+    const int64_t res_lo = a->head_dim == 128 ? kFwdResMinKeys<128> : kFwdResMinKeys<64>;
+    const int64_t res_hi = a->head_dim == 128 ? kFwdResKeys<128> : kFwdResKeys<64>;
+    const bool resident = bf16 && whole && pcs[0].sk > res_lo && pcs[0].sk <= res_hi;
+    const int m = resident ? 4 : (whole ? 0 : 1) | (small ? 2 : 0);
     const ma_tile& t = pcs[0];
     int64_t wgs, chunks;
     if (bf16) {
-      // 8 (or 4) waves of 32 query rows per workgroup; units are (32-row block, head of the group)
+      // units are (32-row block, head of the group): 8 (or 4) per workgroup of the ring
+      // kernel, one per wave; up to kFwdResUnits per workgroup of the resident kernel
       const int waves = small ? 4 : 8;
       const int64_t nqb = (t.sq + 31) / 32;
-      chunks = (nqb * p.gmax + waves - 1) / waves;
+      const int units = resident ? kFwdResUnits : waves;
+      chunks = (nqb * p.gmax + units - 1) / units;
       wgs = (int64_t)a->batch * a->hkv * chunks;
       wgs = (wgs + 7) / 8 * 8;  // keep each tile's first workgroup on XCD 0
     } else {
@@ -351,7 +358,8 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss, p.o_sh,
                             p.l_sb, p.l_sh, stream);
     } else {
-      e = bf16 ? launch_fwd_bf16(batches[pl.idx], a->head_dim, pl.m & 2 ? 4 : 8, pl.wgs, stream)
+      e = pl.m == 4 ? launch_fwd_bf16_resident(batches[pl.idx], a->head_dim, pl.wgs, stream)
+          : bf16    ? launch_fwd_bf16(batches[pl.idx], a->head_dim, pl.m & 2 ? 4 : 8, pl.wgs, stream)
                : launch_fwd_f32(batches[pl.idx], a->head_dim, pl.wgs, stream);
     }
     rc = check_hip(e, pl.m < 0 ? "fill launch" : "tile_fwd launch");

@@ -75,6 +75,48 @@ struct FwdCfg {
   static constexpr int STAGES = WAVES == 8 ? 5 : 2;
 };
 
+// Epilogue of one wave's 32 query rows: normalise O^T by the row sum and store O (bf16) and
+// LSE (fp32, natural log), or fold them into the (O, LSE) the buffers hold (accumulate):
+// L = ln(e^lse_old + e^lse), O = e^(lse_old - L) O_old + e^(lse - L) O.  orow and lrow address
+// the lane's row; m2 is the running max in log2 units, ltot the row sum (both halves of the wave).
+template <int NC>
+__device__ __forceinline__ void fwd_store_rows(const f32x16 (&oacc)[NC], float m2, float ltot, bool accumulate,
+                                               __bf16* orow, float* lrow, int hl) {
+  const bool has = ltot > 0.0f;
+  float lse = has ? (m2 + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f : -INFINITY;
+  float wn = has ? 1.0f / ltot : 0.0f;  // weight of this tile's unnormalised sums
+  float wo = 0.0f;                      // weight of the output already held (accumulate)
+  if (accumulate) {
+    const float lo = *lrow;
+    const float mx = fmaxf(lo, lse);
+    if (mx == -INFINITY) {
+      wn = 0.0f;
+    } else {
+      const float eo = __expf(lo - mx), en = __expf(lse - mx);
+      const float sum = eo + en;
+      wo = eo / sum;
+      wn *= en / sum;
+      lse = mx + __logf(sum);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __bf16* dst = orow + c * 32 + g * 8 + hl * 4;
+      float v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * wn;
+      if (accumulate) {
+        const bf16x4 old = *(const bf16x4*)dst;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = __builtin_fmaf(wo, (float)old[i], v4[i]);
+      }
+      *(bf16x4*)dst = pack_bf16x4(v4);
+    }
+  if (hl == 0) *lrow = lse;
+}
+
 // MASKED: causal on positions, the key positions one segment (global = kgb +
 // t * kst, growing with t), so every mask decision reduces to the last allowed
 // key index of a query position.  Without it only a ragged last block is masked.
@@ -414,48 +456,229 @@ fwd_bf16_kernel(const FwdParams p) {
   }
 
   if (!active) return;
-  // ---- epilogue: normalise, store O (bf16) and LSE (fp32, natural log), or fold them
-  // into the pair the buffers hold ----
-  __bf16* Og = (__bf16*)T.o + (int64_t)b * p.o_sb + (int64_t)my_head * p.o_sh;
-  float* Lg = T.lse + (int64_t)b * p.l_sb + (int64_t)my_head * p.l_sh;
+  // ---- epilogue ----
   const float ltot = xhalf_sum(lsum);
   const int row = q0 + l32;
   if (row >= T.sq) return;
-  const bool has = ltot > 0.0f;
-  float lse = has ? (m2 + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f : -INFINITY;
-  float wn = has ? 1.0f / ltot : 0.0f;  // weight of this tile's unnormalised sums
-  float wo = 0.0f;                      // weight of the output already held (accumulate)
-  __bf16* orow = Og + (int64_t)row * p.o_ss;
-  if (T.accumulate & 1) {
-    // fold into (O_old, lse_old): L = ln(e^lse_old + e^lse), O = e^(lse_old-L) O_old + e^(lse-L) O
-    const float lo = Lg[row];
-    const float mx = fmaxf(lo, lse);
-    if (mx == -INFINITY) {
-      wn = 0.0f;
-    } else {
-      const float eo = __expf(lo - mx), en = __expf(lse - mx);
-      const float sum = eo + en;
-      wo = eo / sum;
-      wn *= en / sum;
-      lse = mx + __logf(sum);
+  __bf16* orow = (__bf16*)T.o + (int64_t)b * p.o_sb + (int64_t)my_head * p.o_sh + (int64_t)row * p.o_ss;
+  float* lrow = T.lse + (int64_t)b * p.l_sb + (int64_t)my_head * p.l_sh + row;
+  fwd_store_rows(oacc, m2, ltot, T.accumulate & 1, orow, lrow, hl);
+}
+
+// Resident-KV instance, for unmasked tiles of few keys (kFwdResMinKeys < sk <= kFwdResKeys<D>):
+// one workgroup of 8 waves (two per SIMD) per (tile, batch, KV head, chunk of up to
+// kFwdResUnits units) loads the whole K and V of its KV head into LDS once, then every wave runs
+// its units (32 query rows of one query head; unit u of the chunk goes to wave u % 8) in turn
+// against the resident blocks, with no barrier after the loads and the next unit's query
+// fragments loaded under the current unit's blocks.  The ring kernel instead gives each
+// workgroup only 4 or 8 units and re-streams K/V for every workgroup, so at a few hundred keys
+// its start-up dominates.  A unit's online softmax is the ring kernel's, step for step (the
+// results are the same bit for bit), over the 32-key halves that hold a key of the tile: a half
+// wholly past the last key, and the scores after the last half, are not computed.
+template <int D>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_bf16_resident_kernel(const FwdParams p) {
+  using C = FwdCfg<D, 8>;
+  constexpr int kWaves = 8;
+  constexpr int RB = kFwdResKeys<D> / kBN;  // resident blocks
+  __shared__ __attribute__((aligned(1024))) __bf16 kv_s[2][RB][C::BLK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  // ---- which tile / batch / KV head / chunk of units (the ring kernel's decode) ----
+  const int w = blockIdx.x;
+  int ti = 0;
+#pragma unroll
+  for (int j = 1; j < kFwdTilesPerLaunch; ++j) ti += (j < p.ntiles && w >= p.tiles[j].wg_begin) ? 1 : 0;
+  const FwdTile T = p.tiles[__builtin_amdgcn_readfirstlane(ti)];
+  const int local = w - T.wg_begin;
+  const int kvh = local % p.hkv;
+  const int rest = local / p.hkv;
+  const int chunk = rest % T.chunks;
+  const int b = rest / T.chunks;
+  if (b >= p.batch) return;  // padding workgroup (uniform)
+  const int g0 = p.kv_first[kvh];
+  const int gsz = p.kv_first[kvh + 1] - g0;
+  if (gsz <= 0) return;
+  // units (32-row block, head of the group), query-block major
+  const int nunits = (T.sq + kQW - 1) / kQW * gsz;
+  const int u_begin = chunk * kFwdResUnits;
+  const int u_end = min(nunits, u_begin + kFwdResUnits);
+  if (u_begin >= u_end) return;  // uniform
+
+  const __bf16* Kg = (const __bf16*)T.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+  const __bf16* Vg = (const __bf16*)T.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+  const int sk = T.sk;
+  const int nkb = (sk + kBN - 1) / kBN;  // at most RB: the host routes longer tiles elsewhere
+  const int klast = sk - 1;
+  const int kfull = sk / kBN;  // blocks with every key inside the tile
+  const int k_ss = (int)p.k_ss, v_ss = (int)p.v_ss;  // below 2^24 (checked by the caller)
+
+  // ---- every K and V block into LDS (block kb in slot kb; rows past the end repeat the last) ----
+  auto load_row = [&](int i) { return ((wave * C::LPW + i) * 64 + lane) / C::CH; };
+  auto load_col = [&](int i) { return ((((wave * C::LPW + i) * 64 + lane) % C::CH) ^ swz<D>(load_row(i))) * 8; };
+#pragma unroll
+  for (int kb = 0; kb < RB; ++kb) {
+    if (kb < nkb) {
+      const __bf16* kbase = Kg + (int64_t)kb * kBN * p.k_ss;
+      const __bf16* vbase = Vg + (int64_t)kb * kBN * p.v_ss;
+      const int valid = sk - kb * kBN;
+#pragma unroll
+      for (int i = 0; i < C::LPW; ++i) {
+        const int r = min(load_row(i), valid - 1);
+        lds_dma16(kbase, (uint32_t)(r * k_ss + load_col(i)) * 2u, lds_addr(&kv_s[0][kb][(wave * C::LPW + i) * 512]));
+        lds_dma16(vbase, (uint32_t)(r * v_ss + load_col(i)) * 2u, lds_addr(&kv_s[1][kb][(wave * C::LPW + i) * 512]));
+      }
     }
   }
+
+  // ---- query fragments of a unit (B operand of S^T = K Q^T) ----
+  auto unit_head = [&](int u) { return p.heads_of[g0 + (u % gsz)]; };
+  auto load_q = [&](int u, bf16x8 (&f)[C::KS]) {
+    const int row = (u / gsz) * kQW + l32;
+    const bool ok = row < T.sq;
+    const __bf16* Qg = (const __bf16*)T.q + (int64_t)b * p.q_sb + (int64_t)unit_head(u) * p.q_sh + (int64_t)row * p.q_ss;
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      __bf16* dst = orow + c * 32 + g * 8 + hl * 4;
-      float v4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * wn;
-      if (T.accumulate & 1) {
-        const bf16x4 old = *(const bf16x4*)dst;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = __builtin_fmaf(wo, (float)old[i], v4[i]);
-      }
-      *(bf16x4*)dst = pack_bf16x4(v4);
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8 z = {};
+      f[ks] = ok ? *(const bf16x8*)(Qg + ks * 16 + hl * 8) : z;
     }
-  if (hl == 0) Lg[row] = lse;
+  };
+  int u = u_begin + wave;
+  bf16x8 qf[C::KS];
+  if (u < u_end) load_q(u, qf);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the blocks and the first fragments
+  __syncthreads();
+  if (u >= u_end) return;  // no unit for this wave
+
+  uint32_t kaddr[C::KS], kaddr_tr_unused[C::NC][2], vaddr_b128_unused[C::KS], vaddr[C::NC][2];
+  tile_lane_addrs<D>(kv_s[0][0], lane, kaddr, kaddr_tr_unused);
+  tile_lane_addrs<D>(kv_s[1][0], lane, vaddr_b128_unused, vaddr);
+  constexpr uint32_t kBlockBytes = C::BLK * 2;
+  const float c2 = p.scale_log2;
+
+  f32x16 oacc[C::NC];
+  float m2, lsum, mb2;  // running max (log2 units), the lane's share of the row sum, a half's max
+  // S^T of 32-key half kb2 of block kb
+  auto s_half = [&](int kb, int kb2, f32x16& s) {
+    const uint32_t off = kb * kBlockBytes + kb2 * 32 * D * 2;
+    s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 kf = lds_read_b128(kaddr[ks] + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+  };
+  // mask (keys past the last one; key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8) and row max of a
+  // half, in log2 units
+  auto half_max = [&](int kb, int kb2, f32x16& s, auto may_mask) {
+    if constexpr (decltype(may_mask)::value) {
+      if (kb >= kfull) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
+          s[e] = key <= klast ? s[e] : -INFINITY;
+        }
+      }
+    }
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+    mb2 = xhalf_max(mx) * c2;
+  };
+  // raise the running max when a row's new max exceeds it by more than 8 (the ring kernel's rule)
+  auto maybe_rescale = [&]() {
+    if (__any(mb2 > m2 + 8.0f)) {
+      const float mn = fmaxf(m2, mb2);
+      const float alpha = (mn == -INFINITY || m2 == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m2 - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+      m2 = mn;
+    }
+  };
+  auto has_keys = [&](int kb, int kb2) { return kb * kBN + kb2 * 32 < sk; };
+  // One step over half kb2 of block kb, whose scores are in sc and whose max is already folded
+  // into m2: the exponentials while the score MFMAs of the next half (block nkb_, half nkb2) run,
+  // then the half's PV MFMAs and the next half's mask and max.  A half with no key of the tile is
+  // only ever the last one (its step does nothing, and no scores follow it).
+  auto half_step = [&](auto may_mask, int kb, int kb2, f32x16& sc, int nkb_, int nkb2, f32x16& sn) {
+    const bool nxt = has_keys(nkb_, nkb2);
+    if (!has_keys(kb, kb2)) {
+      mb2 = -INFINITY;
+      return;
+    }
+    __builtin_amdgcn_iglp_opt(0);
+    const float mref = (m2 == -INFINITY) ? 0.0f : m2;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half * 8 + i], c2, -mref));
+        lsum += pv[i];
+      }
+      pf[half] = pack_bf16x8(pv);
+    }
+    if (nxt) s_half(nkb_, nkb2, sn);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t off = kb * kBlockBytes + (kb2 * 2 + half) * 16 * D * 2;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const bf16x4 lo = lds_read_tr16(vaddr[c][0] + off);
+        const bf16x4 hi = lds_read_tr16(vaddr[c][1] + off);
+        oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(lo, hi), pf[half], oacc[c], 0, 0, 0);
+      }
+    }
+    if (nxt) half_max(nkb_, nkb2, sn, may_mask);
+    else mb2 = -INFINITY;
+  };
+  auto run_unit = [&](auto may_mask) {
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
+    m2 = -INFINITY;
+    lsum = 0.f;
+    f32x16 sA, sB;
+    s_half(0, 0, sA);
+    half_max(0, 0, sA, may_mask);
+    maybe_rescale();
+    for (int j = 0; j < nkb; ++j) {
+      half_step(may_mask, j, 0, sA, j, 1, sB);
+      maybe_rescale();
+      half_step(may_mask, j, 1, sB, j + 1, 0, sA);
+      maybe_rescale();
+    }
+  };
+
+  // ---- the wave's units: u_begin + wave + 8 i ----
+  for (;;) {
+    const int un = u + kWaves;
+    bf16x8 qn[C::KS];
+    if (un < u_end) load_q(un, qn);  // in flight under this unit's blocks
+    if (sk % kBN != 0) run_unit(std::true_type{});  // the last block is ragged
+    else run_unit(std::false_type{});
+    const float ltot = xhalf_sum(lsum);
+    const int row = (u / gsz) * kQW + l32;
+    if (row < T.sq) {
+      const int64_t h = unit_head(u);
+      __bf16* orow = (__bf16*)T.o + (int64_t)b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss;
+      float* lrow = T.lse + (int64_t)b * p.l_sb + h * p.l_sh + row;
+      fwd_store_rows(oacc, m2, ltot, T.accumulate & 1, orow, lrow, hl);
+    }
+    u = un;
+    if (u >= u_end) break;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qn[ks];
+  }
 }
 
 template <int WAVES>
@@ -471,6 +694,14 @@ void launch_waves(const FwdParams& p, int head_dim, dim3 grid, hipStream_t s) {
 }
 
 }  // namespace
+
+int launch_fwd_bf16_resident(const FwdParams& p, int head_dim, int total_wgs, void* stream) {
+  if (total_wgs <= 0) return 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_resident_kernel<128>), dim3(total_wgs), dim3(512), 0, s, p);
+  else hipLaunchKernelGGL((fwd_bf16_resident_kernel<64>), dim3(total_wgs), dim3(512), 0, s, p);
+  return (int)hipGetLastError();
+}
 
 int launch_fwd_bf16(const FwdParams& p, int head_dim, int waves, int total_wgs, void* stream) {
   if (total_wgs <= 0) return 0;

@@ -65,6 +65,15 @@ static_assert(sizeof(FwdParams) <= 4096, "forward parameters exceed the kernel-a
 // two workgroups per CU; for tiles of at most kFwdSmallBlocks key blocks)
 constexpr int kFwdSmallBlocks = 16;
 int launch_fwd_bf16(const FwdParams& p, int head_dim, int waves, int total_wgs, void* stream);
+// bf16 forward with the whole K and V of a tile resident in LDS, for unmasked tiles of
+// kFwdResMinKeys<D> < sk <= kFwdResKeys<D> keys; a workgroup of 8 waves runs up to kFwdResUnits
+// units of (32 query rows, query head) of one (tile, batch, KV head)
+template <int D>
+constexpr int kFwdResKeys = D == 128 ? 256 : 512;
+template <int D>
+constexpr int kFwdResMinKeys = D == 128 ? 128 : 0;
+constexpr int kFwdResUnits = 32;
+int launch_fwd_bf16_resident(const FwdParams& p, int head_dim, int total_wgs, void* stream);
 int launch_fwd_f32(const FwdParams& p, int head_dim, int total_wgs, void* stream);
 int launch_fill_empty(void* o, float* lse, int dtype, int batch, int sq, int hq, int head_dim,
                       int64_t o_sb, int64_t o_ss, int64_t o_sh, int64_t l_sb, int64_t l_sh, void* stream);

@@ -16,6 +16,7 @@ constexpr int kNoDevice = 100;  // hipErrorNoDevice
 }
 
 int launch_fwd_bf16(const FwdParams&, int, int, int, void*) { return kNoDevice; }
+int launch_fwd_bf16_resident(const FwdParams&, int, int, void*) { return kNoDevice; }
 int launch_fwd_f32(const FwdParams&, int, int, void*) { return kNoDevice; }
 int launch_fill_empty(void*, float*, int, int, int, int, int, int64_t, int64_t, int64_t, int64_t, int64_t, void*) {
   return kNoDevice;

@@ -379,11 +379,11 @@ def test_fwd_accumulate_into_incoming_partial():
 
 @pytest.mark.parametrize("d,acc", [(128, False), (64, False), (128, True)])
 def test_small_tiles_mixed_call(d, acc):
-    """30 small tiles in one call, the four-wave kernel's case: 22 tiles of [CHARM+]'s smallest
-    partition size (210 x 210, GQA 32/8) with tiles of one key block (48 keys), a single query row,
-    the 16-block limit (1000 keys) and ragged sizes, every tensor a prefix view of a longer buffer
-    (shared strides), more workgroups than two per CU; optionally folded into seeded incoming
-    partials.  Every row of every tile is checked against the oracle."""
+    """30 small tiles in one call, the case of the resident-KV and four-wave kernels: 22 tiles of
+    [CHARM+]'s smallest partition size (210 x 210, GQA 32/8) with tiles of one key block (48 keys), a
+    single query row, the four-wave kernel's 16-block limit (1000 keys) and ragged sizes, every tensor
+    a prefix view of a longer buffer (shared strides), more workgroups than two per CU; optionally
+    folded into seeded incoming partials.  Every row of every tile is checked against the oracle."""
     hq, hkv = 32, 8
     scale = np.float32(1.0 / math.sqrt(d))
     shapes = [(210, 210)] * 22 + [(210, 48), (37, 48), (64, 64), (100, 130), (210, 1000), (1, 5), (33, 210),
@@ -419,6 +419,54 @@ def test_small_tiles_mixed_call(d, acc):
         refs.append((O, L))
     assert sum(((sq + 31) // 32 * (hq // hkv) + 3) // 4 * hkv for sq, _ in shapes) > 2 * 256
     ma.mesh_attn_tile_fwd(tiles, float(scale), ma.MA_MASK_NONE, accumulate=acc)
+    torch.cuda.synchronize()
+    for t, (Oref, Lref) in zip(tiles, refs):
+        check_close("O", host_f64(t.o), Oref, BF16_O_TOL, normalised_also=False)
+        check_close("LSE", host_f64(t.lse), Lref, BF16_LSE_TOL)
+
+
+# (d, sq, sk, hq, hkv, batch, head_map): unmasked bf16 tiles of the resident-KV kernel's range
+# (128 < sk <= 256 keys at d = 128, sk <= 512 at d = 64) and the sizes just outside it
+RESIDENT_CASES = [
+    (128, 1100, 129, 32, 8, 1, None),  # 35 row blocks x 4 heads: five chunks of 32 units per KV head
+    (128, 300, 210, 32, 8, 1, None),   # [CHARM+]'s smallest partition size, ragged last block
+    (128, 2, 256, 8, 2, 2, None),      # one row block: most waves have no unit; full last block
+    (128, 77, 257, 4, 4, 1, None),     # one key past the range (ring kernel)
+    (128, 64, 128, 8, 4, 1, None),     # the last size below it (ring kernel)
+    (64, 500, 1, 8, 2, 1, None),       # a single key
+    (64, 300, 511, 6, 3, 2, [0, 0, 0, 1, 2, 2]),  # groups of 3, 1 and 2 query heads
+    (64, 33, 512, 16, 2, 1, None),
+    (64, 40, 513, 16, 2, 1, None),     # one key past the range
+]
+
+
+@pytest.mark.parametrize("acc", [False, True])
+@pytest.mark.parametrize("case", range(len(RESIDENT_CASES)))
+def test_fwd_resident_kv_tiles(case, acc):
+    """Two tiles of one shape in one call, plain or folded into seeded incoming partials; every row
+    of both checked against the oracle."""
+    d, sq, sk, hq, hkv, B, head_map = RESIDENT_CASES[case]
+    log(f"[fwd resident kv] d={d} sq={sq} sk={sk} hq={hq} hkv={hkv} B={B} acc={acc}")
+    scale = np.float32(1.0 / math.sqrt(d))
+    wid = 2700 + 2 * case + (1 if acc else 0)
+    tiles, refs = [], []
+    for i in range(2):
+        q, qv = gen(wid, synthetic.T_Q, i, (B, sq, hq, d))
+        k, kv = gen(wid, synthetic.T_K, i, (B, sk, hkv, d))
+        v, vv = gen(wid, synthetic.T_V, i, (B, sk, hkv, d))
+        O, L = attn_tile(qv, kv, vv, scale, head_map)
+        if acc:
+            o, ov = gen(wid, synthetic.T_O_IN, i, (B, sq, hq, d))
+            li = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (B, hq, sq)) + np.float32(math.log(sk + 1))).astype(
+                np.float32)
+            lse = torch.from_numpy(li).to(DEV)
+            O, L = merge([(ov, li.astype(np.float64)), (O, L)])
+        else:
+            o = torch.full((B, sq, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((B, hq, sq), float("nan"), dtype=torch.float32, device=DEV)
+        tiles.append(Tile(q, k, v, o, lse))
+        refs.append((O, L))
+    ma.mesh_attn_tile_fwd(tiles, float(scale), ma.MA_MASK_NONE, head_map, accumulate=acc)
     torch.cuda.synchronize()
     for t, (Oref, Lref) in zip(tiles, refs):
         check_close("O", host_f64(t.o), Oref, BF16_O_TOL, normalised_also=False)
