@@ -242,11 +242,11 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def stored_traffic():
-    """HBM bytes per headline tile-backward call from the committed counter summary, or None when
-    the summary is missing or was taken on other kernel sources."""
+def stored_traffic(path=None, key="tile_bwd_bytes_per_launch"):
+    """HBM bytes per call from a committed counter summary (default: the headline's tile backward),
+    or None when the summary is missing or was taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             text = f.read()
     except OSError:
         return None
@@ -258,26 +258,63 @@ def stored_traffic():
     if vals.get("source_sha256") != kernel_source_hash():
         return None
     try:
-        return int(vals["tile_bwd_bytes_per_launch"])
+        return int(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+SMALL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_small_tiles_210.md")
+
+
+def _pmc_per_dispatch(path):
+    import csv
+    import collections
+    by = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
+    return by
+
+
+def summarize_pmc_small(fetch_csv, write_csv, copy_mib, calls, command):
+    """Write the HBM-traffic summary of the 210-token small-tile forward (every dispatch of the
+    resident-KV kernel in the run belongs to its `calls` calls) from two rocprofv3 --pmc runs,
+    scaled like summarize_pmc by the plain device copy of copy_mib MiB."""
+    fetch, write = _pmc_per_dispatch(fetch_csv), _pmc_per_dispatch(write_csv)
+    copy_kib = copy_mib * 1024.0
+    cf = [v for (_, n), v in fetch.items() if "copyBuffer" in n]
+    cw = [v for (_, n), v in write.items() if "copyBuffer" in n]
+    f_scale, w_scale = copy_kib / (sum(cf) / len(cf)), copy_kib / (sum(cw) / len(cw))
+    sel = [k for k in fetch if "fwd_bf16_resident_kernel" in k[1]]
+    read = sum(fetch[k] for k in sel) * f_scale * 1024 / calls
+    written = sum(write.get(k, 0.0) for k in sel) * w_scale * 1024 / calls
+    tile_bytes = 210 * HQ * D * 2 * 2 + 2 * 210 * HKV * D * 2 + HQ * 210 * 4
+    lines = ["# HBM traffic of the small-tile forward: the 13440 x 13440 share in 210 x 210 tiles (counters)", "",
+             "Workload: 4096 non-causal tiles of 210 x 210 tokens (32/8 heads, d = 128, bf16), one",
+             "mesh_attn_tile_fwd call; every tile runs the resident-KV kernel (launches of 30 tiles).",
+             "Two rocprofv3 runs of the same command, one counter each (KiB per dispatch):", "",
+             "    " + command.replace("PMC", "FETCH_SIZE"), "    " + command.replace("PMC", "WRITE_SIZE"), "",
+             f"Calibration: the plain device copy of {copy_mib} MiB gives the factors {f_scale:.4f} (fetch) and "
+             f"{w_scale:.4f} (write).", "",
+             f"Resident-kernel dispatches: {len(sel)} over {calls} calls. Per call: {read / 1e9:.3f} GB read, "
+             f"{written / 1e9:.3f} GB written ({(read + written) / 1e9:.3f} GB), against "
+             f"{4096 * tile_bytes / 1e9:.3f} GB of compulsory bytes (each tile's Q, K, V read once, O and LSE written "
+             "once): tiles that share a Q or KV partition are served from the caches.", "",
+             "Traffic that bench.py reports for this workload while the kernel sources are unchanged:", "",
+             f"    fwd_p210_bytes_per_call: {int(round(read + written))}",
+             f"    source_sha256: {kernel_source_hash()}", ""]
+    with open(SMALL_TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {SMALL_TRAFFIC_FILE}: {(read + written) / 1e9:.3f} GB per call")
 
 
 def summarize_pmc(fetch_csv, write_csv, copy_mib, command):
     """Write the HBM-traffic summary of the headline's tile backward from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
     the plain device copy of copy_mib MiB made by --calib-copy-mb."""
-    import csv
     import collections
 
-    def per_dispatch(path):
-        by = collections.OrderedDict()
-        for r in csv.DictReader(open(path)):
-            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
-            by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
-        return by
-
-    fetch, write = per_dispatch(fetch_csv), per_dispatch(write_csv)
+    fetch, write = _pmc_per_dispatch(fetch_csv), _pmc_per_dispatch(write_csv)
 
     def by_kernel(d):
         agg = collections.OrderedDict()
@@ -550,14 +587,6 @@ def headline(args, dev, scale):
                 pk = PEAK_BF16_TFLOPS * pw["gfx_mhz_median"] / 2400.0
                 pw["bf16_peak_at_held_clock_tflops"] = round(pk, 1)
                 pw["frac_of_peak_at_held_clock"] = round(parts[name]["TFLOP/s"] / pk, 4)
-    if args.calib_copy_mb > 0:
-        n = args.calib_copy_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     return value, ms_step, parts, rl, power
 
 
@@ -874,7 +903,8 @@ def config_small(args, dev, scale):
         r[f"fwd_P{P}"] = e
     small = r["fwd_P210"]
     r["roofline"] = {"bound": "hbm", "achieved": small["hbm_GB/s_of_compulsory_bytes"], "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": small["frac_hbm_peak"], "traffic": None,
+                     "unit": "GB/s", "frac": small["frac_hbm_peak"],
+                     "traffic": stored_traffic(SMALL_TRAFFIC_FILE, "fwd_p210_bytes_per_call"),
                      "kernel": "the forward at P = 210 (4096 tiles, one call; 168 FLOP per compulsory byte, below "
                                "the chip's balance of about 315)"}
     return r
@@ -883,6 +913,10 @@ def config_small(args, dev, scale):
 # --------------------------------------------------------------------- main --
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc-small":
+        # bench.py --summarize-pmc-small FETCH_CSV WRITE_CSV COPY_MIB CALLS "COMMAND (with PMC for the counter)"
+        summarize_pmc_small(sys.argv[2], sys.argv[3], int(sys.argv[4]), int(sys.argv[5]), sys.argv[6])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         # bench.py --summarize-pmc FETCH_CSV WRITE_CSV COPY_MIB "COMMAND (with PMC for the counter)"
         summarize_pmc(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5])
@@ -933,6 +967,15 @@ def main():
             blocks[name]["cpu_baseline"] = cpu_baseline(name, oracle_rows[name], np.float32(scale))
     if blocks:
         out["configs"] = blocks
+    if args.calib_copy_mb > 0:
+        # a plain device copy of known size, the reference for the HBM byte counters
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(out), flush=True)
 
 
