@@ -75,6 +75,87 @@ struct FwdCfg {
   static constexpr int STAGES = WAVES == 8 ? 5 : 2;
 };
 
+// ---- pieces of a 32-key step shared by the ring and resident-KV kernels ----
+// A wave owns 32 query rows (one per lane pair l, l^32); a 32-key half of a K/V block is one
+// 32 x 32 score tile S^T = K Q^T whose lane holds its query's 16 keys 16*(e/8) + 8*hl + e%8.
+
+// S^T of the half at LDS byte offset off (fragment addresses kaddr, query fragments qf)
+template <int KS>
+__device__ __forceinline__ void fwd_scores(const uint32_t (&kaddr)[KS], uint32_t off, const bf16x8 (&qf)[KS],
+                                           f32x16& s) {
+  s = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 kf = lds_read_b128(kaddr[ks] + off);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+  }
+}
+
+// keys after klast set to -inf (key0: the key index of the half's first element); branch-free
+__device__ __forceinline__ void fwd_mask_keys(f32x16& s, int key0, int hl, int klast) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int key = key0 + (e >> 3) * 16 + hl * 8 + (e & 7);
+    s[e] = key <= klast ? s[e] : -INFINITY;
+  }
+}
+
+// the row's max over the half, in log2 units (c2 = scale * log2(e))
+__device__ __forceinline__ float fwd_row_max(const f32x16& s, float c2) {
+  float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+  return xhalf_max(mx) * c2;
+}
+
+// Lazy rescale: the running max m2 is raised only when some row's new max mb2 exceeds it by more
+// than 8 (factor 256), which keeps the result exact while skipping most rescales.
+template <int NC>
+__device__ __forceinline__ void fwd_maybe_rescale(f32x16 (&oacc)[NC], float& m2, float& lsum, float mb2) {
+  if (__any(mb2 > m2 + 8.0f)) {
+    const float mn = fmaxf(m2, mb2);
+    const float alpha = (mn == -INFINITY || m2 == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m2 - mn);
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+    m2 = mn;
+  }
+}
+
+// P = exp2(S c2 - m2) of the half, added to the lane's row sum and packed to bf16 (the B
+// operand of O^T += V^T P^T)
+__device__ __forceinline__ void fwd_probs(const f32x16& sc, float c2, float m2, float& lsum, bf16x8 (&pf)[2]) {
+  const float mref = (m2 == -INFINITY) ? 0.0f : m2;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half * 8 + i], c2, -mref));
+      lsum += pv[i];
+    }
+    pf[half] = pack_bf16x8(pv);
+  }
+}
+
+// O^T += V^T P^T over the half whose first 16-key slice starts at LDS byte offset off (V^T
+// fragments read transposed; a slice is 16 rows of 2*D bytes)
+template <int D, int NC>
+__device__ __forceinline__ void fwd_pv(const uint32_t (&vaddr)[NC][2], uint32_t off, const bf16x8 (&pf)[2],
+                                       f32x16 (&oacc)[NC]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bf16x4 lo = lds_read_tr16(vaddr[c][0] + off + half * 16 * D * 2);
+      const bf16x4 hi = lds_read_tr16(vaddr[c][1] + off + half * 16 * D * 2);
+      oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(lo, hi), pf[half], oacc[c], 0, 0, 0);
+    }
+  }
+}
+
 // Epilogue of one wave's 32 query rows: normalise O^T by the row sum and store O (bf16) and
 // LSE (fp32, natural log), or fold them into the (O, LSE) the buffers hold (accumulate):
 // L = ln(e^lse_old + e^lse), O = e^(lse_old - L) O_old + e^(lse - L) O.  orow and lrow address
@@ -271,47 +352,14 @@ fwd_bf16_kernel(const FwdParams p) {
   const float c2 = p.scale_log2;
 
   // S^T of one 32-key half (kb2) of the block in stage st
-  auto s_half = [&](int st, int kb2, f32x16& s) {
-    const uint32_t off = st * kStageBytes + kb2 * 32 * D * 2;
-    s = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 kf = lds_read_b128(kaddr[ks] + off);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
-    }
-  };
-
-  // element mask of a 32-key half: key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8
-  auto mask_half = [&](int kb, int kb2, f32x16& s) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {  // branch-free select
-      const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-      s[e] = key <= klast ? s[e] : -INFINITY;
-    }
-  };
-
-  // mask (when the block is not whole for this wave) and row max of a half, in log2 units
+  auto s_half = [&](int st, int kb2, f32x16& s) { fwd_scores(kaddr, st * kStageBytes + kb2 * 32 * D * 2, qf, s); };
+  // mask (when the block is not whole for this wave) and row max of a half
   float mb2 = -INFINITY;
   auto half_max = [&](int kb, int kb2, f32x16& s) {
-    if (kb >= kfull_w) mask_half(kb, kb2, s);
-    float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
-    mb2 = xhalf_max(mx) * c2;
+    if (kb >= kfull_w) fwd_mask_keys(s, kb * kBN + kb2 * 32, hl, klast);
+    mb2 = fwd_row_max(s, c2);
   };
-  // raise the running max when a row's new max exceeds it by more than 8 (rare after the first step)
-  auto maybe_rescale = [&]() {
-    if (__any(mb2 > m2 + 8.0f)) {
-      const float mn = fmaxf(m2, mb2);
-      const float alpha = (mn == -INFINITY || m2 == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m2 - mn);
-      lsum *= alpha;
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
-      m2 = mn;
-    }
-  };
+  auto maybe_rescale = [&]() { fwd_maybe_rescale(oacc, m2, lsum, mb2); };
 
   // One pipeline step over a 32-key half (stage st, half kb2) whose scores are
   // in sc and whose max is already folded into m2: the exponentials while the
@@ -324,40 +372,17 @@ fwd_bf16_kernel(const FwdParams p) {
   // region the scheduler can interleave; a half past the last block then only
   // has its max forced to -inf.
   auto half_max_plain = [&](bool valid, f32x16& s) {
-    float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
-    const float m = xhalf_max(mx) * c2;
+    const float m = fwd_row_max(s, c2);
     mb2 = valid ? m : -INFINITY;
   };
 
   auto half_step = [&](auto may_mask, int st, int kb2, f32x16& sc, int nkb_, int nst, int nkb2, f32x16& sn) {
     // scheduler hint: LDS reads interleaved with the MFMAs (measured 0.5-1% faster at the 8k tile)
     __builtin_amdgcn_iglp_opt(0);
-    const float mref = (m2 == -INFINITY) ? 0.0f : m2;
     bf16x8 pf[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half * 8 + i], c2, -mref));
-        lsum += pv[i];
-      }
-      pf[half] = pack_bf16x8(pv);
-    }
+    fwd_probs(sc, c2, m2, lsum, pf);
     s_half(nst, nkb2, sn);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t off = st * kStageBytes + (kb2 * 2 + half) * 16 * D * 2;
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        const bf16x4 lo = lds_read_tr16(vaddr[c][0] + off);
-        const bf16x4 hi = lds_read_tr16(vaddr[c][1] + off);
-        const bf16x8 vf = concat_bf16x4(lo, hi);
-        oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[half], oacc[c], 0, 0, 0);
-      }
-    }
+    fwd_pv<D>(vaddr, st * kStageBytes + kb2 * 32 * D * 2, pf, oacc);
     if constexpr (decltype(may_mask)::value) half_max(nkb_, nkb2, sn);
     else half_max_plain(nkb_ < nkb, sn);
   };
@@ -565,45 +590,15 @@ fwd_bf16_resident_kernel(const FwdParams p) {
   f32x16 oacc[C::NC];
   float m2, lsum, mb2;  // running max (log2 units), the lane's share of the row sum, a half's max
   // S^T of 32-key half kb2 of block kb
-  auto s_half = [&](int kb, int kb2, f32x16& s) {
-    const uint32_t off = kb * kBlockBytes + kb2 * 32 * D * 2;
-    s = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 kf = lds_read_b128(kaddr[ks] + off);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
-    }
-  };
-  // mask (keys past the last one; key kb*64 + kb2*32 + 16*(e/8) + 8*hl + e%8) and row max of a
-  // half, in log2 units
+  auto s_half = [&](int kb, int kb2, f32x16& s) { fwd_scores(kaddr, kb * kBlockBytes + kb2 * 32 * D * 2, qf, s); };
+  // mask (keys past the last one) and row max of a half
   auto half_max = [&](int kb, int kb2, f32x16& s, auto may_mask) {
     if constexpr (decltype(may_mask)::value) {
-      if (kb >= kfull) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb * kBN + kb2 * 32 + (e >> 3) * 16 + hl * 8 + (e & 7);
-          s[e] = key <= klast ? s[e] : -INFINITY;
-        }
-      }
+      if (kb >= kfull) fwd_mask_keys(s, kb * kBN + kb2 * 32, hl, klast);
     }
-    float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
-    mb2 = xhalf_max(mx) * c2;
+    mb2 = fwd_row_max(s, c2);
   };
-  // raise the running max when a row's new max exceeds it by more than 8 (the ring kernel's rule)
-  auto maybe_rescale = [&]() {
-    if (__any(mb2 > m2 + 8.0f)) {
-      const float mn = fmaxf(m2, mb2);
-      const float alpha = (mn == -INFINITY || m2 == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m2 - mn);
-      lsum *= alpha;
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
-      m2 = mn;
-    }
-  };
+  auto maybe_rescale = [&]() { fwd_maybe_rescale(oacc, m2, lsum, mb2); };
   auto has_keys = [&](int kb, int kb2) { return kb * kBN + kb2 * 32 < sk; };
   // One step over half kb2 of block kb, whose scores are in sc and whose max is already folded
   // into m2: the exponentials while the score MFMAs of the next half (block nkb_, half nkb2) run,
@@ -616,29 +611,10 @@ fwd_bf16_resident_kernel(const FwdParams p) {
       return;
     }
     __builtin_amdgcn_iglp_opt(0);
-    const float mref = (m2 == -INFINITY) ? 0.0f : m2;
     bf16x8 pf[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[half * 8 + i], c2, -mref));
-        lsum += pv[i];
-      }
-      pf[half] = pack_bf16x8(pv);
-    }
+    fwd_probs(sc, c2, m2, lsum, pf);
     if (nxt) s_half(nkb_, nkb2, sn);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t off = kb * kBlockBytes + (kb2 * 2 + half) * 16 * D * 2;
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        const bf16x4 lo = lds_read_tr16(vaddr[c][0] + off);
-        const bf16x4 hi = lds_read_tr16(vaddr[c][1] + off);
-        oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(concat_bf16x4(lo, hi), pf[half], oacc[c], 0, 0, 0);
-      }
-    }
+    fwd_pv<D>(vaddr, kb * kBlockBytes + kb2 * 32 * D * 2, pf, oacc);
     if (nxt) half_max(nkb_, nkb2, sn, may_mask);
     else mb2 = -INFINITY;
   };
