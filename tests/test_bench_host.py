@@ -1,4 +1,5 @@
-"""Host-side pieces of bench.py: the amd-smi sample parser (socket power and XCD clocks)."""
+"""Host-side pieces of bench.py: the amd-smi sample parser (socket power and XCD clocks) and the
+HBM-traffic summaries made from rocprofv3 counter runs."""
 import json
 import os
 import subprocess
@@ -42,3 +43,50 @@ def test_smi_sample_missing_or_garbled_gives_none(monkeypatch):
     monkeypatch.setattr(subprocess, "run", lambda *a, **k: subprocess.CompletedProcess(a, 0, na, ""))
     assert bench._smi_sample() is None
 
+
+
+def _pmc_csv(path, rows):
+    """A rocprofv3 counter-collection CSV with the columns the summaries read."""
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for did, name, value in rows:
+            f.write(f'{did},"{name}",C,{value}\n')
+
+
+def test_backward_traffic_summary_scales_by_the_copy_and_averages_calls(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.md"))
+    copy = "__amd_rocclr_copyBuffer"
+    pre, dq, dkv = ("void ma::(anonymous namespace)::bwd_pre_kernel<128>(ma::BwdPreParams)",
+                    "void ma::(anonymous namespace)::bwd_dq_kernel<128, false>(ma::BwdParams)",
+                    "void ma::(anonymous namespace)::bwd_dkv_kernel<128, false>(ma::BwdParams)")
+    other = "void ma::(anonymous namespace)::merge_kernel<128, true, 8, 2>(ma::MergeParams)"
+    # a 1 MiB copy reads 512 KiB and writes 1024 KiB by the counters: factors 2 (fetch) and 1 (write)
+    fetch = [(1, copy, 512), (2, pre, 10), (3, dq, 100), (4, dkv, 200), (5, other, 7), (6, pre, 20), (7, dq, 300),
+             (8, dkv, 400)]
+    write = [(1, copy, 1024), (2, pre, 1), (3, dq, 2), (4, dkv, 3), (5, other, 7), (6, pre, 4), (7, dq, 5), (8, dkv, 6)]
+    _pmc_csv(tmp_path / "f.csv", fetch)
+    _pmc_csv(tmp_path / "w.csv", write)
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1, "rocprofv3 --pmc PMC -- cmd")
+    calls = [2 * (10 + 100 + 200) + (1 + 2 + 3), 2 * (20 + 300 + 400) + (4 + 5 + 6)]  # KiB
+    expect = round(sum(calls) / 2 * 1024)
+    assert bench.stored_traffic() == expect
+    text = (tmp_path / "traffic.md").read_text()
+    assert "rocprofv3 --pmc FETCH_SIZE -- cmd" in text and "rocprofv3 --pmc WRITE_SIZE -- cmd" in text
+    # a summary taken on other kernel sources is not reported
+    (tmp_path / "traffic.md").write_text(text.replace(bench.kernel_source_hash(), "0" * 64))
+    assert bench.stored_traffic() is None
+
+
+def test_small_tile_traffic_summary_counts_the_resident_kernel_per_call(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "SMALL_TRAFFIC_FILE", str(tmp_path / "small.md"))
+    copy = "__amd_rocclr_copyBuffer"
+    res = "void ma::(anonymous namespace)::fwd_bf16_resident_kernel<128>(ma::FwdParams)"
+    ring = "void ma::(anonymous namespace)::fwd_bf16_kernel<128, false, 4>(ma::FwdParams)"
+    fetch = [(1, ring, 999), (2, res, 30), (3, res, 50), (4, res, 70), (5, res, 90), (6, copy, 512)]
+    write = [(1, ring, 999), (2, res, 100), (3, res, 100), (4, res, 100), (5, res, 100), (6, copy, 1024)]
+    _pmc_csv(tmp_path / "f.csv", fetch)
+    _pmc_csv(tmp_path / "w.csv", write)
+    bench.summarize_pmc_small(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1, 2, "rocprofv3 --pmc PMC -- cmd")
+    expect = round((2 * (30 + 50 + 70 + 90) + 400) * 1024 / 2)
+    assert bench.stored_traffic(bench.SMALL_TRAFFIC_FILE, "fwd_p210_bytes_per_call") == expect
+    assert bench.stored_traffic(bench.SMALL_TRAFFIC_FILE, "no_such_key") is None
