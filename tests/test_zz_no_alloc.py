@@ -2,7 +2,8 @@
 with a caller workspace (mesh_attn_tile_bwd): the same kernels on the same inputs, so dQ, dK and dV
 must be bitwise equal.  Two calls in a row share the built-in scratch, the second with a smaller
 input (its LSE/D slices land where the first call's were), and the smaller call is checked against
-its own reference too; the first call also goes through the fp64 oracle."""
+its own reference too; the first call also goes through the fp64 oracle.  A HIP graph captures the
+entry point and replays it."""
 import math
 
 import numpy as np
@@ -88,3 +89,29 @@ def test_noalloc_backward_matches_workspace_backward_twice():
         dv_ref = dv_ref + dv_r
     check_grad("dK", new1[2], dk_ref)
     check_grad("dV", new1[3], dv_ref)
+
+
+def test_noalloc_backward_replays_under_graph_capture():
+    """The caller the entry point is for: a HIP graph captures the no-allocation backward once (no
+    allocation, no memset node) and replays it three times, with eager work and synchronisation
+    between the replays; every replay must equal the eager call bitwise."""
+    qps = [Pos([(0, 900, 1)])]
+    kp = Pos([(0, 0, 1)])
+    log("[no-alloc bwd] graph capture: 700 rows vs 900 keys, causal, 8/2 heads, d=128, 3 replays")
+    s, (ref, new), _ = _case(2902, 700, 900, 8, 2, 128, 1, ma.MA_MASK_CAUSAL, qps, kp)
+    ma.mesh_attn_tile_bwd_noalloc(ref[0], float(s), ma.MA_MASK_CAUSAL)
+    ma.mesh_attn_tile_bwd_noalloc(new[0], float(s), ma.MA_MASK_CAUSAL)  # warm-up before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ma.mesh_attn_tile_bwd_noalloc(new[0], float(s), ma.MA_MASK_CAUSAL)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in new[1] + [new[2], new[3]]:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same(f"replay {r} dQ", ref[1][0], new[1][0])
+        _same(f"replay {r} dK", ref[2], new[2])
+        _same(f"replay {r} dV", ref[3], new[3])
