@@ -231,14 +231,40 @@ KERNEL_SOURCES = ["bwd.hip", "fwd_bf16.hip", "merge.hip", "api.hip", "ma_device.
 BWD_KERNELS = ("bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkv_kernel")
 
 
+def strip_comments(src):
+    """C++ source without its comments (// to the end of the line, /* ... */), blank lines and trailing
+    blanks; string and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_hash():
-    """sha256 over the HIP sources the measured kernels are built from (changes invalidate stored counters)."""
+    """sha256 over the HIP sources the measured kernels are built from, comments left out (a change of
+    the code invalidates stored counters; a change of a comment does not)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "distributed_long_context_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

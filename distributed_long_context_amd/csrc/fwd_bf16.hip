@@ -47,6 +47,11 @@
 //    index of its last allowed key, a wave the count of leading blocks it sees
 //    whole and the workgroup the count of blocks with any allowed pair; no
 //    position data stays live in the loop.
+//  * Three instances: the ring kernel above with 8 waves (long tiles) or 4 waves
+//    and a two-stage ring (tiles of at most 16 key blocks, two workgroups per CU),
+//    and a resident-KV kernel for unmasked tiles of a few hundred keys, whose
+//    workgroup holds the tile's whole K and V in LDS and runs up to 32 units of
+//    32 query rows against it (see its own comment below).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <type_traits>

@@ -90,3 +90,12 @@ def test_small_tile_traffic_summary_counts_the_resident_kernel_per_call(tmp_path
     expect = round((2 * (30 + 50 + 70 + 90) + 400) * 1024 / 2)
     assert bench.stored_traffic(bench.SMALL_TRAFFIC_FILE, "fwd_p210_bytes_per_call") == expect
     assert bench.stored_traffic(bench.SMALL_TRAFFIC_FILE, "no_such_key") is None
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    src = ('int f(int a) {  // the sum\n  /* block\n comment */ return a + 1;\n}\n'
+           'const char* s = "not // a comment /* either */";\n')
+    assert bench.strip_comments(src) == ('int f(int a) {\n   return a + 1;\n}\n'
+                                         'const char* s = "not // a comment /* either */";')
+    assert bench.strip_comments(src.replace("the sum", "one more")) == bench.strip_comments(src)
+    assert bench.strip_comments(src.replace("a + 1", "a + 2")) != bench.strip_comments(src)
