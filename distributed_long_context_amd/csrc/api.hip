@@ -205,9 +205,9 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
                              [&](int i) { return a->tiles[i].sq; }, 4, "lse");
   if (rc) return rc;
   // Tiles go to one of five launch classes: by how much masking they need (bit 0) and, in
-  // bf16, by length (bit 1), or (class 4) the resident-KV kernel, which takes the unmasked
-  // bf16 tiles of kFwdResMinKeys < sk <= kFwdResKeys keys.  FULL tiles (and every tile without a mask) run the
-  // unmasked kernel, PARTIAL ones the masked kernel, whose key positions must be one
+  // bf16, by length (bit 1), or the resident-KV kernel (kResident), which takes the unmasked
+  // bf16 tiles of kFwdResMinKeys < sk <= kFwdResKeys keys.  FULL tiles (and every tile
+  // without a mask) run the unmasked kernel, PARTIAL ones the masked kernel, whose key positions must be one
   // segment: a tile whose key positions have several segments is cut into one piece
   // per segment (the keys of a segment are contiguous rows) and its pieces with any
   // allowed pair go to the masked kernel as a chain of consecutive entries, which one
@@ -223,11 +223,12 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   };
   std::vector<Planned> plan;
   std::vector<FwdParams> batches;
-  FwdParams bp[5];
-  int bn[5] = {0, 0, 0, 0, 0}, bwg[5] = {0, 0, 0, 0, 0};
-  for (int m = 0; m < 5; ++m) {
+  constexpr int kClasses = 5, kResident = 4;
+  FwdParams bp[kClasses];
+  int bn[kClasses] = {}, bwg[kClasses] = {};
+  for (int m = 0; m < kClasses; ++m) {
     bp[m] = p;
-    bp[m].mask = m & 1;
+    bp[m].mask = m != kResident && (m & 1);
   }
   auto flush = [&](int m) {
     if (bn[m] == 0) return;
@@ -238,13 +239,13 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     bwg[m] = 0;
   };
   auto flush_all = [&]() {
-    for (int m = 0; m < 5; ++m) flush(m);
+    for (int m = 0; m < kClasses; ++m) flush(m);
   };
   // queue one tile (or the pieces of one, as a chain): cls is the class of the tile (any
   // chain runs masked), acc its accumulate flag, pieces the key segments after the first
   auto enqueue_chain = [&](const ma_tile* pcs, int npcs, int cls, int acc) -> int {
     bool dup = false;
-    for (int k = 0; k < 5; ++k)
+    for (int k = 0; k < kClasses; ++k)
       for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == pcs[0].o || bp[k].tiles[j].lse == pcs[0].lse;
     if (dup) flush_all();
     int64_t blocks = 0;
@@ -254,7 +255,7 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     const int64_t res_lo = a->head_dim == 128 ? kFwdResMinKeys<128> : kFwdResMinKeys<64>;
     const int64_t res_hi = a->head_dim == 128 ? kFwdResKeys<128> : kFwdResKeys<64>;
     const bool resident = bf16 && whole && pcs[0].sk > res_lo && pcs[0].sk <= res_hi;
-    const int m = resident ? 4 : (whole ? 0 : 1) | (small ? 2 : 0);
+    const int m = resident ? kResident : (whole ? 0 : 1) | (small ? 2 : 0);
     const ma_tile& t = pcs[0];
     int64_t wgs, chunks;
     if (bf16) {
@@ -358,9 +359,9 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss, p.o_sh,
                             p.l_sb, p.l_sh, stream);
     } else {
-      e = pl.m == 4 ? launch_fwd_bf16_resident(batches[pl.idx], a->head_dim, pl.wgs, stream)
-          : bf16    ? launch_fwd_bf16(batches[pl.idx], a->head_dim, pl.m & 2 ? 4 : 8, pl.wgs, stream)
-               : launch_fwd_f32(batches[pl.idx], a->head_dim, pl.wgs, stream);
+      if (pl.m == kResident) e = launch_fwd_bf16_resident(batches[pl.idx], a->head_dim, pl.wgs, stream);
+      else if (bf16) e = launch_fwd_bf16(batches[pl.idx], a->head_dim, pl.m & 2 ? 4 : 8, pl.wgs, stream);
+      else e = launch_fwd_f32(batches[pl.idx], a->head_dim, pl.wgs, stream);
     }
     rc = check_hip(e, pl.m < 0 ? "fill launch" : "tile_fwd launch");
     if (rc) return rc;
