@@ -131,7 +131,8 @@ def test_zigzag_diagonal_mask_probe_full_size():
 
 def test_mesh_8x8_1m_forward_and_merge():
     # One GPU (g = 9) of n = 64 at S = 1,048,576: partitions of 16384 tokens, 8 x 8 tile with KV rotation,
-    # non-causal; 8-way merges per Q partition plus 7 incoming seeded partials for the owned partition.
+    # non-causal; 8-way merges per Q partition plus 7 incoming seeded partials for the owned partition; the
+    # fused forward over the gathered KV and the GOO replay of 4 x 4 chunk tasks on the same inputs.
     wid, n, a, b, g, P = 4, 64, 8, 8, 9, 16384
     log("[workload mesh-8x8-1m]")
     qparts, kparts = ma.mesh_attn_map_mesh_tile(n, a, b, g, True)
@@ -170,12 +171,34 @@ def test_mesh_8x8_1m_forward_and_merge():
                           ma.MA_MASK_NONE)
     ma.mesh_attn_merge([fused[g][0]] + [x[0] for x in inc], [fused[g][1]] + [x[2] for x in inc],
                        fused[g][0], fused[g][1])
+    # the GOO replay the bench times ([Mesh] section 3.4): k_Q = k_KV = 4 chunks per partition, chunk c of
+    # every Q (KV) partition gathered into one buffer, the compute tasks C-i-j of the greedy plan in its
+    # order, each folded into its Q chunk's (O, LSE) (the first task of a chunk overwrites)
+    kq = kkv = 4
+    cq, ck = P // kq, P // kkv
+    gq = [torch.cat([Q[i][0][:, c * cq:(c + 1) * cq] for i in qparts], dim=1) for c in range(kq)]
+    gk = [torch.cat([K[j][0][:, c * ck:(c + 1) * ck] for j in kparts], dim=1) for c in range(kkv)]
+    gv = [torch.cat([V[j][0][:, c * ck:(c + 1) * ck] for j in kparts], dim=1) for c in range(kkv)]
+    acc = [empty_out(a * cq) for _ in range(kq)]
+    order = [(ci, cj) for _, comp in ma.mesh_attn_goo_plan(kq, kkv, 0.5, 1.0, 0.5, 0.5, 1.0) for _, ci, cj in comp]
+    assert sorted(order) == [(ci, cj) for ci in range(kq) for cj in range(kkv)]
+    started = set()
+    for ci, cj in order:
+        ma.mesh_attn_tile_fwd([Tile(gq[ci], gk[cj], gv[cj], acc[ci][0], acc[ci][1])], float(SCALE),
+                              ma.MA_MASK_NONE, accumulate=ci in started)
+        started.add(ci)
     torch.cuda.synchronize()
     kall = np.concatenate([K[j][1] for j in kparts], axis=1)
     vall = np.concatenate([V[j][1] for j in kparts], axis=1)
-    for i in qparts:
+    for r, i in enumerate(qparts):
         rows = sample_rows(P, wid + i, extra=6 if i != g else 16)
         Oloc, Lloc = attn_tile(Q[i][1], kall, vall, SCALE, rows=rows)
+        # row t of Q partition i is row r*cq + t%cq of gathered chunk t//cq
+        where = [(int(t) // cq, r * cq + int(t) % cq) for t in rows]
+        got_o = np.concatenate([host_f64(acc[c][0][:, at:at + 1]) for c, at in where], axis=1)
+        got_l = np.concatenate([host_f64(acc[c][1][:, :, at:at + 1]) for c, at in where], axis=2)
+        check_close(f"GOO replay O Q{i}", got_o, Oloc, BF16_O_TOL)
+        check_close(f"GOO replay LSE Q{i}", got_l, Lloc, BF16_LSE_TOL)
         if i == g:
             Oref, Lref = merge([(Oloc, Lloc)] + [(x[1][:, rows], x[3][:, :, rows]) for x in inc])
         else:
