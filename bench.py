@@ -304,20 +304,21 @@ def _pmc_per_dispatch(path):
 
 def summarize_pmc_small(fetch_csv, write_csv, copy_mib, calls, command):
     """Write the HBM-traffic summary of the 210-token small-tile forward (every dispatch of the
-    resident-KV kernel in the run belongs to its `calls` calls) from two rocprofv3 --pmc runs,
-    scaled like summarize_pmc by the plain device copy of copy_mib MiB."""
+    tile-table instance of the resident-KV kernel in the run belongs to its `calls` calls) from two
+    rocprofv3 --pmc runs, scaled like summarize_pmc by the plain device copy of copy_mib MiB."""
     fetch, write = _pmc_per_dispatch(fetch_csv), _pmc_per_dispatch(write_csv)
     copy_kib = copy_mib * 1024.0
     cf = [v for (_, n), v in fetch.items() if "copyBuffer" in n]
     cw = [v for (_, n), v in write.items() if "copyBuffer" in n]
     f_scale, w_scale = copy_kib / (sum(cf) / len(cf)), copy_kib / (sum(cw) / len(cw))
-    sel = [k for k in fetch if "fwd_bf16_resident_kernel" in k[1]]
+    sel = [k for k in fetch if "fwd_bf16_resident_kernel<128, true>" in k[1]]  # the tile-table launches
     read = sum(fetch[k] for k in sel) * f_scale * 1024 / calls
     written = sum(write.get(k, 0.0) for k in sel) * w_scale * 1024 / calls
     tile_bytes = 210 * HQ * D * 2 * 2 + 2 * 210 * HKV * D * 2 + HQ * 210 * 4
     lines = ["# HBM traffic of the small-tile forward: the 13440 x 13440 share in 210 x 210 tiles (counters)", "",
              "Workload: 4096 non-causal tiles of 210 x 210 tokens (32/8 heads, d = 128, bf16), one",
-             "mesh_attn_tile_fwd call; every tile runs the resident-KV kernel (launches of 30 tiles).",
+             "mesh_attn_tile_fwd_tabled call: every tile runs the resident-KV kernel in one launch from the",
+             "tile table (the bench also times the call through mesh_attn_tile_fwd; those launches are not counted).",
              "Two rocprofv3 runs of the same command, one counter each (KiB per dispatch):", "",
              "    " + command.replace("PMC", "FETCH_SIZE"), "    " + command.replace("PMC", "WRITE_SIZE"), "",
              f"Calibration: the plain device copy of {copy_mib} MiB gives the factors {f_scale:.4f} (fetch) and "
@@ -896,8 +897,9 @@ def config_striped(args, dev, scale):
 
 def config_small(args, dev, scale):
     """A 13440 x 13440 share (32/8 heads, d = 128, non-causal) cut into (13440/P)^2 tiles of P x P
-    tokens, all in one forward call, for the partition sizes of [CHARM+]'s scaling table.  Small
-    tiles are bound by HBM: compulsory bytes per tile = Q, K, V read once + O, LSE written once."""
+    tokens, all in one forward call (mesh_attn_tile_fwd_tabled: the resident-KV tiles from a tile
+    table in device memory), for the partition sizes of [CHARM+]'s scaling table.  Compulsory bytes
+    per tile = Q, K, V read once + O, LSE written once."""
     import torch
     import distributed_long_context_amd as ma
     from distributed_long_context_amd import Tile
@@ -919,8 +921,13 @@ def config_small(args, dev, scale):
                 lse = l_all[part * HQ * P:(part + 1) * HQ * P].view(1, HQ, P)
                 tiles.append(Tile(q[:, i * P:(i + 1) * P], k[:, j * P:(j + 1) * P], v[:, j * P:(j + 1) * P], o, lse))
         flop = 4.0 * D * HQ * S * S
-        prep = ma.prepare_tile_fwd(tiles, scale, ma.MA_MASK_NONE)  # argument packing outside the timing
+        # argument packing (and the tile table's upload) outside the timing
+        prep = ma.prepare_tile_fwd(tiles, scale, ma.MA_MASK_NONE, table=True)
         e = timed_tf(flop, lambda: ma.launch_prepared_tile_fwd(prep), reps_of(20, args), 3)
+        if P == 210:  # the same call through mesh_attn_tile_fwd (tiles in kernel arguments, 30 a launch)
+            prep_ka = ma.prepare_tile_fwd(tiles, scale, ma.MA_MASK_NONE)
+            r["fwd_P210_kernel_arguments"] = timed_tf(flop, lambda: ma.launch_prepared_tile_fwd(prep_ka),
+                                                      reps_of(20, args), 3)
         tile_bytes = P * HQ * D * 2 * 2 + 2 * P * HKV * D * 2 + HQ * P * 4
         g = n * n * tile_bytes / (e["ms"] * 1e-3) / 1e9
         e.update({"tiles": n * n, "compulsory_bytes": n * n * tile_bytes, "hbm_GB/s_of_compulsory_bytes": round(g, 1),
@@ -931,8 +938,9 @@ def config_small(args, dev, scale):
     r["roofline"] = {"bound": "hbm", "achieved": small["hbm_GB/s_of_compulsory_bytes"], "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": small["frac_hbm_peak"],
                      "traffic": stored_traffic(SMALL_TRAFFIC_FILE, "fwd_p210_bytes_per_call"),
-                     "kernel": "the forward at P = 210 (4096 tiles, one call; 168 FLOP per compulsory byte, below "
-                               "the chip's balance of about 315)"}
+                     "kernel": "the forward at P = 210 (4096 tiles, one mesh_attn_tile_fwd_tabled call: one "
+                               "resident-KV launch; 168 FLOP per compulsory byte, below the chip's balance of about "
+                               "315)"}
     return r
 
 

@@ -107,18 +107,22 @@ class Tile:
 
 
 def mesh_attn_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
-                       stream=None, accumulate: bool = False) -> None:
+                       stream=None, accumulate: bool = False, table: bool = False) -> None:
     """Partial (O, LSE) of every tile, enqueued on `stream` (default: current stream).
-    With accumulate=True each tile's result is folded into the (O, LSE) its buffers hold."""
-    prepared = prepare_tile_fwd(tiles, scale, mask_mode, head_map, accumulate)
+    With accumulate=True each tile's result is folded into the (O, LSE) its buffers hold.
+    With table=True the call goes through mesh_attn_tile_fwd_tabled (the same results; the tile
+    table is packed on the host, copied to the device on `stream` and launched from there)."""
+    prepared = prepare_tile_fwd(tiles, scale, mask_mode, head_map, accumulate, table=table, stream=stream)
     if prepared is not None:
         launch_prepared_tile_fwd(prepared, stream)
 
 
 def prepare_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
-                     accumulate: bool = False):
+                     accumulate: bool = False, table: bool = False, stream=None):
     """The checked argument block of mesh_attn_tile_fwd, to be launched (possibly many times) by
-    launch_prepared_tile_fwd; it holds the tensors' addresses, so keep the tensors alive."""
+    launch_prepared_tile_fwd; it holds the tensors' addresses, so keep the tensors alive.
+    With table=True the tile table is packed into pinned host memory and copied to the device on
+    `stream` (default: current stream) here, once, for every launch of the prepared call."""
     tiles = list(tiles)
     if not tiles:
         return None
@@ -160,12 +164,28 @@ def prepare_tile_fwd(tiles: Sequence[Tile], scale: float, mask_mode: int = MA_MA
     a.v_stride[:] = _bshd_strides(t0.v, "v")
     a.o_stride[:] = _bshd_strides(t0.o, "o")
     a.lse_stride[:] = (t0.lse.stride(0), t0.lse.stride(1))
-    return (a, arr, hm_keep)
+    if not table:
+        return (a, arr, hm_keep, None)
+    torch = _torch()
+    nbytes = lib().mesh_attn_tile_fwd_table_bytes(C.byref(a))
+    if nbytes == 0:
+        _abi.check(_abi.MA_ERR_INVALID, "mesh_attn_tile_fwd_table_bytes")
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    _abi.check(lib().mesh_attn_tile_fwd_pack(C.byref(a), C.c_void_p(host.data_ptr()), nbytes), "mesh_attn_tile_fwd_pack")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    with torch.cuda.stream(s):
+        dev = host.to(t0.q.device, non_blocking=True)
+    return (a, arr, hm_keep, (host, dev, nbytes))
 
 
 def launch_prepared_tile_fwd(prepared, stream=None) -> None:
     """Enqueue a forward prepared by prepare_tile_fwd (the C call only)."""
-    _abi.check(lib().mesh_attn_tile_fwd(C.byref(prepared[0]), _stream_ptr(stream)), "mesh_attn_tile_fwd")
+    if prepared[3] is None:
+        _abi.check(lib().mesh_attn_tile_fwd(C.byref(prepared[0]), _stream_ptr(stream)), "mesh_attn_tile_fwd")
+        return
+    _, dev, nbytes = prepared[3]
+    _abi.check(lib().mesh_attn_tile_fwd_tabled(C.byref(prepared[0]), C.c_void_p(dev.data_ptr()), nbytes,
+                                               _stream_ptr(stream)), "mesh_attn_tile_fwd_tabled")
 
 
 # ------------------------------------------------------------------ merge --

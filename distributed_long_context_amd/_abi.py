@@ -75,6 +75,9 @@ class ma_tile_bwd_args(C.Structure):
 # exported symbol -> (restype, argtypes)
 SIGNATURES = {
     "mesh_attn_tile_fwd": (I32, [C.POINTER(ma_tile_fwd_args), VP]),
+    "mesh_attn_tile_fwd_table_bytes": (C.c_size_t, [C.POINTER(ma_tile_fwd_args)]),
+    "mesh_attn_tile_fwd_pack": (I32, [C.POINTER(ma_tile_fwd_args), VP, C.c_size_t]),
+    "mesh_attn_tile_fwd_tabled": (I32, [C.POINTER(ma_tile_fwd_args), VP, C.c_size_t, VP]),
     "mesh_attn_merge": (I32, [C.POINTER(ma_merge_args), VP]),
     "mesh_attn_reduce_add": (I32, [C.POINTER(ma_reduce_args), VP]),
     "mesh_attn_goo_plan": (I32, [I32, I32, C.c_double, C.c_double, C.c_double, C.POINTER(C.c_double), C.c_double,

@@ -141,17 +141,40 @@ int check_shifted_outputs(int n, PtrOf ptr_of, RowsOf rows_of, int64_t row_bytes
   return MA_OK;
 }
 
-}  // namespace
-}  // namespace ma
+// One forward call, planned before anything is enqueued: its launches in order (a launch class
+// with its kernel parameters, or the (0, -inf) fill of an EMPTY tile) and, when the resident-KV
+// tiles go through a tile table in device memory, that table (tiles and workgroup map).
+constexpr int kClasses = 5, kResident = 4;
+struct FwdPlan {
+  struct Launch {
+    int m;    // launch class; -1: fill an EMPTY tile's output with (0, -inf)
+    int wgs;  // workgroups of the launch
+    int idx;  // class launches: index into batches; fills: the tile's index
+  };
+  FwdParams p;
+  std::vector<Launch> launches;
+  std::vector<FwdParams> batches;
+  std::vector<FwdTile> table;
+  std::vector<int32_t> wg_map;
+};
 
-using namespace ma;
+// FNV-1a (64-bit) over the table's tiles and map
+uint64_t table_hash(const FwdPlan& plan) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](const void* data, size_t n) {
+    const unsigned char* b = (const unsigned char*)data;
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 1099511628211ull;
+  };
+  if (!plan.table.empty()) mix(plan.table.data(), plan.table.size() * sizeof(FwdTile));
+  if (!plan.wg_map.empty()) mix(plan.wg_map.data(), plan.wg_map.size() * sizeof(int32_t));
+  return h;
+}
 
-extern "C" {
+size_t table_bytes(const FwdPlan& plan) {
+  return sizeof(FwdTableHeader) + plan.table.size() * sizeof(FwdTile) + plan.wg_map.size() * sizeof(int32_t);
+}
 
-const char* mesh_attn_last_error(void) { return g_last_error.c_str(); }
-int mesh_attn_version(void) { return MA_VERSION; }
-
-int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
+int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
   if (!a) return set_error(MA_ERR_INVALID, "null args");
   int rc = check_common(a->dtype, a->batch, a->hq, a->hkv, a->head_dim, a->mask_mode, a->scale);
   if (rc) return rc;
@@ -167,7 +190,7 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   if (a->dtype == MA_BF16 && (a->k_stride[1] >= (1 << 24) || a->v_stride[1] >= (1 << 24)))
     return set_error(MA_ERR_UNSUPPORTED, "K/V sequence strides must be below 2^24 elements");
 
-  FwdParams p;
+  FwdParams& p = plan.p;
   std::memset(&p, 0, sizeof(p));
   const char* why = nullptr;
   p.gmax = build_head_groups(a->hq, a->hkv, a->head_map, p.heads_of, p.kv_first, &why);
@@ -207,8 +230,8 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   // Tiles go to one of five launch classes: by how much masking they need (bit 0) and, in
   // bf16, by length (bit 1), or the resident-KV kernel (kResident), which takes the unmasked
   // bf16 tiles of kFwdResMinKeys < sk <= kFwdResKeys keys.  FULL tiles (and every tile
-  // without a mask) run the unmasked kernel, PARTIAL ones the masked kernel, whose key positions must be one
-  // segment: a tile whose key positions have several segments is cut into one piece
+  // without a mask) run the unmasked kernel, PARTIAL ones the masked kernel, whose key
+  // positions must be one segment: a tile whose key positions have several segments is cut into one piece
   // per segment (the keys of a segment are contiguous rows) and its pieces with any
   // allowed pair go to the masked kernel as a chain of consecutive entries, which one
   // workgroup runs in turn with the softmax state in registers, so the output is
@@ -216,24 +239,26 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   // four-wave kernel.  A tile naming the output of one already queued waits for it.
   // The whole call is planned first and launched afterwards, so an argument error
   // found on any tile leaves nothing enqueued.
-  struct Planned {
-    int m;    // launch class; -1: fill an EMPTY tile's output with (0, -inf)
-    int wgs;  // workgroups of the launch
-    int idx;  // class launches: index into batches; fills: the tile's index
-  };
-  std::vector<Planned> plan;
-  std::vector<FwdParams> batches;
-  constexpr int kClasses = 5, kResident = 4;
+  // With a table (use_table), the resident-KV tiles go to plan.table instead: no limit of tiles
+  // per launch; a launch is a span of the table's workgroup map, cut where a tile names an output
+  // already queued.
+  std::vector<FwdPlan::Launch>& launches = plan.launches;
+  std::vector<FwdParams>& batches = plan.batches;
   FwdParams bp[kClasses];
   int bn[kClasses] = {}, bwg[kClasses] = {};
   for (int m = 0; m < kClasses; ++m) {
     bp[m] = p;
     bp[m].mask = m != kResident && (m & 1);
   }
+  size_t tab_first = 0;  // first table tile of the resident span being filled
   auto flush = [&](int m) {
     if (bn[m] == 0) return;
     bp[m].ntiles = bn[m];
-    plan.push_back(Planned{m, bwg[m], (int)batches.size()});
+    if (use_table && m == kResident) {
+      bp[m].wg_base = bwg[m] == 0 ? 0 : (int32_t)plan.wg_map.size() - bwg[m];
+      tab_first = plan.table.size();
+    }
+    launches.push_back(FwdPlan::Launch{m, bwg[m], (int)batches.size()});
     batches.push_back(bp[m]);
     bn[m] = 0;
     bwg[m] = 0;
@@ -246,7 +271,10 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
   auto enqueue_chain = [&](const ma_tile* pcs, int npcs, int cls, int acc) -> int {
     bool dup = false;
     for (int k = 0; k < kClasses; ++k)
-      for (int j = 0; j < bn[k]; ++j) dup = dup || bp[k].tiles[j].o == pcs[0].o || bp[k].tiles[j].lse == pcs[0].lse;
+      for (int j = 0; j < bn[k] && !(use_table && k == kResident); ++j)
+        dup = dup || bp[k].tiles[j].o == pcs[0].o || bp[k].tiles[j].lse == pcs[0].lse;
+    for (size_t j = tab_first; j < plan.table.size(); ++j)
+      dup = dup || plan.table[j].o == pcs[0].o || plan.table[j].lse == pcs[0].lse;
     if (dup) flush_all();
     int64_t blocks = 0;
     for (int i = 0; i < npcs; ++i) blocks += (pcs[i].sk + 63) / 64;
@@ -273,8 +301,12 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
     }
     if (wgs >= INT32_MAX) return set_error(MA_ERR_INVALID, "tile too large for one launch");
     // a chain stays in one launch, and a launch's workgroup count stays below 2^31
-    if (bn[m] + npcs > kFwdTilesPerLaunch || bwg[m] + wgs >= INT32_MAX) flush(m);
-    FwdTile& ft = bp[m].tiles[bn[m]];
+    const bool tabled = use_table && m == kResident;
+    if (tabled && (int64_t)plan.wg_map.size() + wgs >= INT32_MAX)
+      return set_error(MA_ERR_INVALID, "the tile table's workgroups must stay below 2^31");
+    if ((!tabled && bn[m] + npcs > kFwdTilesPerLaunch) || bwg[m] + wgs >= INT32_MAX) flush(m);
+    FwdTile scratch_tile;
+    FwdTile& ft = tabled ? scratch_tile : bp[m].tiles[bn[m]];
     std::memset(&ft, 0, sizeof(ft));
     ft.q = t.q; ft.k = t.k; ft.v = t.v; ft.o = t.o; ft.lse = t.lse;
     ft.sq = (int32_t)t.sq;
@@ -287,6 +319,14 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       ft.kst = (int32_t)t.k_pos.seg[0].stride;
     } else {
       ft.qp.nseg = 1;
+    }
+    if (tabled) {  // one tile entry in the table and one map entry per workgroup
+      ft.wg_begin = (int32_t)plan.wg_map.size();
+      plan.wg_map.insert(plan.wg_map.end(), (size_t)wgs, (int32_t)plan.table.size());
+      plan.table.push_back(ft);
+      bwg[m] += (int)wgs;
+      ++bn[m];
+      return MA_OK;  // resident tiles have no chained pieces
     }
     ft.wg_begin = bwg[m];
     bwg[m] += (int)wgs;
@@ -347,26 +387,97 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
       }
     } else if (a->accumulate == 0) {  // no piece had an allowed pair: the tile's result is (0, -inf)
       flush_all();  // a queued tile may name the same output
-      plan.push_back(Planned{-1, 0, i});
+      launches.push_back(FwdPlan::Launch{-1, 0, i});
     }
   }
   flush_all();
-  // launch the plan in order
-  for (const Planned& pl : plan) {
+  return MA_OK;
+}
+
+// Enqueues a planned forward; dev_table: the device copy of the plan's tile table (with one).
+int launch_fwd_plan(const ma_tile_fwd_args* a, FwdPlan& plan, const void* dev_table, void* stream) {
+  const FwdParams& p = plan.p;
+  const bool bf16 = a->dtype == MA_BF16;
+  const uint64_t hash = dev_table ? table_hash(plan) : 0;
+  for (const FwdPlan::Launch& pl : plan.launches) {
     int e;
     if (pl.m < 0) {
       const ma_tile& t = a->tiles[pl.idx];
       e = launch_fill_empty(t.o, t.lse, a->dtype, a->batch, (int)t.sq, a->hq, a->head_dim, p.o_sb, p.o_ss, p.o_sh,
                             p.l_sb, p.l_sh, stream);
+    } else if (pl.m == kResident) {
+      FwdParams& rp = plan.batches[pl.idx];
+      if (dev_table) {
+        rp.table_header = (const FwdTableHeader*)dev_table;
+        rp.table = (const FwdTile*)byte_offset(dev_table, sizeof(FwdTableHeader));
+        rp.wg_map = (const int32_t*)byte_offset(dev_table, sizeof(FwdTableHeader) + plan.table.size() * sizeof(FwdTile));
+        rp.table_ntiles = (int32_t)plan.table.size();
+        rp.table_nwgs = (int32_t)plan.wg_map.size();
+        rp.table_hash = hash;
+      }
+      e = launch_fwd_bf16_resident(rp, a->head_dim, pl.wgs, stream);
+    } else if (bf16) {
+      e = launch_fwd_bf16(plan.batches[pl.idx], a->head_dim, pl.m & 2 ? 4 : 8, pl.wgs, stream);
     } else {
-      if (pl.m == kResident) e = launch_fwd_bf16_resident(batches[pl.idx], a->head_dim, pl.wgs, stream);
-      else if (bf16) e = launch_fwd_bf16(batches[pl.idx], a->head_dim, pl.m & 2 ? 4 : 8, pl.wgs, stream);
-      else e = launch_fwd_f32(batches[pl.idx], a->head_dim, pl.wgs, stream);
+      e = launch_fwd_f32(plan.batches[pl.idx], a->head_dim, pl.wgs, stream);
     }
-    rc = check_hip(e, pl.m < 0 ? "fill launch" : "tile_fwd launch");
+    const int rc = check_hip(e, pl.m < 0 ? "fill launch" : "tile_fwd launch");
     if (rc) return rc;
   }
   return MA_OK;
+}
+
+}  // namespace
+}  // namespace ma
+
+using namespace ma;
+
+extern "C" {
+
+const char* mesh_attn_last_error(void) { return g_last_error.c_str(); }
+int mesh_attn_version(void) { return MA_VERSION; }
+
+int mesh_attn_tile_fwd(const ma_tile_fwd_args* a, void* stream) {
+  FwdPlan plan;
+  const int rc = plan_fwd(a, false, plan);
+  if (rc || !a->ntiles) return rc;
+  return launch_fwd_plan(a, plan, nullptr, stream);
+}
+
+size_t mesh_attn_tile_fwd_table_bytes(const ma_tile_fwd_args* a) {
+  FwdPlan plan;
+  if (plan_fwd(a, true, plan)) return 0;
+  return table_bytes(plan);
+}
+
+int mesh_attn_tile_fwd_pack(const ma_tile_fwd_args* a, void* table, size_t bytes) {
+  FwdPlan plan;
+  const int rc = plan_fwd(a, true, plan);
+  if (rc) return rc;
+  const size_t need = table_bytes(plan);
+  if (!table || bytes < need) return set_error(MA_ERR_INVALID, "table missing or smaller than mesh_attn_tile_fwd_table_bytes");
+  FwdTableHeader h;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = kFwdTableMagic;
+  h.ntiles = (int32_t)plan.table.size();
+  h.nwgs = (int32_t)plan.wg_map.size();
+  h.hash = table_hash(plan);
+  unsigned char* out = (unsigned char*)table;
+  std::memcpy(out, &h, sizeof(h));
+  if (!plan.table.empty()) std::memcpy(out + sizeof(h), plan.table.data(), plan.table.size() * sizeof(FwdTile));
+  if (!plan.wg_map.empty())
+    std::memcpy(out + sizeof(h) + plan.table.size() * sizeof(FwdTile), plan.wg_map.data(),
+                plan.wg_map.size() * sizeof(int32_t));
+  return MA_OK;
+}
+
+int mesh_attn_tile_fwd_tabled(const ma_tile_fwd_args* a, const void* table, size_t bytes, void* stream) {
+  FwdPlan plan;
+  const int rc = plan_fwd(a, true, plan);
+  if (rc || !a->ntiles) return rc;
+  if (!table || !aligned16(table) || bytes < table_bytes(plan))
+    return set_error(MA_ERR_INVALID, "device table missing, not 16-byte aligned or smaller than mesh_attn_tile_fwd_table_bytes");
+  return launch_fwd_plan(a, plan, table, stream);
 }
 
 int mesh_attn_merge(const ma_merge_args* a, void* stream) {

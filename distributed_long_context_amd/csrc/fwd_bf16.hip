@@ -505,7 +505,14 @@ fwd_bf16_kernel(const FwdParams p) {
 // its start-up dominates.  A unit's online softmax is the ring kernel's, step for step (the
 // results are the same bit for bit), over the 32-key halves that hold a key of the tile: a half
 // wholly past the last key, and the scores after the last half, are not computed.
-template <int D>
+//
+// TABLE: the tiles come from a table in device memory (p.table, p.wg_map: the tile of each
+// workgroup; this launch's workgroups start at p.wg_base), for calls of many more tiles than
+// the kernel-argument table holds.  Before anything else every workgroup checks the table's
+// header against what the host planned for these arguments (tile and workgroup counts, hash);
+// on a mismatch (a table packed for other arguments, or changed since) it returns at once, so
+// the launch writes nothing rather than reading stale pointers.
+template <int D, bool TABLE>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_resident_kernel(const FwdParams p) {
@@ -521,11 +528,21 @@ fwd_bf16_resident_kernel(const FwdParams p) {
   const int hl = lane >> 5;
 
   // ---- which tile / batch / KV head / chunk of units (the ring kernel's decode) ----
-  const int w = blockIdx.x;
-  int ti = 0;
+  int w = blockIdx.x;
+  FwdTile T;
+  if constexpr (TABLE) {
+    const FwdTableHeader hd = *p.table_header;
+    if (hd.magic != kFwdTableMagic || hd.ntiles != p.table_ntiles || hd.nwgs != p.table_nwgs ||
+        hd.hash != p.table_hash)
+      return;  // uniform: not the table these arguments were packed into
+    w += p.wg_base;
+    T = p.table[__builtin_amdgcn_readfirstlane(p.wg_map[w])];
+  } else {
+    int ti = 0;
 #pragma unroll
-  for (int j = 1; j < kFwdTilesPerLaunch; ++j) ti += (j < p.ntiles && w >= p.tiles[j].wg_begin) ? 1 : 0;
-  const FwdTile T = p.tiles[__builtin_amdgcn_readfirstlane(ti)];
+    for (int j = 1; j < kFwdTilesPerLaunch; ++j) ti += (j < p.ntiles && w >= p.tiles[j].wg_begin) ? 1 : 0;
+    T = p.tiles[__builtin_amdgcn_readfirstlane(ti)];
+  }
   const int local = w - T.wg_begin;
   const int kvh = local % p.hkv;
   const int rest = local / p.hkv;
@@ -679,8 +696,14 @@ void launch_waves(const FwdParams& p, int head_dim, dim3 grid, hipStream_t s) {
 int launch_fwd_bf16_resident(const FwdParams& p, int head_dim, int total_wgs, void* stream) {
   if (total_wgs <= 0) return 0;
   hipStream_t s = (hipStream_t)stream;
-  if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_resident_kernel<128>), dim3(total_wgs), dim3(512), 0, s, p);
-  else hipLaunchKernelGGL((fwd_bf16_resident_kernel<64>), dim3(total_wgs), dim3(512), 0, s, p);
+  const dim3 grid(total_wgs), block(512);
+  if (p.table) {
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_resident_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_resident_kernel<64, true>), grid, block, 0, s, p);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_resident_kernel<128, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fwd_bf16_resident_kernel<64, false>), grid, block, 0, s, p);
+  }
   return (int)hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ struct KPos {
 
 // ---- tile forward ----
 constexpr int kFwdTilesPerLaunch = 30;
-constexpr int32_t kFwdChained = 2;  // FwdTile::accumulate flag of a chained key segment  // the parameter block stays under the 4 KB kernel-argument limit
+constexpr int32_t kFwdChained = 2;  // FwdTile::accumulate flag of a chained key segment
 
 struct FwdTile {
   const void* q;
@@ -57,7 +57,31 @@ struct FwdParams {
   uint8_t heads_of[MA_MAX_HEADS];      // query heads ordered by KV head
   uint8_t kv_first[MA_MAX_HEADS + 1];  // start of each KV head's run in heads_of
   FwdTile tiles[kFwdTilesPerLaunch];
+  // A resident-KV launch from a tile table in device memory (table != nullptr; tiles[] unused):
+  // the table's tiles and workgroup map, the launch's first workgroup in the map, and what the
+  // table's header must hold for the launch to run (the kernel checks it before anything else).
+  const struct FwdTableHeader* table_header;
+  const FwdTile* table;
+  const int32_t* wg_map;
+  int32_t wg_base;
+  int32_t table_ntiles;
+  int32_t table_nwgs;
+  uint64_t table_hash;
 };
+
+// Tile table in device memory (mesh_attn_tile_fwd_pack / mesh_attn_tile_fwd_tabled): this
+// header, then the resident-KV tiles (FwdTile, in call order), then one int32 per workgroup
+// naming its tile.  hash is FNV-1a (64-bit) over the tiles and the map.
+constexpr uint32_t kFwdTableMagic = 0x5441424du;  // "MBAT"
+struct FwdTableHeader {
+  uint32_t magic;
+  int32_t ntiles;
+  int32_t nwgs;
+  int32_t reserved;
+  uint64_t hash;
+  uint64_t reserved2;
+};
+static_assert(sizeof(FwdTableHeader) == 32 && sizeof(FwdTile) % 8 == 0, "table layout");
 
 // launchers (return hipError_t as int)
 static_assert(sizeof(FwdParams) <= 4096, "forward parameters exceed the kernel-argument limit");

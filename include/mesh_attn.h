@@ -3,7 +3,9 @@
  *
  * One GPU's share of the Q-KV assignment matrix of distributed attention:
  *   - mesh_attn_tile_fwd : exact attention of (Q partition, KV partition) tiles,
- *                          each emitting a partial output O and a per-row LSE;
+ *                          each emitting a partial output O and a per-row LSE
+ *                          (mesh_attn_tile_fwd_tabled: the same with the tile
+ *                          table in device memory, for thousands of small tiles);
  *   - mesh_attn_merge    : the LSE-based merge that folds k partial (O, LSE)
  *                          pairs of one Q partition into its output;
  *   - mesh_attn_tile_bwd : the matching backward (dQ, dK, dV from O, LSE, dO);
@@ -171,6 +173,38 @@ typedef struct {
 } ma_tile_fwd_args;
 
 int mesh_attn_tile_fwd(const ma_tile_fwd_args* args, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Tile forward with a tile table in device memory, for calls of many small
+ * tiles: at [CHARM+]'s smallest partition sizes (its scaling table, 13440
+ * tokens over 64 partitions: tiles of 210 tokens) one GPU's share is thousands
+ * of tiles.  mesh_attn_tile_fwd hands tiles to the kernels in kernel arguments,
+ * a few dozen per launch; here the tiles of its resident-KV class (unmasked bf16
+ * tiles of 129-256 keys at d = 128, of at most 512 keys at d = 64) run from a
+ * table in device memory, all in one launch (one more wherever a tile names the
+ * output of a tile before it), and every other tile as in mesh_attn_tile_fwd.
+ * Results, accumulate mode, output ordering and argument checks are those of
+ * mesh_attn_tile_fwd on the same arguments, bit for bit.
+ *
+ * mesh_attn_tile_fwd_table_bytes: the table's size for these arguments (at
+ *   least 32 bytes; 0 when the arguments are invalid, see mesh_attn_last_error).
+ * mesh_attn_tile_fwd_pack: checks the arguments as mesh_attn_tile_fwd does and
+ *   writes the table into host memory `table` of `bytes` >= that size (host
+ *   only; nothing is enqueued).  The caller copies it to device memory, for
+ *   example through pinned memory on the stream of the launch.
+ * mesh_attn_tile_fwd_tabled: the forward, with `table` (device, 16-byte
+ *   aligned, `bytes` >= the size above) holding what mesh_attn_tile_fwd_pack
+ *   wrote for the same arguments by the time the stream reaches the call, and
+ *   unchanged until the launch has run.  The table holds the tiles' device
+ *   pointers, so the library checks it in the kernel: its header must carry the
+ *   tile count, workgroup count and 64-bit hash planned for these arguments, or
+ *   the resident-KV launch returns without reading the tiles or writing any
+ *   output (a table packed for other arguments is not run).  Ownership and
+ *   errors as in mesh_attn_tile_fwd; the table is the caller's memory.
+ * --------------------------------------------------------------------------- */
+size_t mesh_attn_tile_fwd_table_bytes(const ma_tile_fwd_args* args);
+int mesh_attn_tile_fwd_pack(const ma_tile_fwd_args* args, void* table, size_t bytes);
+int mesh_attn_tile_fwd_tabled(const ma_tile_fwd_args* args, const void* table, size_t bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * LSE merge.  [Mesh] section 2.2 (online softmax rescales partial outputs by

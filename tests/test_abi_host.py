@@ -275,3 +275,69 @@ def test_python_workspace_helper_needs_the_mask_mode():
     params = inspect.signature(ma.mesh_attn_tile_bwd_workspace_size).parameters
     assert params["mask_mode"].default is inspect.Parameter.empty
     assert params["scale"].default is inspect.Parameter.empty
+
+
+def _table_case(n, sq=210, sk=210, hq=32, hkv=8):
+    """n tiles of the resident-KV class (unmasked bf16, d = 128, 129-256 keys), fake device pointers
+    (host-only calls never touch them)."""
+    t = _tile_arr(n, sq, sk, step=1 << 26)
+    a = _fwd_args(ntiles=n, hq=hq, hkv=hkv)
+    a.tiles = C.cast(t, C.POINTER(_abi.ma_tile))
+    row = hq * 128
+    a.q_stride[:] = a.o_stride[:] = (sq * row, row, 128)
+    a.k_stride[:] = a.v_stride[:] = (sk * hkv * 128, hkv * 128, 128)
+    a.lse_stride[:] = (hq * sq, sq)
+    return a, t
+
+
+def _parse_table(buf):
+    import struct
+    magic, ntiles, nwgs, _, h = struct.unpack_from("<IiiiQ", buf, 0)
+    tiles = []
+    for i in range(ntiles):
+        off = 32 + 120 * i  # q, k, v, o, lse, sq, sk, wg_begin, chunks
+        tiles.append(struct.unpack_from("<5Q4i", buf, off))
+    wg_map = list(struct.unpack_from(f"<{nwgs}i", buf, 32 + 120 * ntiles))
+    return magic, h, tiles, wg_map
+
+
+def test_tile_table_layout():
+    # 40 tiles of 210 x 210 at 32/8 heads: 7 row blocks x 4 heads = 28 units, one workgroup chunk per
+    # (KV head), 8 workgroups a tile; a tile of 64 keys (ring kernel) in the middle stays out of the table
+    L = _abi.lib()
+    a, t = _table_case(41)
+    t[20].sk = 64
+    n = L.mesh_attn_tile_fwd_table_bytes(C.byref(a))
+    assert n == 32 + 40 * 120 + 40 * 8 * 4
+    buf = (C.c_ubyte * n)()
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf, n) == _abi.MA_OK
+    magic, h, tiles, wg_map = _parse_table(bytes(buf))
+    assert magic == 0x5441424D and len(tiles) == 40 and len(wg_map) == 320
+    resident = [i for i in range(41) if i != 20]
+    for k, (i, e) in enumerate(zip(resident, tiles)):
+        assert e[:5] == (t[i].q, t[i].k, t[i].v, t[i].o, t[i].lse)
+        assert e[5:] == (210, 210, 8 * k, 1)  # sq, sk, first workgroup in the map, chunks
+    assert wg_map == [w // 8 for w in range(320)]
+    # the hash follows the tiles: another output pointer, another hash
+    t[3].o += 1 << 20
+    buf2 = (C.c_ubyte * n)()
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf2, n) == _abi.MA_OK
+    assert _parse_table(bytes(buf2))[1] != h
+
+
+def test_tile_table_calls_reject_bad_buffers_without_launching():
+    L = _abi.lib()
+    a, _ = _table_case(3)
+    n = L.mesh_attn_tile_fwd_table_bytes(C.byref(a))
+    small = (C.c_ubyte * (n - 1))()
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), small, n - 1) == _abi.MA_ERR_INVALID
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), None, n) == _abi.MA_ERR_INVALID
+    # a launch on this host (no GPU) would report MA_ERR_LAUNCH: these are refused before it
+    assert L.mesh_attn_tile_fwd_tabled(C.byref(a), None, n, None) == _abi.MA_ERR_INVALID
+    assert L.mesh_attn_tile_fwd_tabled(C.byref(a), 0x100008, n, None) == _abi.MA_ERR_INVALID
+    assert L.mesh_attn_tile_fwd_tabled(C.byref(a), 0x100000, n - 1, None) == _abi.MA_ERR_INVALID
+    bad = _fwd_args(head_dim=96, ntiles=1)
+    assert L.mesh_attn_tile_fwd_table_bytes(C.byref(bad)) == 0
+    empty = _fwd_args(ntiles=0)
+    assert L.mesh_attn_tile_fwd_table_bytes(C.byref(empty)) == 32
+    assert L.mesh_attn_tile_fwd_tabled(C.byref(empty), None, 0, None) == _abi.MA_OK

@@ -77,13 +77,15 @@ def test_backward_traffic_summary_scales_by_the_copy_and_averages_calls(tmp_path
     assert bench.stored_traffic() is None
 
 
-def test_small_tile_traffic_summary_counts_the_resident_kernel_per_call(tmp_path, monkeypatch):
+def test_small_tile_traffic_summary_counts_the_table_launches_per_call(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "SMALL_TRAFFIC_FILE", str(tmp_path / "small.md"))
     copy = "__amd_rocclr_copyBuffer"
-    res = "void ma::(anonymous namespace)::fwd_bf16_resident_kernel<128>(ma::FwdParams)"
+    res = "void ma::(anonymous namespace)::fwd_bf16_resident_kernel<128, true>(ma::FwdParams)"
+    res_ka = "void ma::(anonymous namespace)::fwd_bf16_resident_kernel<128, false>(ma::FwdParams)"
     ring = "void ma::(anonymous namespace)::fwd_bf16_kernel<128, false, 4>(ma::FwdParams)"
-    fetch = [(1, ring, 999), (2, res, 30), (3, res, 50), (4, res, 70), (5, res, 90), (6, copy, 512)]
-    write = [(1, ring, 999), (2, res, 100), (3, res, 100), (4, res, 100), (5, res, 100), (6, copy, 1024)]
+    fetch = [(1, ring, 999), (2, res, 30), (3, res, 50), (4, res, 70), (5, res, 90), (6, copy, 512), (7, res_ka, 999)]
+    write = [(1, ring, 999), (2, res, 100), (3, res, 100), (4, res, 100), (5, res, 100), (6, copy, 1024),
+             (7, res_ka, 999)]
     _pmc_csv(tmp_path / "f.csv", fetch)
     _pmc_csv(tmp_path / "w.csv", write)
     bench.summarize_pmc_small(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1, 2, "rocprofv3 --pmc PMC -- cmd")

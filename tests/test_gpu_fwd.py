@@ -471,3 +471,109 @@ def test_fwd_resident_kv_tiles(case, acc):
     for t, (Oref, Lref) in zip(tiles, refs):
         check_close("O", host_f64(t.o), Oref, BF16_O_TOL, normalised_also=False)
         check_close("LSE", host_f64(t.lse), Lref, BF16_LSE_TOL)
+
+
+def _tile_set(wid, shapes, hq, hkv, d, acc, shared=()):
+    """Tiles of the given (sq, sk) shapes with seeded inputs; with acc, outputs hold seeded incoming
+    partials (two identical copies of every output: for the table path and the kernel-argument path).
+    `shared` lists groups of tile indices that name one output (applied in list order)."""
+    owner = {}
+    for grp in shared:
+        for i in grp[1:]:
+            owner[i] = grp[0]
+    smax = max(max(sq, sk) for sq, sk in shapes)  # every tensor a prefix view of a buffer this long
+
+    def view(t, n, kind):
+        shape = (1, smax, t.shape[2], t.shape[3]) if kind == "bshd" else (1, t.shape[1], smax)
+        buf = torch.full(shape, float("nan"), dtype=t.dtype, device=DEV)
+        out = buf[:, :n] if kind == "bshd" else buf[:, :, :n]
+        out.copy_(t)
+        return out
+
+    ins, outs = [], [[], []]
+    for i, (sq, sk) in enumerate(shapes):
+        q, qv = gen(wid, synthetic.T_Q, i, (1, sq, hq, d))
+        k, kv = gen(wid, synthetic.T_K, i, (1, sk, hkv, d))
+        v, vv = gen(wid, synthetic.T_V, i, (1, sk, hkv, d))
+        ins.append((view(q, sq, "bshd"), view(k, sk, "bshd"), view(v, sk, "bshd"), qv, kv, vv))
+        for c in range(2):
+            if i in owner:
+                outs[c].append(outs[c][owner[i]])
+                continue
+            if acc:
+                o, ov = gen(wid, synthetic.T_O_IN, i, (1, sq, hq, d))
+                li = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (1, hq, sq)) + np.float32(math.log(sk))).astype(
+                    np.float32)
+                outs[c].append((view(o, sq, "bshd"), view(torch.from_numpy(li).to(DEV), sq, "bhs"), ov,
+                                li.astype(np.float64)))
+            else:
+                outs[c].append((view(torch.full((1, sq, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV), sq,
+                                     "bshd"),
+                                view(torch.full((1, hq, sq), float("nan"), dtype=torch.float32, device=DEV), sq, "bhs"),
+                                None, None))
+    tiles = [[Tile(x[0], x[1], x[2], o[0], o[1]) for x, o in zip(ins, outs[c])] for c in range(2)]
+    return ins, outs, tiles
+
+
+@pytest.mark.parametrize("d,acc", [(128, False), (64, False), (128, True)])
+def test_fwd_tile_table_matches_kernel_arguments(d, acc):
+    """One call of 100 tiles through mesh_attn_tile_fwd_tabled (the resident-KV tiles from a device
+    table, one launch for all of them) and through mesh_attn_tile_fwd (launches of at most 30 tiles
+    from kernel arguments): bitwise equal.  Tiles outside the resident class are mixed in, and with
+    accumulate two groups of tiles name one output each, so the table launch is cut where they
+    repeat; sampled tiles and the shared outputs are checked against the oracle."""
+    hq, hkv = 32, 8
+    scale = np.float32(1.0 / math.sqrt(d))
+    res = 210 if d == 128 else 400
+    shapes = [(res, res)] * 92 + [(res, 64), (37, 1000), (300, 129), (256, 256), (1, 200), (97, res), (res, 33),
+                                  (64, 257)]
+    shared = ((5, 6, 7), (40, 41)) if acc else ()
+    log(f"[fwd tile table] d={d} acc={acc} tiles={len(shapes)}")
+    ins, outs, tiles = _tile_set(2800 + d + (1 if acc else 0), shapes, hq, hkv, d, acc, shared)
+    ma.mesh_attn_tile_fwd(tiles[0], float(scale), ma.MA_MASK_NONE, accumulate=acc, table=True)
+    ma.mesh_attn_tile_fwd(tiles[1], float(scale), ma.MA_MASK_NONE, accumulate=acc)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(tiles[0][i].o, tiles[1][i].o) and torch.equal(tiles[0][i].lse, tiles[1][i].lse), i
+    firsts = {g[0]: g for g in shared}
+    skip = {i for g in shared for i in g[1:]}
+    for i in [0, 5, 40, 91, 92, 94, 95, 97]:
+        if i in skip:
+            continue
+        grp = firsts.get(i, (i,))
+        parts = [attn_tile(ins[j][3], ins[j][4], ins[j][5], scale) for j in grp]
+        if acc:
+            parts = [(outs[0][i][2], outs[0][i][3])] + parts
+        Oref, Lref = merge(parts) if len(parts) > 1 else parts[0]
+        check_close(f"O tile {i}", host_f64(tiles[0][i].o), Oref, BF16_O_TOL, normalised_also=False)
+        check_close(f"LSE tile {i}", host_f64(tiles[0][i].lse), Lref, BF16_LSE_TOL)
+
+
+def test_fwd_tile_table_of_other_arguments_is_not_run():
+    """A device table packed for one set of tiles, handed to the call of another set of the same
+    shapes: the resident-KV launch finds the header's hash different and writes nothing (the
+    outputs keep their NaN fill); the call with its own table then computes them."""
+    from distributed_long_context_amd import _abi
+    import ctypes as C
+    hq, hkv, d = 32, 8, 128
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    shapes = [(210, 210)] * 12
+    log("[fwd tile table] stale table")
+    _, _, ta = _tile_set(2850, shapes, hq, hkv, d, False)
+    _, _, tb = _tile_set(2851, shapes, hq, hkv, d, False)
+    pa = ma.prepare_tile_fwd(ta[0], scale, ma.MA_MASK_NONE, table=True)
+    pb = ma.prepare_tile_fwd(tb[0], scale, ma.MA_MASK_NONE, table=True)
+    _, dev_a, n_a = pa[3]
+    L = _abi.lib()
+    s = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.mesh_attn_tile_fwd_tabled(C.byref(pb[0]), C.c_void_p(dev_a.data_ptr()), n_a, s) == _abi.MA_OK
+    torch.cuda.synchronize()
+    for t in tb[0]:
+        assert torch.isnan(t.o.float()).all() and torch.isnan(t.lse).all()
+    for t in ta[0]:  # the tiles the table was packed for are not touched either
+        assert torch.isnan(t.o.float()).all()
+    ma.launch_prepared_tile_fwd(pb)
+    ma.mesh_attn_tile_fwd(tb[1], scale, ma.MA_MASK_NONE)
+    torch.cuda.synchronize()
+    for t0, t1 in zip(tb[0], tb[1]):
+        assert torch.equal(t0.o, t1.o) and torch.equal(t0.lse, t1.lse)

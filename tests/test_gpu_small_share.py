@@ -1,8 +1,10 @@
 """Full-size parity of the small-tile share the bench times: a 13440 x 13440 non-causal share
 (32/8 heads, d = 128, bf16) cut into P x P tiles at [CHARM+]'s partition sizes (its scaling
 table: 13440 tokens over 1, 4, 16 and 64 partitions), all (13440 / P)^2 tiles in one forward call,
-every output a slice of one long buffer as in the bench.  Tiles of 210 keys run the resident-KV
-kernel, 840 and 3360 the four-wave ring kernel, 13440 the eight-wave one.  Sampled tiles (the
+every output a slice of one long buffer, through mesh_attn_tile_fwd_tabled as in the bench.  Tiles
+of 210 keys run the resident-KV kernel from the tile table (and, at 210, the same call through
+mesh_attn_tile_fwd must give the same bits), 840 and 3360 the four-wave ring kernel, 13440 the
+eight-wave one.  Sampled tiles (the
 corners, the diagonal ends and seeded others) are checked on sampled rows, every query head,
 against the fp64 oracle over all of the tile's keys."""
 import math
@@ -50,8 +52,16 @@ def test_small_tile_share_full_size(share, P, ntiles_checked):
             tiles.append(Tile(q[:, i * P:(i + 1) * P], k[:, j * P:(j + 1) * P], v[:, j * P:(j + 1) * P],
                               o_all[t * P * HQ * D:(t + 1) * P * HQ * D].view(1, P, HQ, D),
                               l_all[t * HQ * P:(t + 1) * HQ * P].view(1, HQ, P)))
-    ma.mesh_attn_tile_fwd(tiles, float(SCALE), ma.MA_MASK_NONE)
+    ma.mesh_attn_tile_fwd(tiles, float(SCALE), ma.MA_MASK_NONE, table=True)  # the bench's path
     torch.cuda.synchronize()
+    if P == 210:  # the same call with the tiles in kernel arguments: bitwise the same
+        o2, l2 = torch.full_like(o_all, float("nan")), torch.full_like(l_all, float("nan"))
+        tiles2 = [Tile(t.q, t.k, t.v, o2[i * P * HQ * D:(i + 1) * P * HQ * D].view(1, P, HQ, D),
+                       l2[i * HQ * P:(i + 1) * HQ * P].view(1, HQ, P)) for i, t in enumerate(tiles)]
+        ma.mesh_attn_tile_fwd(tiles2, float(SCALE), ma.MA_MASK_NONE)
+        torch.cuda.synchronize()
+        assert torch.equal(o_all, o2) and torch.equal(l_all, l2)
+        del o2, l2, tiles2
     rng = np.random.default_rng([WID, P])
     fixed = [0, n - 1, n * (n - 1), n * n - 1, (n // 2) * n + n // 2]
     picks = list(dict.fromkeys(fixed))
