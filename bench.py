@@ -302,15 +302,19 @@ def _pmc_per_dispatch(path):
     return by
 
 
+def _calib_copy(per_dispatch):
+    """The counter value of the calibration copy: the largest runtime blit (__amd_rocclr_copyBuffer)
+    in the run.  The runtime also blits small host-to-device copies, such as the tile tables."""
+    return max(v for (_, n), v in per_dispatch.items() if "copyBuffer" in n)
+
+
 def summarize_pmc_small(fetch_csv, write_csv, copy_mib, calls, command):
     """Write the HBM-traffic summary of the 210-token small-tile forward (every dispatch of the
     tile-table instance of the resident-KV kernel in the run belongs to its `calls` calls) from two
     rocprofv3 --pmc runs, scaled like summarize_pmc by the plain device copy of copy_mib MiB."""
     fetch, write = _pmc_per_dispatch(fetch_csv), _pmc_per_dispatch(write_csv)
     copy_kib = copy_mib * 1024.0
-    cf = [v for (_, n), v in fetch.items() if "copyBuffer" in n]
-    cw = [v for (_, n), v in write.items() if "copyBuffer" in n]
-    f_scale, w_scale = copy_kib / (sum(cf) / len(cf)), copy_kib / (sum(cw) / len(cw))
+    f_scale, w_scale = copy_kib / _calib_copy(fetch), copy_kib / _calib_copy(write)
     sel = [k for k in fetch if "fwd_bf16_resident_kernel<128, true>" in k[1]]  # the tile-table launches
     read = sum(fetch[k] for k in sel) * f_scale * 1024 / calls
     written = sum(write.get(k, 0.0) for k in sel) * w_scale * 1024 / calls
@@ -355,7 +359,8 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, command):
     # the reference copy is the runtime's device-to-device blit of --calib-copy-mb (torch's elementwise
     # copy kernels of the input set-up are not it)
     copy_name = next(k for k in fk if "copyBuffer" in k)
-    f_scale, w_scale = copy_kib / mean(fk[copy_name]), copy_kib / mean(wk[copy_name])
+    f_copy, w_copy = _calib_copy(fetch), _calib_copy(write)
+    f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
     short = lambda n: n.replace("ma::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
     # one backward call = the consecutive dispatches of the three backward kernels
     calls, cur = [], None
@@ -378,7 +383,7 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, command):
              "Two rocprofv3 runs of the same command, one counter each (KiB per dispatch):", "",
              "    " + command.replace("PMC", "FETCH_SIZE"), "    " + command.replace("PMC", "WRITE_SIZE"), "",
              f"Calibration: the plain device copy of {copy_mib} MiB ({short(copy_name)}) reads FETCH_SIZE "
-             f"{mean(fk[copy_name]):.0f} KiB and WRITE_SIZE {mean(wk[copy_name]):.0f} KiB, so the factors are "
+             f"{f_copy:.0f} KiB and WRITE_SIZE {w_copy:.0f} KiB, so the factors are "
              f"{f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
              "| Kernel | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | scaled MiB read | scaled MiB written |",
              "|---|---|---|---|---|---|"]

@@ -83,9 +83,11 @@ def test_small_tile_traffic_summary_counts_the_table_launches_per_call(tmp_path,
     res = "void ma::(anonymous namespace)::fwd_bf16_resident_kernel<128, true>(ma::FwdParams)"
     res_ka = "void ma::(anonymous namespace)::fwd_bf16_resident_kernel<128, false>(ma::FwdParams)"
     ring = "void ma::(anonymous namespace)::fwd_bf16_kernel<128, false, 4>(ma::FwdParams)"
-    fetch = [(1, ring, 999), (2, res, 30), (3, res, 50), (4, res, 70), (5, res, 90), (6, copy, 512), (7, res_ka, 999)]
-    write = [(1, ring, 999), (2, res, 100), (3, res, 100), (4, res, 100), (5, res, 100), (6, copy, 1024),
+    # dispatch 0 is a small tile-table upload the runtime blits: not the calibration copy
+    fetch = [(0, copy, 3), (1, ring, 999), (2, res, 30), (3, res, 50), (4, res, 70), (5, res, 90), (6, copy, 512),
              (7, res_ka, 999)]
+    write = [(0, copy, 0.03), (1, ring, 999), (2, res, 100), (3, res, 100), (4, res, 100), (5, res, 100),
+             (6, copy, 1024), (7, res_ka, 999)]
     _pmc_csv(tmp_path / "f.csv", fetch)
     _pmc_csv(tmp_path / "w.csv", write)
     bench.summarize_pmc_small(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1, 2, "rocprofv3 --pmc PMC -- cmd")
