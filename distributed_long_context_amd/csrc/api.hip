@@ -9,6 +9,7 @@
 #include <vector>
 #include <algorithm>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "mesh_attn.h"
@@ -143,7 +144,8 @@ int check_shifted_outputs(int n, PtrOf ptr_of, RowsOf rows_of, int64_t row_bytes
 
 // One forward call, planned before anything is enqueued: its launches in order (a launch class
 // with its kernel parameters, or the (0, -inf) fill of an EMPTY tile) and, when the resident-KV
-// tiles go through a tile table in device memory, that table (tiles and workgroup map).
+// tiles go through a tile table in device memory, that table (tiles, group entries, workgroup
+// records).
 constexpr int kClasses = 5, kResident = 4;
 struct FwdPlan {
   struct Launch {
@@ -155,23 +157,31 @@ struct FwdPlan {
   std::vector<Launch> launches;
   std::vector<FwdParams> batches;
   std::vector<FwdTile> table;
-  std::vector<int32_t> wg_map;
+  std::vector<FwdResEnt> ents;
+  std::vector<FwdResWg> wgs;
+  int64_t units = 0;  // units numbered so far in the table
 };
 
-// FNV-1a (64-bit) over the table's tiles and map
+// FNV-1a (64-bit) over the table's tiles, entries and workgroup records, taken as 64-bit words
 uint64_t table_hash(const FwdPlan& plan) {
   uint64_t h = 1469598103934665603ull;
   auto mix = [&](const void* data, size_t n) {
     const unsigned char* b = (const unsigned char*)data;
-    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 1099511628211ull;
+    for (size_t i = 0; i + 8 <= n; i += 8) {
+      uint64_t w;
+      std::memcpy(&w, b + i, 8);
+      h = (h ^ w) * 1099511628211ull;
+    }
   };
-  if (!plan.table.empty()) mix(plan.table.data(), plan.table.size() * sizeof(FwdTile));
-  if (!plan.wg_map.empty()) mix(plan.wg_map.data(), plan.wg_map.size() * sizeof(int32_t));
+  mix(plan.table.data(), plan.table.size() * sizeof(FwdTile));
+  mix(plan.ents.data(), plan.ents.size() * sizeof(FwdResEnt));
+  mix(plan.wgs.data(), plan.wgs.size() * sizeof(FwdResWg));
   return h;
 }
 
 size_t table_bytes(const FwdPlan& plan) {
-  return sizeof(FwdTableHeader) + plan.table.size() * sizeof(FwdTile) + plan.wg_map.size() * sizeof(int32_t);
+  return sizeof(FwdTableHeader) + plan.table.size() * sizeof(FwdTile) + plan.ents.size() * sizeof(FwdResEnt) +
+         plan.wgs.size() * sizeof(FwdResWg);
 }
 
 int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
@@ -240,8 +250,9 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
   // The whole call is planned first and launched afterwards, so an argument error
   // found on any tile leaves nothing enqueued.
   // With a table (use_table), the resident-KV tiles go to plan.table instead: no limit of tiles
-  // per launch; a launch is a span of the table's workgroup map, cut where a tile names an output
-  // already queued.
+  // per launch; a launch is a span of the table, cut where a tile names an output already
+  // queued.  The span's tiles with the same K and V form groups, and a workgroup runs a range of
+  // one group's units (group_span below).
   std::vector<FwdPlan::Launch>& launches = plan.launches;
   std::vector<FwdParams>& batches = plan.batches;
   FwdParams bp[kClasses];
@@ -251,11 +262,52 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
     bp[m].mask = m != kResident && (m & 1);
   }
   size_t tab_first = 0;  // first table tile of the resident span being filled
+  int64_t tab_units = 0;  // units of the table's tiles so far
+  // Groups the span's tiles by K/V (pointers and length: one LDS copy serves them all) and writes
+  // each group's entries (its tiles, units numbered on from plan.units) and workgroup records:
+  // per chunk of `cap` consecutive units of the group, one workgroup per (batch, KV head), the KV
+  // head fastest (so the XCD of a workgroup follows its KV head).  cap grows from kFwdResUnits to
+  // kFwdResUnitsMax while the span still gives about 2048 workgroups (8 per CU): more units per
+  // workgroup spread its K/V loads over more work and split evenly over the 8 waves.  Returns the
+  // span's workgroup count.
+  auto group_span = [&](size_t first, size_t last) -> int64_t {
+    std::vector<size_t> idx;
+    for (size_t j = first; j < last; ++j) idx.push_back(j);
+    auto key = [&](size_t j) { return std::make_tuple(plan.table[j].k, plan.table[j].v, plan.table[j].sk); };
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t x, size_t y) { return key(x) < key(y); });
+    auto units_of = [&](size_t j) { return (int64_t)(plan.table[j].sq + 31) / 32 * p.gmax; };
+    int64_t total = 0;
+    for (size_t j : idx) total += units_of(j);
+    const int64_t per_wg = (int64_t)a->batch * a->hkv * total / 2048 / 8 * 8;
+    const int64_t cap = std::min<int64_t>(kFwdResUnitsMax, std::max<int64_t>(kFwdResUnits, per_wg));
+    const size_t wg0 = plan.wgs.size();
+    for (size_t g = 0; g < idx.size();) {
+      size_t g_end = g + 1;
+      while (g_end < idx.size() && key(idx[g_end]) == key(idx[g])) ++g_end;
+      const size_t e0 = plan.ents.size();
+      const int64_t u0 = plan.units;
+      for (size_t i = g; i < g_end; ++i) {
+        plan.ents.push_back(FwdResEnt{(int32_t)idx[i], (int32_t)plan.units});
+        plan.units += units_of(idx[i]);
+      }
+      size_t e = e0;
+      for (int64_t c = u0; c < plan.units; c += cap) {
+        while (e + 1 < plan.ents.size() && plan.ents[e + 1].unit0 <= c) ++e;
+        for (int b = 0; b < a->batch; ++b)
+          for (int h = 0; h < a->hkv; ++h)
+            plan.wgs.push_back(FwdResWg{(int32_t)e, (int32_t)c, (int32_t)std::min(plan.units, c + cap),
+                                        (int32_t)(b * a->hkv + h)});
+      }
+      g = g_end;
+    }
+    return (int64_t)(plan.wgs.size() - wg0);
+  };
   auto flush = [&](int m) {
     if (bn[m] == 0) return;
     bp[m].ntiles = bn[m];
     if (use_table && m == kResident) {
-      bp[m].wg_base = bwg[m] == 0 ? 0 : (int32_t)plan.wg_map.size() - bwg[m];
+      bp[m].wg_base = (int32_t)plan.wgs.size();
+      bwg[m] = (int)group_span(tab_first, plan.table.size());
       tab_first = plan.table.size();
     }
     launches.push_back(FwdPlan::Launch{m, bwg[m], (int)batches.size()});
@@ -302,8 +354,11 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
     if (wgs >= INT32_MAX) return set_error(MA_ERR_INVALID, "tile too large for one launch");
     // a chain stays in one launch, and a launch's workgroup count stays below 2^31
     const bool tabled = use_table && m == kResident;
-    if (tabled && (int64_t)plan.wg_map.size() + wgs >= INT32_MAX)
-      return set_error(MA_ERR_INVALID, "the tile table's workgroups must stay below 2^31");
+    // the table's workgroups (at most the tiles' own counts: grouping only merges chunks) and
+    // units stay below 2^31
+    if (tabled && ((int64_t)plan.wgs.size() + bwg[m] + wgs >= INT32_MAX ||
+                   tab_units + (t.sq + 31) / 32 * p.gmax >= INT32_MAX))
+      return set_error(MA_ERR_INVALID, "the tile table's workgroups and units must stay below 2^31");
     if ((!tabled && bn[m] + npcs > kFwdTilesPerLaunch) || bwg[m] + wgs >= INT32_MAX) flush(m);
     FwdTile scratch_tile;
     FwdTile& ft = tabled ? scratch_tile : bp[m].tiles[bn[m]];
@@ -320,10 +375,11 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
     } else {
       ft.qp.nseg = 1;
     }
-    if (tabled) {  // one tile entry in the table and one map entry per workgroup
-      ft.wg_begin = (int32_t)plan.wg_map.size();
-      plan.wg_map.insert(plan.wg_map.end(), (size_t)wgs, (int32_t)plan.table.size());
+    if (tabled) {  // one tile entry in the table; its workgroups come when the span is flushed
+      ft.wg_begin = 0;
+      ft.chunks = 0;
       plan.table.push_back(ft);
+      tab_units += (t.sq + 31) / 32 * p.gmax;
       bwg[m] += (int)wgs;
       ++bn[m];
       return MA_OK;  // resident tiles have no chained pieces
@@ -410,9 +466,12 @@ int launch_fwd_plan(const ma_tile_fwd_args* a, FwdPlan& plan, const void* dev_ta
       if (dev_table) {
         rp.table_header = (const FwdTableHeader*)dev_table;
         rp.table = (const FwdTile*)byte_offset(dev_table, sizeof(FwdTableHeader));
-        rp.wg_map = (const int32_t*)byte_offset(dev_table, sizeof(FwdTableHeader) + plan.table.size() * sizeof(FwdTile));
+        const size_t ents_off = sizeof(FwdTableHeader) + plan.table.size() * sizeof(FwdTile);
+        rp.res_ents = (const FwdResEnt*)byte_offset(dev_table, ents_off);
+        rp.res_wgs = (const FwdResWg*)byte_offset(dev_table, ents_off + plan.ents.size() * sizeof(FwdResEnt));
         rp.table_ntiles = (int32_t)plan.table.size();
-        rp.table_nwgs = (int32_t)plan.wg_map.size();
+        rp.table_nents = (int32_t)plan.ents.size();
+        rp.table_nwgs = (int32_t)plan.wgs.size();
         rp.table_hash = hash;
       }
       e = launch_fwd_bf16_resident(rp, a->head_dim, pl.wgs, stream);
@@ -460,14 +519,17 @@ int mesh_attn_tile_fwd_pack(const ma_tile_fwd_args* a, void* table, size_t bytes
   std::memset(&h, 0, sizeof(h));
   h.magic = kFwdTableMagic;
   h.ntiles = (int32_t)plan.table.size();
-  h.nwgs = (int32_t)plan.wg_map.size();
+  h.nwgs = (int32_t)plan.wgs.size();
+  h.nents = (int32_t)plan.ents.size();
   h.hash = table_hash(plan);
   unsigned char* out = (unsigned char*)table;
   std::memcpy(out, &h, sizeof(h));
-  if (!plan.table.empty()) std::memcpy(out + sizeof(h), plan.table.data(), plan.table.size() * sizeof(FwdTile));
-  if (!plan.wg_map.empty())
-    std::memcpy(out + sizeof(h) + plan.table.size() * sizeof(FwdTile), plan.wg_map.data(),
-                plan.wg_map.size() * sizeof(int32_t));
+  out += sizeof(h);
+  if (!plan.table.empty()) std::memcpy(out, plan.table.data(), plan.table.size() * sizeof(FwdTile));
+  out += plan.table.size() * sizeof(FwdTile);
+  if (!plan.ents.empty()) std::memcpy(out, plan.ents.data(), plan.ents.size() * sizeof(FwdResEnt));
+  out += plan.ents.size() * sizeof(FwdResEnt);
+  if (!plan.wgs.empty()) std::memcpy(out, plan.wgs.data(), plan.wgs.size() * sizeof(FwdResWg));
   return MA_OK;
 }
 

@@ -80,6 +80,14 @@ struct FwdCfg {
   static constexpr int STAGES = WAVES == 8 ? 5 : 2;
 };
 
+// The same address as a global-memory pointer: loads and stores through it are global, not flat,
+// instructions (a flat access also counts against the LDS wait counter), also where the compiler
+// cannot tell the address space itself, as for pointers read from a tile table.
+template <class X>
+__device__ __forceinline__ __attribute__((address_space(1))) X* gmem(X* ptr) {
+  return (__attribute__((address_space(1))) X*)ptr;
+}
+
 // ---- pieces of a 32-key step shared by the ring and resident-KV kernels ----
 // A wave owns 32 query rows (one per lane pair l, l^32); a 32-key half of a K/V block is one
 // 32 x 32 score tile S^T = K Q^T whose lane holds its query's 16 keys 16*(e/8) + 8*hl + e%8.
@@ -172,8 +180,13 @@ __device__ __forceinline__ void fwd_store_rows(const f32x16 (&oacc)[NC], float m
   float lse = has ? (m2 + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f : -INFINITY;
   float wn = has ? 1.0f / ltot : 0.0f;  // weight of this tile's unnormalised sums
   float wo = 0.0f;                      // weight of the output already held (accumulate)
+  bf16x4 old[NC][4];                    // the output already held, all loads issued before any use
   if (accumulate) {
-    const float lo = *lrow;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) old[c][g] = *gmem((const bf16x4*)(orow + c * 32 + g * 8 + hl * 4));
+    const float lo = *gmem(lrow);
     const float mx = fmaxf(lo, lse);
     if (mx == -INFINITY) {
       wn = 0.0f;
@@ -194,13 +207,12 @@ __device__ __forceinline__ void fwd_store_rows(const f32x16 (&oacc)[NC], float m
 #pragma unroll
       for (int i = 0; i < 4; ++i) v4[i] = oacc[c][g * 4 + i] * wn;
       if (accumulate) {
-        const bf16x4 old = *(const bf16x4*)dst;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = __builtin_fmaf(wo, (float)old[i], v4[i]);
+        for (int i = 0; i < 4; ++i) v4[i] = __builtin_fmaf(wo, (float)old[c][g][i], v4[i]);
       }
-      *(bf16x4*)dst = pack_bf16x4(v4);
+      *gmem((bf16x4*)dst) = pack_bf16x4(v4);
     }
-  if (hl == 0) *lrow = lse;
+  *gmem(lrow) = lse;  // lanes l and l^32 hold the same row and value: one store, no branch
 }
 
 // MASKED: causal on positions, the key positions one segment (global = kgb +
@@ -495,6 +507,20 @@ fwd_bf16_kernel(const FwdParams p) {
   fwd_store_rows(oacc, m2, ltot, T.accumulate & 1, orow, lrow, hl);
 }
 
+// Through the scalar cache: the tile table is written before the launch and never during it.
+template <class X>
+__device__ __forceinline__ X table_load(const X* ptr) {
+  static_assert(sizeof(X) % 4 == 0, "whole dwords");
+  typedef const __attribute__((address_space(4))) uint32_t* cptr;
+  const cptr src = (cptr)(const __attribute__((address_space(4))) char*)(const char*)ptr;
+  uint32_t w[sizeof(X) / 4];
+#pragma unroll
+  for (size_t i = 0; i < sizeof(X) / 4; ++i) w[i] = src[i];
+  X x;
+  __builtin_memcpy(&x, w, sizeof(X));
+  return x;
+}
+
 // Resident-KV instance, for unmasked tiles of few keys (kFwdResMinKeys < sk <= kFwdResKeys<D>):
 // one workgroup of 8 waves (two per SIMD) per (tile, batch, KV head, chunk of up to
 // kFwdResUnits units) loads the whole K and V of its KV head into LDS once, then every wave runs
@@ -506,12 +532,14 @@ fwd_bf16_kernel(const FwdParams p) {
 // results are the same bit for bit), over the 32-key halves that hold a key of the tile: a half
 // wholly past the last key, and the scores after the last half, are not computed.
 //
-// TABLE: the tiles come from a table in device memory (p.table, p.wg_map: the tile of each
-// workgroup; this launch's workgroups start at p.wg_base), for calls of many more tiles than
-// the kernel-argument table holds.  Before anything else every workgroup checks the table's
-// header against what the host planned for these arguments (tile and workgroup counts, hash);
-// on a mismatch (a table packed for other arguments, or changed since) it returns at once, so
-// the launch writes nothing rather than reading stale pointers.
+// TABLE: the tiles come from a table in device memory, for calls of many more tiles than the
+// kernel-argument table holds.  Tiles with the same K and V form a group, and a workgroup runs a
+// range of units of one group (p.res_wgs[p.wg_base + blockIdx.x]), whatever tiles they belong to,
+// against one LDS copy of K/V: with many tiles sharing a KV partition a workgroup amortises its
+// loads over up to kFwdResUnitsMax units, split evenly over its waves.  Before anything else every
+// workgroup checks the table's header against what the host planned for these arguments (tile,
+// entry and workgroup counts, hash); on a mismatch (a table packed for other arguments, or changed
+// since) it returns at once, so the launch writes nothing rather than reading stale pointers.
 template <int D, bool TABLE>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -527,35 +555,41 @@ fwd_bf16_resident_kernel(const FwdParams p) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  // ---- which tile / batch / KV head / chunk of units (the ring kernel's decode) ----
-  int w = blockIdx.x;
-  FwdTile T;
+  // ---- the workgroup's batch, KV head, K/V tile and range of units ----
+  FwdTile T;  // the tile (TABLE: the group's first tile, whose K/V every tile of the group has)
+  int b, kvh, u_begin, u_end, ent = 0;
   if constexpr (TABLE) {
-    const FwdTableHeader hd = *p.table_header;
-    if (hd.magic != kFwdTableMagic || hd.ntiles != p.table_ntiles || hd.nwgs != p.table_nwgs ||
-        hd.hash != p.table_hash)
+    const FwdTableHeader hd = table_load(p.table_header);
+    if (hd.magic != kFwdTableMagic || hd.ntiles != p.table_ntiles || hd.nents != p.table_nents ||
+        hd.nwgs != p.table_nwgs || hd.hash != p.table_hash)
       return;  // uniform: not the table these arguments were packed into
-    w += p.wg_base;
-    T = p.table[__builtin_amdgcn_readfirstlane(p.wg_map[w])];
+    const FwdResWg R = table_load(p.res_wgs + p.wg_base + blockIdx.x);
+    ent = R.ent;
+    T = table_load(p.table + table_load(&p.res_ents[ent].tile));
+    b = R.bk / p.hkv;
+    kvh = R.bk % p.hkv;
+    u_begin = R.u_begin;
+    u_end = R.u_end;
   } else {
+    const int w = blockIdx.x;
     int ti = 0;
 #pragma unroll
     for (int j = 1; j < kFwdTilesPerLaunch; ++j) ti += (j < p.ntiles && w >= p.tiles[j].wg_begin) ? 1 : 0;
     T = p.tiles[__builtin_amdgcn_readfirstlane(ti)];
+    const int local = w - T.wg_begin;
+    kvh = local % p.hkv;
+    const int rest = local / p.hkv;
+    b = rest / T.chunks;
+    u_begin = rest % T.chunks * kFwdResUnits;
+    u_end = u_begin + kFwdResUnits;  // clipped to the tile's units below
+    if (b >= p.batch) return;        // padding workgroup (uniform)
   }
-  const int local = w - T.wg_begin;
-  const int kvh = local % p.hkv;
-  const int rest = local / p.hkv;
-  const int chunk = rest % T.chunks;
-  const int b = rest / T.chunks;
-  if (b >= p.batch) return;  // padding workgroup (uniform)
-  const int g0 = p.kv_first[kvh];
-  const int gsz = p.kv_first[kvh + 1] - g0;
+  // byte arrays of the parameter block through scalar loads (a vector byte load would make the wave
+  // wait for every vector memory operation in flight, the previous unit's stores included)
+  const int g0 = kernarg_byte(offsetof(FwdParams, kv_first) + kvh);
+  const int gsz = kernarg_byte(offsetof(FwdParams, kv_first) + kvh + 1) - g0;
   if (gsz <= 0) return;
-  // units (32-row block, head of the group), query-block major
-  const int nunits = (T.sq + kQW - 1) / kQW * gsz;
-  const int u_begin = chunk * kFwdResUnits;
-  const int u_end = min(nunits, u_begin + kFwdResUnits);
+  if constexpr (!TABLE) u_end = min(u_end, (T.sq + kQW - 1) / kQW * gsz);  // units (32-row block, head)
   if (u_begin >= u_end) return;  // uniform
 
   const __bf16* Kg = (const __bf16*)T.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
@@ -584,21 +618,62 @@ fwd_bf16_resident_kernel(const FwdParams p) {
     }
   }
 
-  // ---- query fragments of a unit (B operand of S^T = K Q^T) ----
-  auto unit_head = [&](int u) { return p.heads_of[g0 + (u % gsz)]; };
-  auto load_q = [&](int u, bf16x8 (&f)[C::KS]) {
-    const int row = (u / gsz) * kQW + l32;
-    const bool ok = row < T.sq;
-    const __bf16* Qg = (const __bf16*)T.q + (int64_t)b * p.q_sb + (int64_t)unit_head(u) * p.q_sh + (int64_t)row * p.q_ss;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      bf16x8 z = {};
-      f[ks] = ok ? *(const bf16x8*)(Qg + ks * 16 + hl * 8) : z;
-    }
+  // ---- units: which rows of which tile, and their query fragments ----
+  struct Unit {
+    const __bf16* q;
+    __bf16* o;
+    float* lse;
+    int sq, row0, head, acc;
   };
-  int u = u_begin + wave;
+  // unit u of the workgroup's range; false for an empty head slot (a KV head with fewer than
+  // gmax query heads).  TABLE: ent only moves forward (a wave's units grow), and the entries'
+  // first units grow, so the entry holding u is the last one that starts at or before it.
+  auto decode = [&](int u, Unit& x) -> bool {
+    if constexpr (TABLE) {
+      while (ent + 1 < p.table_nents && table_load(&p.res_ents[ent + 1].unit0) <= u) ++ent;
+      const FwdResEnt en = table_load(p.res_ents + ent);
+      const int lu = u - en.unit0;
+      const int hs = lu % p.gmax;
+      if (hs >= gsz) return false;
+      const FwdTile* X = p.table + en.tile;
+      x.q = (const __bf16*)table_load(&X->q);
+      x.o = (__bf16*)table_load(&X->o);
+      x.lse = table_load(&X->lse);
+      x.sq = table_load(&X->sq);
+      x.acc = table_load(&X->accumulate) & 1;
+      x.row0 = lu / p.gmax * kQW;
+      x.head = kernarg_byte(offsetof(FwdParams, heads_of) + g0 + hs);
+    } else {
+      x.q = (const __bf16*)T.q;
+      x.o = (__bf16*)T.o;
+      x.lse = T.lse;
+      x.sq = T.sq;
+      x.acc = T.accumulate & 1;
+      x.row0 = u / gsz * kQW;
+      x.head = kernarg_byte(offsetof(FwdParams, heads_of) + g0 + u % gsz);
+    }
+    return true;
+  };
+  // the first unit at or after u, in steps of kWaves, that has rows (u_end: none)
+  auto seek = [&](int u, Unit& x) {
+    while (u < u_end && !decode(u, x)) u += kWaves;
+    return u;
+  };
+  // A lane whose row is past the tile's end takes the last row: it computes that row's result
+  // bit for bit (its scores, max and sums are the same, and the wave's rescale decisions, taken
+  // over all lanes, do not change) and stores the same values to the same place.  So no load or
+  // store of a unit sits under a branch: a branch would make the wait for the next unit's query
+  // fragments also wait for this unit's stores (the wait counter is merged over both paths).
+  auto unit_row = [&](const Unit& x) { return min(x.row0 + l32, x.sq - 1); };
+  auto load_q = [&](const Unit& x, bf16x8 (&f)[C::KS]) {
+    const __bf16* Qg = x.q + (int64_t)b * p.q_sb + (int64_t)x.head * p.q_sh + (int64_t)unit_row(x) * p.q_ss;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) f[ks] = *gmem((const bf16x8*)(Qg + ks * 16 + hl * 8));
+  };
+  Unit cur;
+  int u = seek(u_begin + wave, cur);
   bf16x8 qf[C::KS];
-  if (u < u_end) load_q(u, qf);
+  if (u < u_end) load_q(cur, qf);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the blocks and the first fragments
   __syncthreads();
   if (u >= u_end) return;  // no unit for this wave
@@ -659,21 +734,20 @@ fwd_bf16_resident_kernel(const FwdParams p) {
 
   // ---- the wave's units: u_begin + wave + 8 i ----
   for (;;) {
-    const int un = u + kWaves;
+    Unit nxt;
+    const int un = seek(u + kWaves, nxt);
     bf16x8 qn[C::KS];
-    if (un < u_end) load_q(un, qn);  // in flight under this unit's blocks
+    if (un < u_end) load_q(nxt, qn);  // in flight under this unit's blocks
     if (sk % kBN != 0) run_unit(std::true_type{});  // the last block is ragged
     else run_unit(std::false_type{});
     const float ltot = xhalf_sum(lsum);
-    const int row = (u / gsz) * kQW + l32;
-    if (row < T.sq) {
-      const int64_t h = unit_head(u);
-      __bf16* orow = (__bf16*)T.o + (int64_t)b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_ss;
-      float* lrow = T.lse + (int64_t)b * p.l_sb + h * p.l_sh + row;
-      fwd_store_rows(oacc, m2, ltot, T.accumulate & 1, orow, lrow, hl);
-    }
+    const int row = unit_row(cur);
+    __bf16* orow = cur.o + (int64_t)b * p.o_sb + (int64_t)cur.head * p.o_sh + (int64_t)row * p.o_ss;
+    float* lrow = cur.lse + (int64_t)b * p.l_sb + (int64_t)cur.head * p.l_sh + row;
+    fwd_store_rows(oacc, m2, ltot, cur.acc, orow, lrow, hl);
     u = un;
     if (u >= u_end) break;
+    cur = nxt;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = qn[ks];
   }

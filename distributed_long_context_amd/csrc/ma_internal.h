@@ -58,30 +58,50 @@ struct FwdParams {
   uint8_t kv_first[MA_MAX_HEADS + 1];  // start of each KV head's run in heads_of
   FwdTile tiles[kFwdTilesPerLaunch];
   // A resident-KV launch from a tile table in device memory (table != nullptr; tiles[] unused):
-  // the table's tiles and workgroup map, the launch's first workgroup in the map, and what the
-  // table's header must hold for the launch to run (the kernel checks it before anything else).
+  // the table's tiles, group entries and workgroup records, the launch's first workgroup record,
+  // and what the table's header must hold for the launch to run (the kernel checks it before
+  // anything else).
   const struct FwdTableHeader* table_header;
   const FwdTile* table;
-  const int32_t* wg_map;
+  const struct FwdResEnt* res_ents;
+  const struct FwdResWg* res_wgs;
   int32_t wg_base;
   int32_t table_ntiles;
+  int32_t table_nents;
   int32_t table_nwgs;
   uint64_t table_hash;
 };
 
 // Tile table in device memory (mesh_attn_tile_fwd_pack / mesh_attn_tile_fwd_tabled): this
-// header, then the resident-KV tiles (FwdTile, in call order), then one int32 per workgroup
-// naming its tile.  hash is FNV-1a (64-bit) over the tiles and the map.
+// header, then the resident-KV tiles (FwdTile, in call order), then the group entries
+// (FwdResEnt), then one record per workgroup (FwdResWg).  Tiles with the same K and V (pointers
+// and length) form a group, whose workgroups share one LDS copy of K/V per (batch, KV head).
+// A tile's units are (32-row block, head slot of the KV head's group of gmax slots), numbered
+// block-major; units are numbered across the whole table, group after group, so each entry's
+// unit0 is larger than the one before.  hash is FNV-1a (64-bit) taken over the tiles, entries
+// and records as 64-bit words.
 constexpr uint32_t kFwdTableMagic = 0x5441424du;  // "MBAT"
 struct FwdTableHeader {
   uint32_t magic;
   int32_t ntiles;
   int32_t nwgs;
-  int32_t reserved;
+  int32_t nents;
   uint64_t hash;
-  uint64_t reserved2;
+  uint64_t reserved;
 };
-static_assert(sizeof(FwdTableHeader) == 32 && sizeof(FwdTile) % 8 == 0, "table layout");
+struct FwdResEnt {
+  int32_t tile;   // index into the table's tiles
+  int32_t unit0;  // the tile's first unit
+};
+struct FwdResWg {
+  int32_t ent;      // the entry holding unit u_begin (the group's K/V are its tile's)
+  int32_t u_begin;  // units [u_begin, u_end) of the group, unit u to wave u % 8
+  int32_t u_end;
+  int32_t bk;       // batch * hkv + KV head
+};
+static_assert(sizeof(FwdTableHeader) == 32 && sizeof(FwdTile) % 8 == 0 && sizeof(FwdResEnt) == 8 &&
+                  sizeof(FwdResWg) == 16,
+              "table layout");
 
 // launchers (return hipError_t as int)
 static_assert(sizeof(FwdParams) <= 4096, "forward parameters exceed the kernel-argument limit");
@@ -91,12 +111,14 @@ constexpr int kFwdSmallBlocks = 16;
 int launch_fwd_bf16(const FwdParams& p, int head_dim, int waves, int total_wgs, void* stream);
 // bf16 forward with the whole K and V of a tile resident in LDS, for unmasked tiles of
 // kFwdResMinKeys<D> < sk <= kFwdResKeys<D> keys; a workgroup of 8 waves runs up to kFwdResUnits
-// units of (32 query rows, query head) of one (tile, batch, KV head)
+// units of (32 query rows, query head) of one (tile, batch, KV head), or from a tile table
+// kFwdResUnits to kFwdResUnitsMax units of a group of tiles sharing K/V
 template <int D>
 constexpr int kFwdResKeys = D == 128 ? 256 : 512;
 template <int D>
 constexpr int kFwdResMinKeys = D == 128 ? 128 : 0;
 constexpr int kFwdResUnits = 32;
+constexpr int kFwdResUnitsMax = 128;
 int launch_fwd_bf16_resident(const FwdParams& p, int head_dim, int total_wgs, void* stream);
 int launch_fwd_f32(const FwdParams& p, int head_dim, int total_wgs, void* stream);
 int launch_fill_empty(void* o, float* lse, int dtype, int batch, int sq, int hq, int head_dim,

@@ -292,37 +292,81 @@ def _table_case(n, sq=210, sk=210, hq=32, hkv=8):
 
 def _parse_table(buf):
     import struct
-    magic, ntiles, nwgs, _, h = struct.unpack_from("<IiiiQ", buf, 0)
+    magic, ntiles, nwgs, nents, h = struct.unpack_from("<IiiiQ", buf, 0)
     tiles = []
     for i in range(ntiles):
         off = 32 + 120 * i  # q, k, v, o, lse, sq, sk, wg_begin, chunks
         tiles.append(struct.unpack_from("<5Q4i", buf, off))
-    wg_map = list(struct.unpack_from(f"<{nwgs}i", buf, 32 + 120 * ntiles))
-    return magic, h, tiles, wg_map
+    off = 32 + 120 * ntiles
+    ents = [struct.unpack_from("<2i", buf, off + 8 * i) for i in range(nents)]  # tile, first unit
+    off += 8 * nents
+    wgs = [struct.unpack_from("<4i", buf, off + 16 * i) for i in range(nwgs)]  # entry, unit range, b*hkv+h
+    return magic, h, tiles, ents, wgs
 
 
 def test_tile_table_layout():
-    # 40 tiles of 210 x 210 at 32/8 heads: 7 row blocks x 4 heads = 28 units, one workgroup chunk per
-    # (KV head), 8 workgroups a tile; a tile of 64 keys (ring kernel) in the middle stays out of the table
+    # 40 tiles of 210 x 210 at 32/8 heads, each with its own K/V: 7 row blocks x 4 heads = 28 units,
+    # one group and one chunk per tile, one workgroup per KV head; a tile of 64 keys (ring kernel)
+    # in the middle stays out of the table
     L = _abi.lib()
     a, t = _table_case(41)
     t[20].sk = 64
     n = L.mesh_attn_tile_fwd_table_bytes(C.byref(a))
-    assert n == 32 + 40 * 120 + 40 * 8 * 4
+    assert n == 32 + 40 * 120 + 40 * 8 + 320 * 16
     buf = (C.c_ubyte * n)()
     assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf, n) == _abi.MA_OK
-    magic, h, tiles, wg_map = _parse_table(bytes(buf))
-    assert magic == 0x5441424D and len(tiles) == 40 and len(wg_map) == 320
+    magic, h, tiles, ents, wgs = _parse_table(bytes(buf))
+    assert magic == 0x5441424D and len(tiles) == 40 and len(wgs) == 320
     resident = [i for i in range(41) if i != 20]
     for k, (i, e) in enumerate(zip(resident, tiles)):
         assert e[:5] == (t[i].q, t[i].k, t[i].v, t[i].o, t[i].lse)
-        assert e[5:] == (210, 210, 8 * k, 1)  # sq, sk, first workgroup in the map, chunks
-    assert wg_map == [w // 8 for w in range(320)]
+        assert e[5:] == (210, 210, 0, 0)  # sq, sk; workgroups come from the records
+    assert ents == [(k, 28 * k) for k in range(40)]
+    assert wgs == [(w // 8, 28 * (w // 8), 28 * (w // 8) + 28, w % 8) for w in range(320)]
     # the hash follows the tiles: another output pointer, another hash
     t[3].o += 1 << 20
     buf2 = (C.c_ubyte * n)()
     assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf2, n) == _abi.MA_OK
     assert _parse_table(bytes(buf2))[1] != h
+
+
+def test_tile_table_groups_tiles_sharing_kv():
+    # tiles 0, 2, 4 share one K/V of 210 keys and tiles 1, 3 another of 200; tile 5 has the first
+    # K/V's pointers but 150 keys (a group of its own).  Groups in (K, V, length) order: [5],
+    # [0, 2, 4], [1, 3]; units ceil(sq / 32) x 4 numbered on across the groups; chunks of 32 units
+    # (small call), each naming the entry that holds its first unit
+    L = _abi.lib()
+    a, t = _table_case(6)
+    ka, kb = t[0].k, t[0].k + (1 << 30)
+    for i, (sq, sk, k) in enumerate([(210, 210, ka), (37, 200, kb), (300, 210, ka), (64, 200, kb), (1, 210, ka),
+                                     (129, 150, ka)]):
+        t[i].sq, t[i].sk, t[i].k, t[i].v = sq, sk, k, k + (1 << 29)
+    n = L.mesh_attn_tile_fwd_table_bytes(C.byref(a))
+    buf = (C.c_ubyte * n)()
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf, n) == _abi.MA_OK
+    _, _, tiles, ents, wgs = _parse_table(bytes(buf))
+    assert len(tiles) == 6
+    assert ents == [(5, 0), (0, 20), (2, 48), (4, 88), (1, 92), (3, 100)]
+    chunks = [(0, 0, 20), (1, 20, 52), (2, 52, 84), (2, 84, 92), (4, 92, 108)]
+    assert wgs == [(e, ub, ue, h) for e, ub, ue in chunks for h in range(8)]
+    assert n == 32 + 6 * 120 + 6 * 8 + 40 * 16
+
+
+def test_tile_table_chunk_size_grows_with_the_call():
+    # two tiles of 65536 rows on one K/V: 2 x 8192 units at 8 KV heads give 64 units a workgroup
+    # (about 2048 workgroups), the second tile's first chunk naming the second entry
+    L = _abi.lib()
+    a, t = _table_case(2, sq=65536)
+    t[1].k, t[1].v = t[0].k, t[0].v
+    t[1].o, t[1].lse = t[0].o + (1 << 34), t[0].lse + (1 << 34)  # 512 MiB of O per tile: no overlap
+    n = L.mesh_attn_tile_fwd_table_bytes(C.byref(a))
+    buf = (C.c_ubyte * n)()
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf, n) == _abi.MA_OK
+    _, _, _, ents, wgs = _parse_table(bytes(buf))
+    assert ents == [(0, 0), (1, 8192)]
+    assert len(wgs) == 256 * 8
+    assert wgs[0] == (0, 0, 64, 0) and wgs[127 * 8 + 7] == (0, 8128, 8192, 7)
+    assert wgs[128 * 8] == (1, 8192, 8256, 0) and wgs[-1] == (1, 16320, 16384, 7)
 
 
 def test_tile_table_calls_reject_bad_buffers_without_launching():

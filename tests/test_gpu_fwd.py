@@ -440,20 +440,23 @@ RESIDENT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("table", [False, True])
 @pytest.mark.parametrize("acc", [False, True])
 @pytest.mark.parametrize("case", range(len(RESIDENT_CASES)))
-def test_fwd_resident_kv_tiles(case, acc):
+def test_fwd_resident_kv_tiles(case, acc, table):
     """Two tiles of one shape in one call, plain or folded into seeded incoming partials; every row
-    of both checked against the oracle."""
+    of both checked against the oracle.  Through the tile table the two tiles share one K/V, so
+    they form one group whose units the workgroups take across the tile boundary."""
     d, sq, sk, hq, hkv, B, head_map = RESIDENT_CASES[case]
-    log(f"[fwd resident kv] d={d} sq={sq} sk={sk} hq={hq} hkv={hkv} B={B} acc={acc}")
+    log(f"[fwd resident kv] d={d} sq={sq} sk={sk} hq={hq} hkv={hkv} B={B} acc={acc} table={table}")
     scale = np.float32(1.0 / math.sqrt(d))
     wid = 2700 + 2 * case + (1 if acc else 0)
     tiles, refs = [], []
     for i in range(2):
         q, qv = gen(wid, synthetic.T_Q, i, (B, sq, hq, d))
-        k, kv = gen(wid, synthetic.T_K, i, (B, sk, hkv, d))
-        v, vv = gen(wid, synthetic.T_V, i, (B, sk, hkv, d))
+        if i == 0 or not table:
+            k, kv = gen(wid, synthetic.T_K, i, (B, sk, hkv, d))
+            v, vv = gen(wid, synthetic.T_V, i, (B, sk, hkv, d))
         O, L = attn_tile(qv, kv, vv, scale, head_map)
         if acc:
             o, ov = gen(wid, synthetic.T_O_IN, i, (B, sq, hq, d))
@@ -466,17 +469,18 @@ def test_fwd_resident_kv_tiles(case, acc):
             lse = torch.full((B, hq, sq), float("nan"), dtype=torch.float32, device=DEV)
         tiles.append(Tile(q, k, v, o, lse))
         refs.append((O, L))
-    ma.mesh_attn_tile_fwd(tiles, float(scale), ma.MA_MASK_NONE, head_map, accumulate=acc)
+    ma.mesh_attn_tile_fwd(tiles, float(scale), ma.MA_MASK_NONE, head_map, accumulate=acc, table=table)
     torch.cuda.synchronize()
     for t, (Oref, Lref) in zip(tiles, refs):
         check_close("O", host_f64(t.o), Oref, BF16_O_TOL, normalised_also=False)
         check_close("LSE", host_f64(t.lse), Lref, BF16_LSE_TOL)
 
 
-def _tile_set(wid, shapes, hq, hkv, d, acc, shared=()):
+def _tile_set(wid, shapes, hq, hkv, d, acc, shared=(), kv_of=None):
     """Tiles of the given (sq, sk) shapes with seeded inputs; with acc, outputs hold seeded incoming
     partials (two identical copies of every output: for the table path and the kernel-argument path).
-    `shared` lists groups of tile indices that name one output (applied in list order)."""
+    `shared` lists groups of tile indices that name one output (applied in list order); kv_of[i],
+    when given, is the tile whose K and V tile i uses (the same tensors; equal sk)."""
     owner = {}
     for grp in shared:
         for i in grp[1:]:
@@ -493,9 +497,14 @@ def _tile_set(wid, shapes, hq, hkv, d, acc, shared=()):
     ins, outs = [], [[], []]
     for i, (sq, sk) in enumerate(shapes):
         q, qv = gen(wid, synthetic.T_Q, i, (1, sq, hq, d))
-        k, kv = gen(wid, synthetic.T_K, i, (1, sk, hkv, d))
-        v, vv = gen(wid, synthetic.T_V, i, (1, sk, hkv, d))
-        ins.append((view(q, sq, "bshd"), view(k, sk, "bshd"), view(v, sk, "bshd"), qv, kv, vv))
+        if kv_of is not None and kv_of[i] != i:
+            j = kv_of[i]
+            assert j < i and shapes[j][1] == sk
+            ins.append((view(q, sq, "bshd"), ins[j][1], ins[j][2], qv, ins[j][4], ins[j][5]))
+        else:
+            k, kv = gen(wid, synthetic.T_K, i, (1, sk, hkv, d))
+            v, vv = gen(wid, synthetic.T_V, i, (1, sk, hkv, d))
+            ins.append((view(q, sq, "bshd"), view(k, sk, "bshd"), view(v, sk, "bshd"), qv, kv, vv))
         for c in range(2):
             if i in owner:
                 outs[c].append(outs[c][owner[i]])
@@ -547,6 +556,36 @@ def test_fwd_tile_table_matches_kernel_arguments(d, acc):
         Oref, Lref = merge(parts) if len(parts) > 1 else parts[0]
         check_close(f"O tile {i}", host_f64(tiles[0][i].o), Oref, BF16_O_TOL, normalised_also=False)
         check_close(f"LSE tile {i}", host_f64(tiles[0][i].lse), Lref, BF16_LSE_TOL)
+
+
+@pytest.mark.parametrize("d,acc", [(128, False), (64, False), (128, True)])
+def test_fwd_tile_table_groups_tiles_sharing_kv(d, acc):
+    """A Mesh-like block: 12 query partitions of ragged lengths against 3 KV partitions (36 tiles,
+    every KV partition shared by 12 tiles), through the tile table, where the tiles of one KV
+    partition form a group and a workgroup runs units of several tiles against one LDS copy of
+    K/V, and through kernel arguments: bitwise equal, and sampled tiles against the oracle."""
+    hq, hkv = 32, 8
+    scale = np.float32(1.0 / math.sqrt(d))
+    sqs = [210, 37, 300, 1, 129, 256, 64, 500, 33, 210, 97, 2000]
+    sks = [210, 256, 150] if d == 128 else [400, 512, 3]
+    shapes, kv_of = [], []
+    for j, sk in enumerate(sks):
+        for i, sq in enumerate(sqs):
+            kv_of.append(len(shapes) if i == 0 else j * len(sqs))
+            shapes.append((sq, sk))
+    log(f"[fwd tile table groups] d={d} acc={acc} tiles={len(shapes)}")
+    ins, outs, tiles = _tile_set(2860 + d + (1 if acc else 0), shapes, hq, hkv, d, acc, kv_of=kv_of)
+    ma.mesh_attn_tile_fwd(tiles[0], float(scale), ma.MA_MASK_NONE, accumulate=acc, table=True)
+    ma.mesh_attn_tile_fwd(tiles[1], float(scale), ma.MA_MASK_NONE, accumulate=acc)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(tiles[0][i].o, tiles[1][i].o) and torch.equal(tiles[0][i].lse, tiles[1][i].lse), i
+    for i in [0, 1, 3, 11, 13, 20, 23, 26, 35]:
+        O, L = attn_tile(ins[i][3], ins[i][4], ins[i][5], scale)
+        if acc:
+            O, L = merge([(outs[0][i][2], outs[0][i][3]), (O, L)])
+        check_close(f"O tile {i}", host_f64(tiles[0][i].o), O, BF16_O_TOL, normalised_also=False)
+        check_close(f"LSE tile {i}", host_f64(tiles[0][i].lse), L, BF16_LSE_TOL)
 
 
 def test_fwd_tile_table_of_other_arguments_is_not_run():
