@@ -38,7 +38,6 @@ namespace ma {
 namespace {
 
 constexpr int kThreads = 256;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // rows of one workgroup: at least one full pass of the 256 threads, and 16
 template <int D, bool BF16>
