@@ -443,17 +443,24 @@ fwd_bf16_kernel(const FwdParams p) {
       if constexpr (decltype(may_mask)::value) half_max(0, 0, sA);
       else half_max_plain(true, sA);
       maybe_rescale();
-      for (int j = 0;; ++j) {
-        const int st = j & 1;
+      // one block in stage ST (a compile-time stage, so every LDS offset is an immediate);
+      // false once the last block is done
+      auto block = [&](auto stage, int j) -> bool {
+        constexpr int st = decltype(stage)::value;
         half_step(may_mask, st, 0, sA, j, st, 1, sB);
         maybe_rescale();
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         half_step(may_mask, st, 1, sB, j + 1, st ^ 1, 0, sA);
         maybe_rescale();
-        if (j + 1 >= nkb) break;
+        if (j + 1 >= nkb) return false;
         __syncthreads();
         if (j + 2 < nkb) issue(st, j + 2);
+        return true;
+      };
+      for (int j = 0;; j += 2) {
+        if (!block(std::integral_constant<int, 0>{}, j)) break;
+        if (!block(std::integral_constant<int, 1>{}, j + 1)) break;
       }
     } else {
     if (0 < nkb) issue(0, 0);
