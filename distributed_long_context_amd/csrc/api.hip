@@ -273,7 +273,9 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
   auto group_span = [&](size_t first, size_t last) -> int64_t {
     std::vector<size_t> idx;
     for (size_t j = first; j < last; ++j) idx.push_back(j);
-    auto key = [&](size_t j) { return std::make_tuple(plan.table[j].k, plan.table[j].v, plan.table[j].sk); };
+    auto key = [&](size_t j) {
+      return std::make_tuple((uintptr_t)plan.table[j].k, (uintptr_t)plan.table[j].v, plan.table[j].sk);
+    };
     std::stable_sort(idx.begin(), idx.end(), [&](size_t x, size_t y) { return key(x) < key(y); });
     auto units_of = [&](size_t j) { return (int64_t)(plan.table[j].sq + 31) / 32 * p.gmax; };
     int64_t total = 0;

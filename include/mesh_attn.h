@@ -183,8 +183,10 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* args, void* stream);
  * tiles of 129-256 keys at d = 128, of at most 512 keys at d = 64) run from a
  * table in device memory, all in one launch (one more wherever a tile names the
  * output of a tile before it), and every other tile as in mesh_attn_tile_fwd.
- * Results, accumulate mode, output ordering and argument checks are those of
- * mesh_attn_tile_fwd on the same arguments, bit for bit.
+ * Tiles with the same K and V (pointers and length), such as the tiles of one
+ * KV partition in a Mesh share ([Mesh] section 3.1), share one copy of K/V per
+ * workgroup.  Results, accumulate mode, output ordering and argument checks are
+ * those of mesh_attn_tile_fwd on the same arguments, bit for bit.
  *
  * mesh_attn_tile_fwd_table_bytes: the table's size for these arguments (at
  *   least 32 bytes; 0 when the arguments are invalid, see mesh_attn_last_error).
@@ -197,7 +199,8 @@ int mesh_attn_tile_fwd(const ma_tile_fwd_args* args, void* stream);
  *   wrote for the same arguments by the time the stream reaches the call, and
  *   unchanged until the launch has run.  The table holds the tiles' device
  *   pointers, so the library checks it in the kernel: its header must carry the
- *   tile count, workgroup count and 64-bit hash planned for these arguments, or
+ *   tile, group-entry and workgroup counts and the 64-bit hash planned for these
+ *   arguments, or
  *   the resident-KV launch returns without reading the tiles or writing any
  *   output (a table packed for other arguments is not run).  Ownership and
  *   errors as in mesh_attn_tile_fwd; the table is the caller's memory.
