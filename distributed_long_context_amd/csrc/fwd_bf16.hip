@@ -115,9 +115,11 @@ __device__ __forceinline__ void fwd_mask_keys(f32x16& s, int key0, int hl, int k
 
 // the row's max over the half, in log2 units (c2 = scale * log2(e))
 __device__ __forceinline__ float fwd_row_max(const f32x16& s, float c2) {
-  float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-  for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+  // a tree of three-input maxima (v_max3_f32): 8 instructions, 3 deep
+  const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float c = fmaxf(fmaxf(s[6], s[7]), s[8]), d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  const float mx = fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
   return xhalf_max(mx) * c2;
 }
 
