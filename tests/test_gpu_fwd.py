@@ -596,6 +596,56 @@ def test_fwd_tile_table_groups_tiles_sharing_kv(d, acc):
         check_close(f"LSE tile {i}", host_f64(tiles[0][i].lse), L, BF16_LSE_TOL)
 
 
+@pytest.mark.parametrize("acc", [False, True])
+def test_fwd_tile_table_under_a_causal_mask(acc):
+    """A causal 6 x 6 block of 210-token partitions (contiguous positions): the 15 tiles below the
+    diagonal are FULL and run from the tile table (groups of up to five tiles per KV partition),
+    the 6 diagonal tiles are PARTIAL and run the masked kernel from kernel arguments, the 15 above
+    are EMPTY (filled with (0, -inf), or left as they are with accumulate).  The tabled call must
+    equal the kernel-argument call bitwise; sampled tiles of each class against the oracle."""
+    hq, hkv, d, P, n = 32, 8, 128, 210, 6
+    scale = np.float32(1.0 / math.sqrt(d))
+    wid = 2870 + (1 if acc else 0)
+    log(f"[fwd tile table causal] acc={acc}")
+    qs = [gen(wid, synthetic.T_Q, i, (1, P, hq, d)) for i in range(n)]
+    ks = [gen(wid, synthetic.T_K, j, (1, P, hkv, d)) for j in range(n)]
+    vs = [gen(wid, synthetic.T_V, j, (1, P, hkv, d)) for j in range(n)]
+    pos = [Pos([(0, i * P, 1)]) for i in range(n)]
+    tiles, incoming = [[], []], {}
+    for i in range(n):
+        for j in range(n):
+            for c in range(2):
+                if acc:
+                    o, ov = gen(wid, synthetic.T_O_IN, i * n + j, (1, P, hq, d))
+                    li = (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i * n + j, (1, hq, P)) +
+                          np.float32(math.log(P))).astype(np.float32)
+                    incoming[(i, j)] = (ov, li.astype(np.float64))
+                    lse = torch.from_numpy(li).to(DEV)
+                else:
+                    o = torch.full((1, P, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+                    lse = torch.full((1, hq, P), float("nan"), dtype=torch.float32, device=DEV)
+                tiles[c].append(Tile(qs[i][0], ks[j][0], vs[j][0], o, lse, q_pos=pos[i], k_pos=pos[j]))
+    ma.mesh_attn_tile_fwd(tiles[0], float(scale), ma.MA_MASK_CAUSAL, accumulate=acc, table=True)
+    ma.mesh_attn_tile_fwd(tiles[1], float(scale), ma.MA_MASK_CAUSAL, accumulate=acc)
+    torch.cuda.synchronize()
+    for t0, t1 in zip(tiles[0], tiles[1]):
+        assert torch.equal(t0.o, t1.o) and torch.equal(t0.lse, t1.lse)
+    for i, j in [(1, 0), (5, 2), (3, 3), (0, 0), (2, 4)]:  # FULL, FULL, PARTIAL, PARTIAL, EMPTY
+        t = tiles[0][i * n + j]
+        if j > i:  # no allowed pair
+            if acc:
+                O, L = incoming[(i, j)]
+            else:
+                O, L = np.zeros((1, P, hq, d)), np.full((1, hq, P), -np.inf)
+        else:
+            O, L = attn_tile(qs[i][1], ks[j][1], vs[j][1], scale, None, True,
+                             positions(pos[i], P), positions(pos[j], P))
+            if acc:
+                O, L = merge([incoming[(i, j)], (O, L)])
+        check_close(f"O tile ({i},{j})", host_f64(t.o), O, BF16_O_TOL, normalised_also=False)
+        check_close(f"LSE tile ({i},{j})", host_f64(t.lse), L, BF16_LSE_TOL)
+
+
 def test_fwd_tile_table_of_other_arguments_is_not_run():
     """A device table packed for one set of tiles, handed to the call of another set of the same
     shapes: the resident-KV launch finds the header's hash different and writes nothing (the
