@@ -260,3 +260,86 @@ def test_random_head_major_layout(seed):
     check_grad("dQ", dq, dq_r)
     check_grad("dK", dk, dk_r)
     check_grad("dV", dv, dv_r)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_tile_table(seed):
+    """A random Mesh-like call through the tile table and through kernel arguments: query and KV
+    partitions of random lengths (mostly in the resident-KV range, some outside it), a random
+    subset of their pairs, batch, GQA map (sometimes an irregular explicit one) and head dim; with
+    accumulate every tile folds into its query partition's output, otherwise each tile has its
+    own.  The two calls must agree bitwise; sampled outputs against the oracle."""
+    rng = random.Random(9100 + seed)
+    d = rng.choice([64, 128])
+    hkv = rng.choice([1, 2, 4, 8])
+    hq = hkv * rng.choice([1, 2, 4])
+    hm = None
+    if rng.random() < 0.3:
+        hm = [rng.randrange(hkv) for _ in range(hq)]
+    B = rng.choice([1, 1, 2])
+    acc = rng.random() < 0.5
+    lo, hi = (129, 256) if d == 128 else (1, 512)
+    nq, nk = rng.randint(1, 6), rng.randint(1, 4)
+    sqs = [rng.randint(1, 300) for _ in range(nq)]
+    sks = [rng.randint(lo, hi) if rng.random() < 0.8 else rng.choice([64, 600]) for _ in range(nk)]
+    pairs = [(i, j) for i in range(nq) for j in range(nk) if rng.random() < 0.8] or [(0, 0)]
+    rng.shuffle(pairs)
+    log(f"[random tile table {seed}] d={d} hq={hq} hkv={hkv} map={hm} B={B} acc={acc} sq={sqs} sk={sks} "
+        f"pairs={len(pairs)}")
+    wid = 9200 + seed
+    scale = np.float32(1.0 / math.sqrt(d))
+    smax = max(sqs + sks)
+
+    def view(t, n, kind):  # every tensor a prefix of a buffer smax long: one set of strides per call
+        shape = (B, smax, t.shape[2], t.shape[3]) if kind == "bshd" else (B, t.shape[1], smax)
+        buf = torch.full(shape, float("nan"), dtype=t.dtype, device=DEV)
+        out = buf[:, :n] if kind == "bshd" else buf[:, :, :n]
+        out.copy_(t)
+        return out
+
+    def drawn(tensor, i, n, h):
+        dev, host = gen(wid, tensor, i, (B, n, h, d))
+        return view(dev, n, "bshd"), host
+
+    qs = [drawn(synthetic.T_Q, i, sqs[i], hq) for i in range(nq)]
+    ks = [drawn(synthetic.T_K, j, sks[j], hkv) for j in range(nk)]
+    vs = [drawn(synthetic.T_V, j, sks[j], hkv) for j in range(nk)]
+
+    def outputs():
+        if acc:  # one (O, LSE) per query partition, starting from a seeded incoming partial
+            outs = []
+            for i in range(nq):
+                o, _ = drawn(synthetic.T_O_IN, i, sqs[i], hq)
+                li = synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (B, hq, sqs[i])) + np.float32(4)
+                outs.append((o, view(torch.from_numpy(li.astype(np.float32)).to(DEV), sqs[i], "bhs")))
+            return [outs[i] for i, _ in pairs]
+        nan = float("nan")
+        return [(view(torch.full((B, sqs[i], hq, d), nan, dtype=torch.bfloat16, device=DEV), sqs[i], "bshd"),
+                 view(torch.full((B, hq, sqs[i]), nan, dtype=torch.float32, device=DEV), sqs[i], "bhs"))
+                for i, _ in pairs]
+
+    runs = []
+    for table in (True, False):
+        outs = outputs()
+        tiles = [Tile(qs[i][0], ks[j][0], vs[j][0], o, lse) for (i, j), (o, lse) in zip(pairs, outs)]
+        ma.mesh_attn_tile_fwd(tiles, float(scale), ma.MA_MASK_NONE, hm, accumulate=acc, table=table)
+        runs.append(outs)
+    torch.cuda.synchronize()
+    for (o0, l0), (o1, l1) in zip(*runs):
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    if acc:
+        i = pairs[0][0]
+        parts = [(gen(wid, synthetic.T_O_IN, i, (B, sqs[i], hq, d))[1],
+                  (synthetic.normal_f32(wid, synthetic.T_LSE_IN, i, (B, hq, sqs[i])) + np.float32(4)).astype(
+                      np.float64))]
+        parts += [attn_tile(qs[i][1], ks[j][1], vs[j][1], scale, hm) for ii, j in pairs if ii == i]
+        O, L = merge(parts)
+        o, lse = runs[0][pairs.index(next(p for p in pairs if p[0] == i))]
+        check_close("O", host_f64(o), O, BF16_O_TOL, normalised_also=False)
+        check_close("LSE", host_f64(lse), L, BF16_LSE_TOL)
+    else:
+        for t in rng.sample(range(len(pairs)), min(2, len(pairs))):
+            i, j = pairs[t]
+            O, L = attn_tile(qs[i][1], ks[j][1], vs[j][1], scale, hm)
+            check_close(f"O pair {pairs[t]}", host_f64(runs[0][t][0]), O, BF16_O_TOL, normalised_also=False)
+            check_close(f"LSE pair {pairs[t]}", host_f64(runs[0][t][1]), L, BF16_LSE_TOL)
