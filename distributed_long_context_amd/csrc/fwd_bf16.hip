@@ -51,7 +51,8 @@
 //    and a two-stage ring (tiles of at most 16 key blocks, two workgroups per CU),
 //    and a resident-KV kernel for unmasked tiles of a few hundred keys, whose
 //    workgroup holds the tile's whole K and V in LDS and runs up to 32 units of
-//    32 query rows against it (see its own comment below).
+//    32 query rows against it, or from a tile table up to 128 units of the tiles
+//    that share that K and V (see its own comment below).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <type_traits>
