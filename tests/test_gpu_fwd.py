@@ -646,6 +646,24 @@ def test_fwd_tile_table_under_a_causal_mask(acc):
         check_close(f"LSE tile ({i},{j})", host_f64(t.lse), L, BF16_LSE_TOL)
 
 
+def test_fwd_tile_table_with_no_resident_tile():
+    """A tabled call whose tiles are all outside the resident-KV class (the table holds only its
+    header): the same launches as mesh_attn_tile_fwd, bitwise."""
+    hq, hkv, d = 32, 8, 128
+    scale = np.float32(1.0 / math.sqrt(d))
+    shapes = [(300, 600), (64, 1000), (1, 64), (210, 840)]
+    log("[fwd tile table] no resident tile")
+    _, _, tiles = _tile_set(2880, shapes, hq, hkv, d, False)
+    prep = ma.prepare_tile_fwd(tiles[0], float(scale), ma.MA_MASK_NONE, table=True)
+    assert prep[3][2] == 32  # the header only
+    ma.launch_prepared_tile_fwd(prep)
+    ma.mesh_attn_tile_fwd(tiles[1], float(scale), ma.MA_MASK_NONE)
+    torch.cuda.synchronize()
+    for t0, t1 in zip(tiles[0], tiles[1]):
+        assert torch.equal(t0.o, t1.o) and torch.equal(t0.lse, t1.lse)
+        assert not torch.isnan(t0.o.float()).any()
+
+
 def test_fwd_tile_table_of_other_arguments_is_not_run():
     """A device table packed for one set of tiles, handed to the call of another set of the same
     shapes: the resident-KV launch finds the header's hash different and writes nothing (the
