@@ -369,6 +369,33 @@ def test_tile_table_chunk_size_grows_with_the_call():
     assert wgs[128 * 8] == (1, 8192, 8256, 0) and wgs[-1] == (1, 16320, 16384, 7)
 
 
+@pytest.mark.parametrize("d,sks,resident", [
+    (128, [128, 129, 256, 257], [False, True, True, False]),  # 129-256 keys at d = 128
+    (64, [1, 512, 513], [True, True, False]),                  # 1-512 keys at d = 64
+])
+def test_tile_table_takes_the_resident_class_only(d, sks, resident):
+    # the table holds exactly the unmasked bf16 tiles of the resident-KV key range, in call order
+    L = _abi.lib()
+    n = len(sks)
+    a, t = _table_case(n)
+    a.head_dim = d
+    row, krow = 32 * d, 8 * d
+    a.q_stride[:] = a.o_stride[:] = (210 * row, row, d)
+    a.k_stride[:] = a.v_stride[:] = (600 * krow, krow, d)
+    for i, sk in enumerate(sks):
+        t[i].sk = sk
+    nb = L.mesh_attn_tile_fwd_table_bytes(C.byref(a))
+    buf = (C.c_ubyte * nb)()
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf, nb) == _abi.MA_OK
+    _, _, tiles, ents, wgs = _parse_table(bytes(buf))
+    assert [e[0] for e in tiles] == [t[i].q for i in range(n) if resident[i]]
+    assert len(ents) == sum(resident)
+    # fp32 tiles never use the resident-KV kernel: the table is its header
+    a.dtype = _abi.MA_F32
+    a.q_stride[:] = a.o_stride[:] = (210 * row, row, d)
+    assert L.mesh_attn_tile_fwd_table_bytes(C.byref(a)) == 32
+
+
 def test_tile_table_calls_reject_bad_buffers_without_launching():
     L = _abi.lib()
     a, _ = _table_case(3)
