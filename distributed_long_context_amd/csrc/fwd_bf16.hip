@@ -741,13 +741,15 @@ fwd_bf16_resident_kernel(const FwdParams p) {
       mb2 = -INFINITY;
       return;
     }
-    __builtin_amdgcn_s_setprio(1);  // as in the ring kernel's step (measured 1.3% faster here)
+    // as in the ring kernel's step, with many units per workgroup (the table instance: measured
+    // 1.3% faster; with the few units of a kernel-argument workgroup 5% slower, so not there)
+    if constexpr (TABLE) __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_iglp_opt(0);
     bf16x8 pf[2];
     fwd_probs(sc, c2, m2, lsum, pf);
     if (nxt) s_half(nkb_, nkb2, sn);
     fwd_pv<D>(vaddr, kb * kBlockBytes + kb2 * 32 * D * 2, pf, oacc);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (TABLE) __builtin_amdgcn_s_setprio(0);
     if (nxt) half_max(nkb_, nkb2, sn, may_mask);
     else mb2 = -INFINITY;
   };
