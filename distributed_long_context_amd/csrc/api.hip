@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <mutex>
 #include <tuple>
+#include <unordered_set>
 #include <utility>
 
 #include "mesh_attn.h"
@@ -263,6 +264,9 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
   }
   size_t tab_first = 0;  // first table tile of the resident span being filled
   int64_t tab_units = 0;  // units of the table's tiles so far
+  // outputs (O and LSE addresses) of the resident span being filled: a set, so that a call of
+  // thousands of tiles checks each new tile in constant time
+  std::unordered_set<uintptr_t> tab_o, tab_lse;
   // Groups the span's tiles by K/V (pointers and length: one LDS copy serves them all) and writes
   // each group's entries (its tiles, units numbered on from plan.units) and workgroup records:
   // per chunk of `cap` consecutive units of the group, one workgroup per (batch, KV head), the KV
@@ -311,6 +315,8 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
       bp[m].wg_base = (int32_t)plan.wgs.size();
       bwg[m] = (int)group_span(tab_first, plan.table.size());
       tab_first = plan.table.size();
+      tab_o.clear();
+      tab_lse.clear();
     }
     launches.push_back(FwdPlan::Launch{m, bwg[m], (int)batches.size()});
     batches.push_back(bp[m]);
@@ -327,8 +333,7 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
     for (int k = 0; k < kClasses; ++k)
       for (int j = 0; j < bn[k] && !(use_table && k == kResident); ++j)
         dup = dup || bp[k].tiles[j].o == pcs[0].o || bp[k].tiles[j].lse == pcs[0].lse;
-    for (size_t j = tab_first; j < plan.table.size(); ++j)
-      dup = dup || plan.table[j].o == pcs[0].o || plan.table[j].lse == pcs[0].lse;
+    dup = dup || tab_o.count((uintptr_t)pcs[0].o) || tab_lse.count((uintptr_t)pcs[0].lse);
     if (dup) flush_all();
     int64_t blocks = 0;
     for (int i = 0; i < npcs; ++i) blocks += (pcs[i].sk + 63) / 64;
@@ -381,6 +386,8 @@ int plan_fwd(const ma_tile_fwd_args* a, bool use_table, FwdPlan& plan) {
       ft.wg_begin = 0;
       ft.chunks = 0;
       plan.table.push_back(ft);
+      tab_o.insert((uintptr_t)t.o);
+      tab_lse.insert((uintptr_t)t.lse);
       tab_units += (t.sq + 31) / 32 * p.gmax;
       bwg[m] += (int)wgs;
       ++bn[m];
