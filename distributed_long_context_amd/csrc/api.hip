@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <mutex>
 #include <tuple>
+#include <unordered_map>
 #include <unordered_set>
 #include <utility>
 
@@ -670,14 +671,15 @@ BwdGroups bwd_groups(const ma_tile_bwd_args* a) {
   BwdGroups g;
   g.q_of.assign(a->ntiles, -1);
   g.kv_of.assign(a->ntiles, -1);
+  std::unordered_map<uintptr_t, int> q_group, kv_group;  // dq / dk address -> group
   for (int i = 0; i < a->ntiles; ++i) {
-    for (int j = 0; j < i; ++j)
-      if (a->tiles[j].dq == a->tiles[i].dq) { g.q_of[i] = g.q_of[j]; break; }
-    if (g.q_of[i] < 0) { g.q_of[i] = (int)g.qg.size(); g.qg.emplace_back(); }
+    const auto q = q_group.emplace((uintptr_t)a->tiles[i].dq, (int)g.qg.size());
+    if (q.second) g.qg.emplace_back();
+    g.q_of[i] = q.first->second;
     g.qg[g.q_of[i]].push_back(i);
-    for (int j = 0; j < i; ++j)
-      if (a->tiles[j].dk == a->tiles[i].dk) { g.kv_of[i] = g.kv_of[j]; break; }
-    if (g.kv_of[i] < 0) { g.kv_of[i] = (int)g.kvg.size(); g.kvg.emplace_back(); }
+    const auto kv = kv_group.emplace((uintptr_t)a->tiles[i].dk, (int)g.kvg.size());
+    if (kv.second) g.kvg.emplace_back();
+    g.kv_of[i] = kv.first->second;
     g.kvg[g.kv_of[i]].push_back(i);
   }
   return g;
@@ -736,6 +738,7 @@ int validate_bwd(const ma_tile_bwd_args* a) {
     return set_error(MA_ERR_INVALID, "strides must be >= 0 and multiples of 16 bytes");
   if (a->q_stride[1] >= (1 << 24) || a->k_stride[1] >= (1 << 24))
     return set_error(MA_ERR_UNSUPPORTED, "Q/K/V sequence strides must be below 2^24 elements");
+  std::unordered_map<uintptr_t, int> kv_first, q_first;  // output address -> first tile naming it
   for (int i = 0; i < a->ntiles; ++i) {
     const ma_bwd_tile& t = a->tiles[i];
     if (!t.q || !t.k || !t.v || !t.o || !t.dout || !t.lse || !t.dq || !t.dk || !t.dv)
@@ -747,18 +750,29 @@ int validate_bwd(const ma_tile_bwd_args* a) {
       return set_error(MA_ERR_INVALID, "tile sizes must be in [1, 2^31-1)");
     rc = check_positions(a->mask_mode, t.q_pos, t.sq, t.k_pos, t.sk);
     if (rc) return rc;
-    for (int j = 0; j < i; ++j) {
-      const ma_bwd_tile& u = a->tiles[j];
-      // tiles sharing dk or dv must share the whole KV description
-      if ((u.dk == t.dk || u.dv == t.dv || u.dk == t.dv || u.dv == t.dk) &&
-          (u.dk != t.dk || u.dv != t.dv || u.k != t.k || u.v != t.v || u.sk != t.sk ||
-           (a->mask_mode != MA_MASK_NONE && std::memcmp(&u.k_pos, &t.k_pos, sizeof(ma_pos)) != 0)))
+    // Tiles sharing dk or dv must share the whole KV description, and tiles sharing dq the whole
+    // Q description.  Each tile is compared with the first tile that named the same address (the
+    // tiles before it that named it were all found equal to that one), found through hash maps so
+    // that a call of thousands of tiles is checked in linear time.
+    const auto kv_same_as = [&](const ma_bwd_tile& u) {
+      return u.dk == t.dk && u.dv == t.dv && u.k == t.k && u.v == t.v && u.sk == t.sk &&
+             (a->mask_mode == MA_MASK_NONE || std::memcmp(&u.k_pos, &t.k_pos, sizeof(ma_pos)) == 0);
+    };
+    for (const void* addr : {(const void*)t.dk, (const void*)t.dv}) {
+      const auto it = kv_first.find((uintptr_t)addr);
+      if (it != kv_first.end() && !kv_same_as(a->tiles[it->second]))
         return set_error(MA_ERR_INVALID, "tiles naming the same dk/dv must name the same k, v, sk and k_pos");
-      // tiles sharing dq must share the whole Q description
-      if (u.dq == t.dq &&
-          (u.q != t.q || u.o != t.o || u.dout != t.dout || u.lse != t.lse || u.sq != t.sq ||
-           (a->mask_mode != MA_MASK_NONE && std::memcmp(&u.q_pos, &t.q_pos, sizeof(ma_pos)) != 0)))
+    }
+    kv_first.emplace((uintptr_t)t.dk, i);
+    kv_first.emplace((uintptr_t)t.dv, i);
+    const auto qit = q_first.find((uintptr_t)t.dq);
+    if (qit != q_first.end()) {
+      const ma_bwd_tile& u = a->tiles[qit->second];
+      if (u.q != t.q || u.o != t.o || u.dout != t.dout || u.lse != t.lse || u.sq != t.sq ||
+          (a->mask_mode != MA_MASK_NONE && std::memcmp(&u.q_pos, &t.q_pos, sizeof(ma_pos)) != 0))
         return set_error(MA_ERR_INVALID, "tiles naming the same dq must name the same q, o, dout, lse, sq and q_pos");
+    } else {
+      q_first.emplace((uintptr_t)t.dq, i);
     }
   }
   rc = check_shifted_outputs(a->ntiles, [&](int i) { return (const void*)a->tiles[i].dq; },

@@ -242,6 +242,69 @@ def test_bwd_rejects_shifted_gradient_outputs():
     assert L.mesh_attn_tile_bwd_noalloc(C.byref(a), None) == _abi.MA_ERR_INVALID
 
 
+def test_bwd_tiles_sharing_an_output_must_share_its_description():
+    # A zero-byte workspace: a call that passes every argument check stops at the workspace check,
+    # before anything is enqueued, so "workspace" in the error means the tiles were accepted.
+    L = _abi.lib()
+
+    def verdict(t, n, mask=_abi.MA_MASK_NONE):
+        a = _bwd_args_c(t, n, mask=mask)
+        rc = L.mesh_attn_tile_bwd(C.byref(a), None, 0, None)
+        assert rc == _abi.MA_ERR_INVALID
+        return L.mesh_attn_last_error()
+
+    def share_kv(t, i, j):
+        t[i].k, t[i].v, t[i].dk, t[i].dv, t[i].sk = t[j].k, t[j].v, t[j].dk, t[j].dv, t[j].sk
+
+    def share_q(t, i, j):
+        t[i].q, t[i].o, t[i].dout, t[i].lse, t[i].dq, t[i].sq = t[j].q, t[j].o, t[j].dout, t[j].lse, t[j].dq, t[j].sq
+
+    n = 6
+    t = _bwd_tiles(n)
+    share_kv(t, 3, 1)
+    share_kv(t, 5, 1)
+    share_q(t, 4, 0)
+    share_q(t, 2, 0)
+    assert b"workspace" in verdict(t, n)
+    for field in ("k", "v", "sk"):  # a third tile on the same dk/dv with another KV description
+        t = _bwd_tiles(n)
+        share_kv(t, 3, 1)
+        share_kv(t, 5, 1)
+        setattr(t[5], field, getattr(t[5], field) + 128)
+        assert b"dk/dv" in verdict(t, n), field
+    t = _bwd_tiles(n)
+    t[4].dv = t[2].dk  # one tile's dv is another's dk
+    assert b"dk/dv" in verdict(t, n)
+    t = _bwd_tiles(n)
+    t[4].dk = t[2].dv
+    assert b"dk/dv" in verdict(t, n)
+    t = _bwd_tiles(n)
+    t[4].dk = t[4].dv = t[2].dk = t[2].dv  # both name one buffer for dk and dv, with another k
+    assert b"dk/dv" in verdict(t, n)
+    t = _bwd_tiles(n)
+    share_kv(t, 4, 2)
+    t[4].dk, t[4].dv = t[4].dk, t[0].dv  # same dk, another dv
+    assert b"dk/dv" in verdict(t, n)
+    for field in ("q", "o", "dout", "lse", "sq"):
+        t = _bwd_tiles(n)
+        share_q(t, 4, 0)
+        share_q(t, 2, 0)
+        setattr(t[4], field, getattr(t[4], field) + (1 if field == "sq" else 256))
+        assert b"same dq" in verdict(t, n), field
+    # positions count only under a mask
+    t = _bwd_tiles(n)
+    share_q(t, 4, 0)
+    share_kv(t, 5, 1)
+    t[4].q_pos.seg[0].global_begin = 64
+    t[5].k_pos.seg[0].global_begin = 64
+    assert b"workspace" in verdict(t, n)
+    assert b"same dq" in verdict(t, n, mask=_abi.MA_MASK_CAUSAL)
+    t[4].q_pos.seg[0].global_begin = 0
+    assert b"dk/dv" in verdict(t, n, mask=_abi.MA_MASK_CAUSAL)
+    t[5].k_pos.seg[0].global_begin = 0
+    assert b"workspace" in verdict(t, n, mask=_abi.MA_MASK_CAUSAL)
+
+
 def test_bwd_workspace_size_rejects_bad_segments():
     # under a mask the segments are expanded: a position map with more than MA_MAX_SEGMENTS
     # segments (or a bad stride) gives 0 instead of being read past its end
