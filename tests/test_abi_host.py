@@ -459,6 +459,71 @@ def test_tile_table_takes_the_resident_class_only(d, sks, resident):
     assert L.mesh_attn_tile_fwd_table_bytes(C.byref(a)) == 32
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_tile_table_covers_every_unit_once(seed):
+    # Random calls: tiles of random lengths on a few shared K/V buffers, some outside the resident
+    # class.  Whatever the grouping and chunking, the table must hold the resident tiles in call
+    # order, number each group's units on from the previous group, and give every (batch, KV head)
+    # each unit of every tile exactly once, in workgroups that stay inside one group and name the
+    # entry holding their first unit.
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    L = _abi.lib()
+    hq, hkv = [(32, 8), (8, 8), (16, 2), (4, 1)][seed % 4]
+    batch = 1 + seed % 2
+    gmax = hq // hkv
+    n = int(rng.integers(1, 48))
+    nkv = int(rng.integers(1, 6))
+    a, t = _table_case(n, hq=hq, hkv=hkv)
+    a.batch = batch
+    smax = 700 if seed < 9 else 60000  # long tiles: chunks of up to 128 units
+    row = hq * 128
+    a.q_stride[:] = a.o_stride[:] = (smax * row, row, 128)
+    a.k_stride[:] = a.v_stride[:] = (smax * hkv * 128, hkv * 128, 128)
+    a.lse_stride[:] = (hq * smax, smax)
+    kv_base = [(1 << 40) + j * (1 << 32) for j in range(nkv)]
+    for i in range(n):
+        j = int(rng.integers(nkv))
+        t[i].k, t[i].v = kv_base[j], kv_base[j] + (1 << 31)
+        t[i].sq = int(rng.integers(1, smax + 1))
+        t[i].sk = int(rng.choice([64, 100, 129, 200, 210, 256, 257, 600])) if rng.random() < 0.3 else 210
+        t[i].o, t[i].lse = (1 << 44) + i * (1 << 30), (1 << 45) + i * (1 << 30)
+    nb = L.mesh_attn_tile_fwd_table_bytes(C.byref(a))
+    assert nb >= 32
+    buf = (C.c_ubyte * nb)()
+    assert L.mesh_attn_tile_fwd_pack(C.byref(a), buf, nb) == _abi.MA_OK
+    magic, _, tiles, ents, wgs = _parse_table(bytes(buf))
+    assert magic == 0x5441424D
+    resident = [i for i in range(n) if 128 < t[i].sk <= 256]
+    assert [e[0] for e in tiles] == [t[i].q for i in resident]
+    assert nb == 32 + 120 * len(tiles) + 8 * len(ents) + 16 * len(wgs)
+    # entries: every table tile once, units numbered on without gaps, groups contiguous
+    assert sorted(e[0] for e in ents) == list(range(len(tiles)))
+    key = lambda e: (tiles[e[0]][1], tiles[e[0]][2], tiles[e[0]][6])  # k, v, sk
+    unit = 0
+    for k, e in enumerate(ents):
+        assert e[1] == unit
+        unit += (tiles[e[0]][5] + 31) // 32 * gmax
+        if k and key(ents[k - 1]) != key(e):
+            assert key(e) not in {key(x) for x in ents[:k]}, "a group split in two"
+    total = unit
+    group_end = {}
+    for k, e in enumerate(ents):
+        nxt = [x[1] for x in ents[k + 1:] if key(x) != key(e)]
+        group_end[k] = nxt[0] if nxt else total
+    # workgroups: per (batch, KV head) a partition of [0, total) into ranges of at most 128 units
+    seen = {bk: [] for bk in range(batch * hkv)}
+    for ent, ub, ue, bk in wgs:
+        assert 0 <= bk < batch * hkv and 0 <= ub < ue <= ub + 128
+        assert ents[ent][1] <= ub and (ent + 1 == len(ents) or ents[ent + 1][1] > ub)
+        assert ue <= group_end[ent], "a workgroup crosses into another group"
+        seen[bk].append((ub, ue))
+    for bk, ranges in seen.items():
+        ranges.sort()
+        assert [r[0] for r in ranges] == [0] + [r[1] for r in ranges[:-1]], bk
+        assert (ranges[-1][1] if ranges else 0) == total
+
+
 def test_tile_table_calls_reject_bad_buffers_without_launching():
     L = _abi.lib()
     a, _ = _table_case(3)
