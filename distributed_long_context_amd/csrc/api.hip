@@ -861,12 +861,17 @@ int run_bwd(const ma_tile_bwd_args* a, void* workspace, void* stream) {
     // kind 0: unmasked; 1: masked
     struct Piece { int group; std::vector<int> partners; int accumulate; int kind; };
     std::vector<Piece> pieces;
+    // (partner group, kind) -> the last own group that listed it: partners listed once, in the
+    // order the group's tiles name them, in time linear in the tile count
+    std::vector<int> listed(2 * (dq_side ? grp.kvg.size() : grp.qg.size()), -1);
     for (int gi = 0; gi < (int)own.size(); ++gi) {
       std::vector<int> full, other;  // partner groups of FULL pairs; of PARTIAL or EMPTY pairs
       for (int ti : own[gi]) {
         const int pg = dq_side ? grp.kv_of[ti] : grp.q_of[ti];
-        auto& lst = tile_cls[ti] == MA_TILE_FULL ? full : other;
-        if (std::find(lst.begin(), lst.end(), pg) == lst.end()) lst.push_back(pg);
+        const int kind = tile_cls[ti] == MA_TILE_FULL ? 0 : 1;
+        if (listed[2 * pg + kind] == gi) continue;
+        listed[2 * pg + kind] = gi;
+        (kind == 0 ? full : other).push_back(pg);
       }
       bool first = true;
       for (int kind = 0; kind < 2; ++kind) {
@@ -882,21 +887,23 @@ int run_bwd(const ma_tile_bwd_args* a, void* workspace, void* stream) {
         }
       }
     }
+    // A group's pieces are consecutive in `pieces`; next_of[g] is the first of group g's pieces
+    // that has not run (none: pieces.size()), the only one of them that may join a launch.
     std::vector<bool> done(pieces.size(), false);
-    size_t remaining = pieces.size();
+    std::vector<size_t> next_of(own.size(), pieces.size());
+    for (size_t pi = pieces.size(); pi-- > 0;) next_of[pieces[pi].group] = pi;
+    size_t remaining = pieces.size(), first_open = 0;  // pieces before first_open have all run
     while (remaining > 0) {
       BwdParams p = base;
       std::vector<int> own_tab, part_tab, groups_in;
       int ne = 0, wg = 0, kind = -1;  // kind: mask kind of this launch, set by its first piece
-      for (size_t pi = 0; pi < pieces.size() && ne < kBwdPerLaunch; ++pi) {
+      while (done[first_open]) ++first_open;
+      for (size_t pi = first_open; pi < pieces.size() && ne < kBwdPerLaunch; ++pi) {
         if (done[pi]) continue;
         const Piece& pc = pieces[pi];
         if (std::find(groups_in.begin(), groups_in.end(), pc.group) != groups_in.end()) continue;
         // earlier pieces of this group must have run in an earlier launch
-        bool earlier_pending = false;
-        for (size_t pj = 0; pj < pi; ++pj)
-          if (!done[pj] && pieces[pj].group == pc.group) earlier_pending = true;
-        if (earlier_pending) continue;
+        if (next_of[pc.group] != pi) continue;
         if (kind >= 0 && kind != pc.kind) continue;
         std::vector<int> new_part = part_tab;
         for (int x : pc.partners)
@@ -927,6 +934,7 @@ int run_bwd(const ma_tile_bwd_args* a, void* workspace, void* stream) {
         wg += (int)wgs;
         ++ne;
         done[pi] = true;
+        next_of[pc.group] = pi + 1 < pieces.size() && pieces[pi + 1].group == pc.group ? pi + 1 : pieces.size();
         --remaining;
       }
       p.nentries = ne;
