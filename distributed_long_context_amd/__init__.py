@@ -49,8 +49,16 @@ class Pos:
         return f"Pos({self.segments})"
 
 
+_CONTIGUOUS_FROM_0 = None  # the ma_pos of a tile without positions (one segment from 0), built once
+
+
 def _pos_c(pos: Optional[Pos]) -> _abi.ma_pos:
-    return pos.to_c() if pos is not None else Pos([(0, 0, 1)]).to_c()
+    global _CONTIGUOUS_FROM_0
+    if pos is not None:
+        return pos.to_c()
+    if _CONTIGUOUS_FROM_0 is None:
+        _CONTIGUOUS_FROM_0 = Pos([(0, 0, 1)]).to_c()
+    return _CONTIGUOUS_FROM_0  # ctypes copies a structure on assignment into a tile record
 
 
 # ------------------------------------------------------------ tensor checks --
@@ -260,33 +268,45 @@ def _bwd_args(tiles, scale, mask_mode, head_map, accumulate):
     t0 = tiles[0]
     B, _, Hq, d = t0.q.shape
     Hkv = t0.k.shape[2]
+    bf16, f32 = torch.bfloat16, torch.float32
+    # tile 0's head/dim extents and strides, which every tile must share (read once)
+    q_tail, k_tail = t0.q.shape[2:], t0.k.shape[2:]
+    q_st, k_st = t0.q.stride()[:3], t0.k.stride()[:3]
+    dq_st, dk_st, l_st = t0.dq.stride()[:3], t0.dk.stride()[:3], t0.lse.stride()[:2]
+
+    def dev4(x, name):  # a device tensor with a contiguous last axis; its first three strides
+        if not x.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        st = x.stride()
+        if st[-1] != 1:
+            raise ValueError(f"{name}: last axis must be contiguous")
+        return st[:3]
+
     arr = (_abi.ma_bwd_tile * len(tiles))()
     for i, t in enumerate(tiles):
-        for name, x, ref in (("q", t.q, t0.q), ("o", t.o, t0.q), ("dout", t.dout, t0.q)):
-            if x.dtype != torch.bfloat16 or x.dim() != 4 or x.shape[0] != B or x.shape[2:] != t0.q.shape[2:] \
-                    or x.shape[1] != t.q.shape[1] or x.stride()[:3] != ref.stride()[:3]:
+        sq, sk = t.q.shape[1], t.k.shape[1]
+        for name, x in (("q", t.q), ("o", t.o), ("dout", t.dout)):
+            shp = x.shape
+            if x.dtype != bf16 or len(shp) != 4 or shp[0] != B or shp[2:] != q_tail or shp[1] != sq \
+                    or dev4(x, name) != q_st:
                 raise ValueError(f"tile {i}: {name} must be bf16 [B, Sq, Hq, d] with q's strides")
-            _check_dev(x, name)
         for name, x in (("k", t.k), ("v", t.v)):
-            if x.dtype != torch.bfloat16 or x.shape[0] != B or x.shape[2:] != t0.k.shape[2:] \
-                    or x.shape[1] != t.k.shape[1] or x.stride()[:3] != t0.k.stride()[:3]:
+            shp = x.shape
+            if x.dtype != bf16 or shp[0] != B or shp[2:] != k_tail or shp[1] != sk or dev4(x, name) != k_st:
                 raise ValueError(f"tile {i}: {name} must be bf16 [B, Sk, Hkv, d] with k's strides")
-            _check_dev(x, name)
-        if t.dq.dtype != torch.float32 or tuple(t.dq.shape) != tuple(t.q.shape) or t.dq.stride()[:3] != t0.dq.stride()[:3]:
+        if t.dq.dtype != f32 or t.dq.shape != t.q.shape or dev4(t.dq, "dq") != dq_st:
             raise ValueError(f"tile {i}: dq must be float32 shaped like q")
         for name, x in (("dk", t.dk), ("dv", t.dv)):
-            if x.dtype != torch.float32 or tuple(x.shape) != tuple(t.k.shape) or x.stride()[:3] != t0.dk.stride()[:3]:
+            if x.dtype != f32 or x.shape != t.k.shape or dev4(x, name) != dk_st:
                 raise ValueError(f"tile {i}: {name} must be float32 shaped like k")
-            _check_dev(x, name)
-        _check_dev(t.dq, "dq")
-        if tuple(t.lse.shape) != (B, Hq, t.q.shape[1]) or t.lse.dtype != torch.float32 \
-                or t.lse.stride()[:2] != t0.lse.stride()[:2]:
+        lse = t.lse
+        if tuple(lse.shape) != (B, Hq, sq) or lse.dtype != f32 or lse.stride()[:2] != l_st:
             raise ValueError(f"tile {i}: lse must be float32 [B, Hq, Sq]")
-        _check_dev(t.lse, "lse")
+        _check_dev(lse, "lse")
         c = arr[i]
         c.q, c.k, c.v, c.o, c.dout = t.q.data_ptr(), t.k.data_ptr(), t.v.data_ptr(), t.o.data_ptr(), t.dout.data_ptr()
-        c.lse, c.dq, c.dk, c.dv = t.lse.data_ptr(), t.dq.data_ptr(), t.dk.data_ptr(), t.dv.data_ptr()
-        c.sq, c.sk = t.q.shape[1], t.k.shape[1]
+        c.lse, c.dq, c.dk, c.dv = lse.data_ptr(), t.dq.data_ptr(), t.dk.data_ptr(), t.dv.data_ptr()
+        c.sq, c.sk = sq, sk
         c.q_pos, c.k_pos = _pos_c(t.q_pos), _pos_c(t.k_pos)
     a = _abi.ma_tile_bwd_args()
     a.dtype, a.batch, a.hq, a.hkv, a.head_dim, a.mask_mode = MA_BF16, B, Hq, Hkv, d, int(mask_mode)
@@ -314,18 +334,36 @@ def mesh_attn_tile_bwd(tiles: Sequence[BwdTile], scale: float, mask_mode: int = 
 
     `workspace` is a device uint8 tensor of at least mesh_attn_tile_bwd_workspace_size bytes; when None
     one is allocated here through torch (the library itself never allocates)."""
-    torch = _torch()
+    prepared = prepare_tile_bwd(tiles, scale, mask_mode, head_map, accumulate)
+    if prepared is None:
+        return
+    if workspace is None:
+        workspace = _torch().empty(max(prepared[2], 256), dtype=_torch().uint8, device=tiles[0].q.device)
+    launch_prepared_tile_bwd(prepared, workspace, stream)
+
+
+def prepare_tile_bwd(tiles: Sequence[BwdTile], scale: float, mask_mode: int = MA_MASK_NONE, head_map=None,
+                     accumulate: bool = False):
+    """The checked argument block of mesh_attn_tile_bwd and its workspace size in bytes, to be launched
+    (possibly many times) by launch_prepared_tile_bwd; it holds the tensors' addresses, so keep the
+    tensors alive.  None for an empty tile list."""
     tiles = list(tiles)
     if not tiles:
-        return
+        return None
     a, keep = _bwd_args(tiles, scale, mask_mode, head_map, accumulate)
-    need = int(lib().mesh_attn_tile_bwd_workspace_size(C.byref(a)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=tiles[0].q.device)
-    if workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+    return a, keep, int(lib().mesh_attn_tile_bwd_workspace_size(C.byref(a)))
+
+
+def launch_prepared_tile_bwd(prepared, workspace, stream=None) -> None:
+    """Enqueue a backward prepared by prepare_tile_bwd with `workspace`, a device uint8 tensor of at
+    least prepared[2] bytes (the C call and these two checks only)."""
+    if prepared is None:
+        return
+    a, _, need = prepared
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need or not workspace.is_cuda:
         raise ValueError(f"workspace must be a device buffer of >= {need} bytes")
-    _abi.check(lib().mesh_attn_tile_bwd(C.byref(a), C.c_void_p(workspace.data_ptr()),
-                                        workspace.numel() * workspace.element_size(), _stream_ptr(stream)),
+    _abi.check(lib().mesh_attn_tile_bwd(C.byref(a), C.c_void_p(workspace.data_ptr()), nbytes, _stream_ptr(stream)),
                "mesh_attn_tile_bwd")
 
 

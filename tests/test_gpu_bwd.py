@@ -154,6 +154,36 @@ def test_bwd_accumulate_adds():
     check_grad("dV+3", dv, dv_r + 3)
 
 
+def test_bwd_prepared_call_matches_the_direct_one():
+    # prepare_tile_bwd marshals the tiles once; every launch_prepared_tile_bwd is then the same C
+    # call as mesh_attn_tile_bwd: bitwise the same gradients, launch after launch
+    log("[bwd prepared call]")
+    sq, sk, hq, hkv, d = 150, 190, 8, 2, 128
+    tiles = run_case(1500, sq, sk, hq, hkv, d, ntiles=2)  # checked against the oracle here
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    outs = [t.dq for t in tiles] + [tiles[0].dk, tiles[0].dv]
+    want = [x.clone() for x in outs]
+    prep = ma.prepare_tile_bwd(tiles, scale, ma.MA_MASK_NONE)
+    assert prep[2] == ma.mesh_attn_tile_bwd_workspace_size(tiles, scale, ma.MA_MASK_NONE)
+    ws = torch.empty(max(prep[2], 256), dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        for x in outs:
+            x.fill_(float("nan"))
+        ma.launch_prepared_tile_bwd(prep, ws)
+        torch.cuda.synchronize()
+        for x, w in zip(outs, want):
+            assert torch.equal(x, w)
+    with pytest.raises(ValueError):
+        ma.launch_prepared_tile_bwd(prep, ws[:prep[2] - 1])
+    # accumulate: one more launch onto buffers that hold the gradients doubles them
+    prep_acc = ma.prepare_tile_bwd(tiles, scale, ma.MA_MASK_NONE, accumulate=True)
+    ma.launch_prepared_tile_bwd(prep_acc, ws)
+    torch.cuda.synchronize()
+    for x, w in zip(outs, want):
+        torch.testing.assert_close(x, 2 * w, rtol=1e-6, atol=1e-12)
+    assert ma.prepare_tile_bwd([], scale) is None
+
+
 def test_bwd_distributed_share():
     # The row's final O and LSE come from a merge over two KV partitions; the backward of one
     # partition with them gives that partition's share ([Mesh] section 3.5).
