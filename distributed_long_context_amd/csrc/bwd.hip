@@ -488,19 +488,37 @@ bwd_dkv_kernel(const BwdParams p) {
     const int gb = QP.qp.gb[0], st = QP.qp.st[0];
     return kp <= gb ? 0 : (int)min((int64_t)QP.sq, ((int64_t)kp - gb + st - 1) / st);
   };
-  // 64-row blocks of a partition, and the first one with any allowed pair for the workgroup
-  auto part_qb0 = [&](const BwdQPart& QP) {
-    if constexpr (MASKED) return first_row(QP, wg_kmin) / kBN;
-    else return 0;
-  };
-  int total = 0;  // blocks of the walk
-#pragma unroll
-  for (int i = 0; i < kBwdPerLaunch; ++i) {
-    if (i < E.n) {
-      const BwdQPart QP = qpart_at(partner_at(ei, i));
-      total += gsz * ((QP.sq + kBN - 1) / kBN - part_qb0(QP));
+  // The walk visits, per (Q partition, head of the group), the 64-row blocks from the first one
+  // with any allowed pair for the workgroup.  Masked, it runs in two phases: first the blocks in
+  // which some key of the workgroup needs the element mask (two or three: the workgroup's 128 keys
+  // span 128 query positions of a one-segment map), with the masked body; then the blocks that
+  // every key of the workgroup sees whole, with the unmasked body, so that the mask's VALU work
+  // is spent on the diagonal blocks only.  [qbeg, qend): the blocks of partition QP in this phase.
+  int phase = MASKED ? 0 : 1;
+  auto seg_range = [&](const BwdQPart& QP, int& qbeg, int& qend) {
+    const int nqb = (QP.sq + kBN - 1) / kBN;
+    if constexpr (MASKED) {
+      const int qb0 = first_row(QP, wg_kmin) / kBN;
+      const int qwhole = max(qb0, min(nqb, (first_row(QP, wg_kmax) + kBN - 1) / kBN));
+      qbeg = phase == 0 ? qb0 : qwhole;
+      qend = phase == 0 ? qwhole : nqb;
+    } else {
+      qbeg = 0;
+      qend = nqb;
     }
-  }
+  };
+  int total = 0;  // blocks of the walk in this phase
+  auto count_blocks = [&]() {
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < kBwdPerLaunch; ++i) {
+      if (i < E.n) {
+        int qbeg, qend;
+        seg_range(qpart_at(partner_at(ei, i)), qbeg, qend);
+        total += gsz * (qend - qbeg);
+      }
+    }
+  };
   auto next_block = [&](int from) -> int { return from < total ? from : total; };
 
   // ---- direct-to-LDS loads of one Q block, one dO block and the LSE2/D block ----
@@ -515,7 +533,7 @@ bwd_dkv_kernel(const BwdParams p) {
   // when those change, stand in for a per-block decode: no division or parameter
   // load per block (a scalar load would also make the wave wait for all of its
   // LDS reads).
-  int c_pi = 0, c_hi = 0, c_qb = 0, c_qb0 = 0, c_nqb = 0, c_sq = 0, c_qfull = 0, c_tfirst = 0;
+  int c_pi = 0, c_hi = 0, c_qb = 0, c_qb0 = 0, c_qend = 0, c_nqb = 0, c_sq = 0, c_qfull = 0, c_tfirst = 0;
   const __bf16* c_q = nullptr;
   const __bf16* c_g = nullptr;
   const float* c_l = nullptr;
@@ -524,13 +542,13 @@ bwd_dkv_kernel(const BwdParams p) {
       const BwdQPart QP = qpart_at(partner_at(ei, c_pi));
       c_sq = QP.sq;
       c_nqb = (QP.sq + kBN - 1) / kBN;
-      c_qb0 = part_qb0(QP);
+      seg_range(QP, c_qb0, c_qend);
       if constexpr (MASKED) {
         c_tfirst = key_ok ? first_row(QP, my_kpos) : 0;
         c_qfull = (first_row(QP, w_kmax) + kBN - 1) / kBN;
       }
-      if (c_qb0 < c_nqb || c_pi + 1 >= E.n) break;
-      ++c_pi;  // no allowed pair with this partition
+      if (c_qb0 < c_qend || c_pi + 1 >= E.n) break;
+      ++c_pi;  // no block of this partition in this phase
     }
     c_qb = c_qb0;
     const int h = head_of(g0 + c_hi);
@@ -565,7 +583,7 @@ bwd_dkv_kernel(const BwdParams p) {
       bm.whole = c_qb >= c_qfull;
       bm.lim = bm.whole ? -(1 << 30) : c_tfirst - c_qb * kBN;
     }
-    if (++c_qb == c_nqb) {
+    if (++c_qb == c_qend) {
       if (++c_hi == gsz) {
         c_hi = 0;
         ++c_pi;
@@ -575,7 +593,6 @@ bwd_dkv_kernel(const BwdParams p) {
     return bm;
   };
   auto issue_at = [&](int st, int g) -> BlkMask { return issue_next(st); };
-  cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (2 * LPW + 1)));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW + 1));
@@ -620,10 +637,10 @@ bwd_dkv_kernel(const BwdParams p) {
   };
   // one 32-query step: element e of the lane is query 32u + 16(e/8) + 8hl + e%8.
   // Keys past the end of the partition need no mask: their dK/dV rows are never
-  // stored and do not feed any other key's rows.  With position masks, blocks
-  // that are not fully allowed for the wave take a second copy of the body that
-  // zeroes P where the key comes after the query; both copies are straight-line
-  // code, so the VALU work interleaves with the MFMAs.
+  // stored and do not feed any other key's rows.  With position masks, the first
+  // phase's blocks (not fully allowed for the workgroup) take a second copy of the
+  // body that zeroes P where the key comes after the query; both copies are
+  // straight-line code, so the VALU work interleaves with the MFMAs.
   auto half_body = [&](auto masked, int g, const BlkMask& bm, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu,
                        f32x16& sn, f32x16& dn) {
     // one wave per SIMD: ask the scheduler to interleave the LDS reads with the
@@ -661,14 +678,15 @@ bwd_dkv_kernel(const BwdParams p) {
       }
     }
   };
+  // One phase of the walk: the ring of 4 stages, 3 blocks ahead, over the phase's blocks; the body
+  // of every block is the masked or the unmasked one, straight-line code either way.
+  auto run_phase = [&](auto masked) {
   auto half_step = [&](int g, const BlkMask& bm, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu, f32x16& sn,
-                       f32x16& dn) {
-    // masked: one straight-line body for every block (the row test costs two VALU
-    // ops per element, less than a second copy of the body costs in registers)
-    if constexpr (MASKED) half_body(std::true_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
-    else half_body(std::false_type{}, g, bm, st, u, sc, dc, nst, nu, sn, dn);
-  };
-
+                       f32x16& dn) { half_body(masked, g, bm, st, u, sc, dc, nst, nu, sn, dn); };
+  c_pi = 0;
+  c_hi = 0;
+  count_blocks();
+  cur_load();
   int bj0 = next_block(0);
   int bj1 = bj0 < total ? next_block(bj0 + 1) : total;
   int bj2 = bj1 < total ? next_block(bj1 + 1) : total;
@@ -705,6 +723,15 @@ bwd_dkv_kernel(const BwdParams p) {
     MA_DKV_BLOCK(3)
   }
 #undef MA_DKV_BLOCK
+  };
+  if constexpr (MASKED) {
+    run_phase(std::true_type{});
+    __syncthreads();  // every wave is done with the stages before the second phase refills them
+    phase = 1;
+    run_phase(std::false_type{});
+  } else {
+    run_phase(std::false_type{});
+  }
 
   // ---- dK (scaled) and dV of the wave's 32 keys ----
   float* dKg = KV.dk + (int64_t)b * p.dk_sb + (int64_t)kvh * p.dk_sh;

@@ -157,11 +157,12 @@ def test_random_head_map(seed):
     check_grad("dV", dv, dv_r)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(10))
 def test_random_multi_tile_calls(seed):
     """One accumulate forward call over a random set of (Q partition, KV partition) pairs in random
     order, each folding into its Q partition's output, then one backward call over the same pairs
-    (dQ summed per Q partition, dK/dV per KV partition)."""
+    (dQ summed per Q partition, dK/dV per KV partition).  Seeds 6-9 are wide calls (6-20 partitions
+    a side): more groups than one backward launch holds, partner sets split over launches."""
     rng = random.Random(8000 + seed)
     hkv = rng.choice([1, 2, 4])
     hq = hkv * rng.choice([1, 2, 4])
@@ -170,6 +171,8 @@ def test_random_multi_tile_calls(seed):
     mask = {"none": ma.MA_MASK_NONE, "causal": ma.MA_MASK_CAUSAL, "striped": ma.MA_MASK_STRIPED_ZIGZAG}[mode]
     nq, nk = rng.randint(1, 5), rng.randint(1, 12)
     P = rng.choice([16, 33, 64, 100, 129])
+    if seed >= 6:
+        nq, nk, P = rng.randint(6, 20), rng.randint(6, 20), rng.choice([16, 33, 64])
     log(f"[random multi-tile {seed}] hq={hq} hkv={hkv} d={d} {mode} nq={nq} nk={nk} P={P}")
     wid = 7100 + seed
     scale = np.float32(1.0 / math.sqrt(d))
