@@ -1,6 +1,7 @@
 """GPU parity at the limits the C ABI declares: MA_MAX_HEADS query heads (single-byte head
 tables in the kernel arguments; a 128-head group under one KV head) and MA_MAX_TILES tiles in
-one forward call (137 launches of the tile table), each checked against the fp64 oracle."""
+one forward call (137 launches of the tile table) and in one backward call (independent pairs: 4096
+query groups and 4096 KV groups, 512 launches a side), each checked against the fp64 oracle."""
 import math
 
 import numpy as np
@@ -12,9 +13,9 @@ torch = pytest.importorskip("torch")
 
 import distributed_long_context_amd as ma  # noqa: E402
 from distributed_long_context_amd import Pos, Tile, _abi  # noqa: E402
-from oracle import attn_tile  # noqa: E402
+from oracle import attn_tile, attn_tile_bwd  # noqa: E402
 from gpu_helpers import BF16_LSE_TOL, BF16_O_TOL, DEV, check_close, gen, host_f64, log, positions  # noqa: E402
-from test_gpu_bwd import run_case  # noqa: E402
+from test_gpu_bwd import GRAD_REL_TOL, run_case  # noqa: E402
 
 import synthetic  # noqa: E402
 
@@ -82,3 +83,38 @@ def test_max_tiles_one_call():
             el = max(el, float(np.max(np.abs(l_h[i * n + j] - L))))
     log(f"  O max_abs_err={eo:.3e}  LSE max_abs_err={el:.3e}")
     assert eo <= BF16_O_TOL and el <= BF16_LSE_TOL
+
+
+def test_max_tiles_backward_independent_pairs():
+    """MA_MAX_TILES independent (Q partition, KV partition) pairs of 16 tokens (GQA 2/1, d = 64) in
+    one backward call: every pair its own dQ and dK/dV group, so the call packs 4096 pieces a side
+    into launches of 8.  O and LSE are the GPU forward's (checked against the oracle by the test
+    above); the oracle's backward reads the same stored values.  Every pair's gradients checked."""
+    m, P, hq, hkv, d = _abi.MA_MAX_TILES, 16, 2, 1, 64
+    log(f"[limits bwd pairs] {m} independent pairs of {P} x {P}")
+    wid = 2650
+    q_all, qv = gen(wid, synthetic.T_Q, 0, (m, 1, P, hq, d))
+    k_all, kv = gen(wid, synthetic.T_K, 0, (m, 1, P, hkv, d))
+    v_all, vv = gen(wid, synthetic.T_V, 0, (m, 1, P, hkv, d))
+    do_all, dov = gen(wid, synthetic.T_DO, 0, (m, 1, P, hq, d))
+    o_all = torch.empty((m, 1, P, hq, d), dtype=torch.bfloat16, device=DEV)
+    l_all = torch.empty((m, 1, hq, P), dtype=torch.float32, device=DEV)
+    scale = np.float32(0.125)
+    ma.mesh_attn_tile_fwd([Tile(q_all[i], k_all[i], v_all[i], o_all[i], l_all[i]) for i in range(m)], float(scale))
+    dq_all = torch.full((m, 1, P, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    dk_all = torch.full((m, 1, P, hkv, d), float("nan"), dtype=torch.float32, device=DEV)
+    dv_all = torch.full_like(dk_all, float("nan"))
+    ma.mesh_attn_tile_bwd([ma.BwdTile(q_all[i], k_all[i], v_all[i], o_all[i], do_all[i], l_all[i], dq_all[i], dk_all[i],
+                                      dv_all[i]) for i in range(m)], float(scale))
+    torch.cuda.synchronize()
+    o_h, l_h = host_f64(o_all), host_f64(l_all)
+    dq_h, dk_h, dv_h = host_f64(dq_all), host_f64(dk_all), host_f64(dv_all)
+    worst = 0.0
+    for i in range(m):
+        refs = attn_tile_bwd(qv[i], kv[i], vv[i], o_h[i], dov[i], l_h[i], scale)
+        for name, got, ref in zip(("dQ", "dK", "dV"), (dq_h[i], dk_h[i], dv_h[i]), refs):
+            scl = max(float(np.max(np.abs(ref))), 1e-3)
+            err = float(np.max(np.abs(got - ref)))
+            worst = max(worst, err / scl)
+            assert err <= GRAD_REL_TOL * scl, (i, name, err, scl)
+    log(f"  worst max_abs_err / max|ref| over {m} pairs x 3 gradients: {worst:.2e}")
