@@ -287,7 +287,7 @@ bwd_dq_kernel(const BwdParams p) {
     }
     return bm;
   };
-  auto issue_at = [&](int st, int g) -> BlkMask { return issue_next(st); };
+  auto issue_at = [&](int st, int /*position*/) -> BlkMask { return issue_next(st); };
   cur_load();
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * LPW));
@@ -321,7 +321,7 @@ bwd_dq_kernel(const BwdParams p) {
   // walk the block carries its mask: whole (no key masked), or the lane's last
   // allowed key index within the block (keys past a partition's end included;
   // -1 past the end of the walk: every key masked).
-  auto mask_half = [&](int g, const BlkMask& bm, int kb2, f32x16& s) {
+  auto mask_half = [&](int /*position*/, const BlkMask& bm, int kb2, f32x16& s) {
     if (__builtin_expect(bm.whole, 1)) return;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -460,7 +460,6 @@ bwd_dkv_kernel(const BwdParams p) {
   if (wg_keys <= 0) return;
   const int my_key = key0 + wave * kKW + l32;
   const bool key_ok = my_key < KV.sk;
-  const bool wg_tail = wg_keys < kWaves * kKW;
   int wg_kmin = 0, wg_kmax = 0, w_kmin = 0, w_kmax = 0, my_kpos = INT32_MAX;
   if constexpr (MASKED) {
     pos_minmax_dev(KV.kp, KV.sk, key0, key0 + wg_keys, wg_kmin, wg_kmax);
@@ -592,7 +591,7 @@ bwd_dkv_kernel(const BwdParams p) {
     }
     return bm;
   };
-  auto issue_at = [&](int st, int g) -> BlkMask { return issue_next(st); };
+  auto issue_at = [&](int st, int /*position*/) -> BlkMask { return issue_next(st); };
   auto wait_positions = [&](int n) {  // at most n later positions in flight
     if (n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (2 * LPW + 1)));
     else if (n == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW + 1));
@@ -641,7 +640,7 @@ bwd_dkv_kernel(const BwdParams p) {
   // phase's blocks (not fully allowed for the workgroup) take a second copy of the
   // body that zeroes P where the key comes after the query; both copies are
   // straight-line code, so the VALU work interleaves with the MFMAs.
-  auto half_body = [&](auto masked, int g, const BlkMask& bm, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu,
+  auto half_body = [&](auto masked, int /*position*/, const BlkMask& bm, int st, int u, f32x16& sc, f32x16& dc, int nst, int nu,
                        f32x16& sn, f32x16& dn) {
     // one wave per SIMD: ask the scheduler to interleave the LDS reads with the
     // MFMAs (measured: 14% faster than the default schedule for this kernel)

@@ -343,7 +343,6 @@ fwd_bf16_kernel(const FwdParams p) {
     }
   };
   set_keys(T);
-  auto next_block = [&](int from) -> int { return from < nkb ? from : nkb; };
 
   // ---- direct-to-LDS loads: wave instruction i fills LDS chunks [(wave*LPW+i)*64, +64) ----
   auto load_row = [&](int i) { return ((wave * C::LPW + i) * 64 + lane) / C::CH; };

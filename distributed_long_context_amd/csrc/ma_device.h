@@ -140,9 +140,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // states that, it is free when they already sit in scalar registers).  Written as
 // inline asm so that the compiler does not add vmcnt(0) waits in front of every
 // LDS read; the kernels order these loads themselves with s_waitcnt vmcnt and a
-// barrier.  M0 carries the LDS address and is declared clobbered, so the compiler
-// sets it again wherever it relies on it (in these kernels nowhere: no save and
-// restore around each load).
+// barrier.  M0 carries the LDS address and is declared clobbered; M0 is a reserved
+// register, which the compiler does not promise to preserve across inline asm, so
+// the kernels rely on its keeping nothing of its own in M0.  A test compiles every
+// kernel to assembly and checks that M0 appears only in this sequence
+// (tests/test_m0_discipline.py).
 __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff_bytes, uint32_t lds_dst) {
   const uint64_t g = (uint64_t)(uintptr_t)gbase;
   // readfirstlane returns int: go through uint32_t so the low word is not sign-extended
