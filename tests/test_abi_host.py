@@ -247,7 +247,7 @@ def test_bwd_tiles_sharing_an_output_must_share_its_description():
     # before anything is enqueued, so "workspace" in the error means the tiles were accepted.
     L = _abi.lib()
 
-    def verdict(t, n, mask=_abi.MA_MASK_NONE):
+    def outcome(t, n, mask=_abi.MA_MASK_NONE):
         a = _bwd_args_c(t, n, mask=mask)
         rc = L.mesh_attn_tile_bwd(C.byref(a), None, 0, None)
         assert rc == _abi.MA_ERR_INVALID
@@ -265,44 +265,44 @@ def test_bwd_tiles_sharing_an_output_must_share_its_description():
     share_kv(t, 5, 1)
     share_q(t, 4, 0)
     share_q(t, 2, 0)
-    assert b"workspace" in verdict(t, n)
+    assert b"workspace" in outcome(t, n)
     for field in ("k", "v", "sk"):  # a third tile on the same dk/dv with another KV description
         t = _bwd_tiles(n)
         share_kv(t, 3, 1)
         share_kv(t, 5, 1)
         setattr(t[5], field, getattr(t[5], field) + 128)
-        assert b"dk/dv" in verdict(t, n), field
+        assert b"dk/dv" in outcome(t, n), field
     t = _bwd_tiles(n)
     t[4].dv = t[2].dk  # one tile's dv is another's dk
-    assert b"dk/dv" in verdict(t, n)
+    assert b"dk/dv" in outcome(t, n)
     t = _bwd_tiles(n)
     t[4].dk = t[2].dv
-    assert b"dk/dv" in verdict(t, n)
+    assert b"dk/dv" in outcome(t, n)
     t = _bwd_tiles(n)
     t[4].dk = t[4].dv = t[2].dk = t[2].dv  # both name one buffer for dk and dv, with another k
-    assert b"dk/dv" in verdict(t, n)
+    assert b"dk/dv" in outcome(t, n)
     t = _bwd_tiles(n)
     share_kv(t, 4, 2)
     t[4].dk, t[4].dv = t[4].dk, t[0].dv  # same dk, another dv
-    assert b"dk/dv" in verdict(t, n)
+    assert b"dk/dv" in outcome(t, n)
     for field in ("q", "o", "dout", "lse", "sq"):
         t = _bwd_tiles(n)
         share_q(t, 4, 0)
         share_q(t, 2, 0)
         setattr(t[4], field, getattr(t[4], field) + (1 if field == "sq" else 256))
-        assert b"same dq" in verdict(t, n), field
+        assert b"same dq" in outcome(t, n), field
     # positions count only under a mask
     t = _bwd_tiles(n)
     share_q(t, 4, 0)
     share_kv(t, 5, 1)
     t[4].q_pos.seg[0].global_begin = 64
     t[5].k_pos.seg[0].global_begin = 64
-    assert b"workspace" in verdict(t, n)
-    assert b"same dq" in verdict(t, n, mask=_abi.MA_MASK_CAUSAL)
+    assert b"workspace" in outcome(t, n)
+    assert b"same dq" in outcome(t, n, mask=_abi.MA_MASK_CAUSAL)
     t[4].q_pos.seg[0].global_begin = 0
-    assert b"dk/dv" in verdict(t, n, mask=_abi.MA_MASK_CAUSAL)
+    assert b"dk/dv" in outcome(t, n, mask=_abi.MA_MASK_CAUSAL)
     t[5].k_pos.seg[0].global_begin = 0
-    assert b"workspace" in verdict(t, n, mask=_abi.MA_MASK_CAUSAL)
+    assert b"workspace" in outcome(t, n, mask=_abi.MA_MASK_CAUSAL)
 
 
 def test_bwd_workspace_size_rejects_bad_segments():
