@@ -59,9 +59,9 @@ def _case(seed):
                 qp=_segments(rng, sq, rng.randint(0, 300)), kp=_segments(rng, sk, 0))
 
 
-# 72: four key segments folded into an incoming partial with |O| near 3.5; when the segments of a
-# tile were separate folds, each rounding O to bf16, its error reached 0.021 (bar 0.02)
-@pytest.mark.parametrize("seed", list(range(24)) + [72])
+# seed 72: four key segments folded into an incoming partial with |O| near 3.5; when the segments
+# of a tile were separate folds, each rounding O to bf16, its error reached 0.021 (bar 0.02)
+@pytest.mark.parametrize("seed", list(range(120)))
 def test_random_forward(seed):
     c = _case(1000 + seed)
     log(f"[random fwd {seed}] {c}")
@@ -90,7 +90,7 @@ def test_random_forward(seed):
     check_close("LSE", host_f64(lse), Lref, BF16_LSE_TOL)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(100))
 def test_random_backward(seed):
     c = _case(3000 + seed)
     log(f"[random bwd {seed}] {c}")
@@ -117,7 +117,7 @@ def test_random_backward(seed):
     check_grad("dV", dv, dv_r)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_head_map(seed):
     """Irregular explicit GQA maps (groups of unequal size, KV heads no query head reads):
     forward and backward of one drawn tile."""
@@ -157,12 +157,13 @@ def test_random_head_map(seed):
     check_grad("dV", dv, dv_r)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_multi_tile_calls(seed):
     """One accumulate forward call over a random set of (Q partition, KV partition) pairs in random
     order, each folding into its Q partition's output, then one backward call over the same pairs
-    (dQ summed per Q partition, dK/dV per KV partition).  Seeds 6-9 are wide calls (6-20 partitions
-    a side): more groups than one backward launch holds, partner sets split over launches."""
+    (dQ summed per Q partition, dK/dV per KV partition).  Seeds 6-15 are wide calls (6-20
+    partitions a side): more groups than one backward launch holds, partner sets split over
+    launches."""
     rng = random.Random(8000 + seed)
     hkv = rng.choice([1, 2, 4])
     hq = hkv * rng.choice([1, 2, 4])
@@ -229,7 +230,7 @@ def _head_major(t):
     return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
 
 
-@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("seed", range(8))
 def test_random_head_major_layout(seed):
     """Forward and backward of a drawn tile with every [B, S, H, d] tensor in head-major storage."""
     c = _case(20000 + seed)
@@ -265,7 +266,7 @@ def test_random_head_major_layout(seed):
     check_grad("dV", dv, dv_r)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_tile_table(seed):
     """A random Mesh-like call through the tile table and through kernel arguments: query and KV
     partitions of random lengths (mostly in the resident-KV range, some outside it), a random
